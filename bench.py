@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode-attention hot path on one MI355X.
+
+One step = pa_kv_append of every sequence's new token + pa_decode over the whole batch (one
+decode step of one attention layer).  The default workload is the 7B-style multi-head layer:
+16 sequences x 2048 tokens, 32 query heads = 32 KV heads, head_dim 128, fp16, 16-token blocks
+scattered over a pool twice the needed size.  Inputs are seeded synthetic data, resident in HBM
+before the timed region; the pool is replicated `rotations` times and the steps cycle through the
+copies so that no step finds its K/V in the 256 MB last-level cache.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s"
+PEAK_GBS = 8000.0           # MI355X HBM3E
+DEFAULT_WORKLOAD = "mha_b16_h32_d128_f16_l2048"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, decode_bytes_fn, append_bytes, min_s: float = 10.0,
+                 max_s: float = 25.0) -> dict:
+    """The fp64 oracle, as it stands, on one thread: repeated passes of append + decode over the
+    workload until about min_s seconds have run (a pass stops early past max_s)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    s = wl.spec
+    nbytes, seqs, appends = 0, 0, 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while True:
+            k, v = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
+            nbytes += append_bytes
+            appends += 1
+            for b in range(wl.batch):
+                sl = slice(b, b + 1)
+                oracle.decode(wl.q[sl], k, v, wl.block_tables[sl], wl.context_lens[sl], wl.scale,
+                              s.q_dtype, s.kv_dtype, wl.k_scale, wl.v_scale)
+                nbytes += decode_bytes_fn(wl.context_lens[sl])
+                seqs += 1
+                if time.perf_counter() - t0 > max_s:
+                    break
+            secs = time.perf_counter() - t0
+            if secs >= min_s:
+                break
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{appends} append(s) of {wl.batch} tokens + {seqs} sequence decodes "
+                      f"({seqs / wl.batch:.2f} passes over the batch) in {secs:.1f} s, numpy "
+                      f"float64 on 1 thread; same byte model as the GPU figure"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="key-partition tokens (default: the workload's, else the library's)")
+    ap.add_argument("--rotations", type=int, default=0, help="pool copies cycled (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; no multi-GPU path is built, so "
+              f"--gpus {args.gpus} is not supported (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_31_amd as pa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    pa.lib()
+
+    t0 = time.perf_counter()
+    wl = workloads.make(args.workload, poison=False)
+    s = wl.spec
+    B, Hq, Hkv, D = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim
+    log(f"workload {args.workload}: generated in {time.perf_counter() - t0:.1f} s")
+
+    def dbytes(lens, unique=None):
+        return workloads.decode_bytes(lens, Hq, Hkv, D, s.q_dtype, s.kv_dtype, unique)
+
+    bytes_decode = dbytes(wl.context_lens, wl.unique_tokens)
+    bytes_decode_logical = dbytes(wl.context_lens)
+    bytes_append = workloads.append_bytes(B, Hkv, D, s.kv_dtype)
+    pool_bytes = wl.k_cache.nbytes + wl.v_cache.nbytes
+    R = args.rotations or max(2, math.ceil(2 * 2**30 / bytes_decode))
+    R = max(1, min(R, int(48 * 2**30 // pool_bytes)))
+
+    def to_dev(bits, dtype):
+        a = np.ascontiguousarray(bits)
+        if dtype == "fp8_e4m3":
+            return torch.from_numpy(a).to(dev)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+        return torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
+
+    base = {
+        "q": to_dev(wl.q, s.q_dtype), "k": to_dev(wl.k_cache, s.kv_dtype),
+        "v": to_dev(wl.v_cache, s.kv_dtype),
+        "k_new": to_dev(wl.k_new, s.kv_dtype), "v_new": to_dev(wl.v_new, s.kv_dtype),
+    }
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    lens = torch.from_numpy(wl.context_lens).to(dev)
+    k_scale = None if wl.k_scale is None else torch.from_numpy(wl.k_scale).to(dev)
+    v_scale = None if wl.v_scale is None else torch.from_numpy(wl.v_scale).to(dev)
+    rots = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
+    for r in rots:
+        r["out"] = torch.empty_like(r["q"])
+    torch.cuda.synchronize()
+    log(f"uploaded: {R} pool copies of {pool_bytes / 2**30:.2f} GiB")
+
+    P = s.partition_tokens if args.partition is None else args.partition
+    desc = pa.decode_desc(base["q"], base["k"], tables, wl.max_context_len, P)
+    P_used = pa.pa_decode_partition_tokens(desc)
+    ws_bytes = pa.pa_decode_workspace_size(desc)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    scale = float(wl.scale)
+    mcl = wl.max_context_len
+
+    def step(r, ev=None):
+        x = rots[r]
+        pa.pa_kv_append(x["k_new"], x["v_new"], slots, x["k"], x["v"])
+        if ev is not None:
+            ev[0].record()
+        pa.pa_decode(x["q"], x["k"], x["v"], tables, lens, scale, x["out"], k_scale=k_scale,
+                     v_scale=v_scale, max_context_len=mcl, partition_tokens=P,
+                     workspace=workspace)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % R, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decode_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    dec_s = float(decode_ms.mean()) / 1e3
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, decode "
+        f"{dec_s * 1e6:.1f} us (median {np.median(decode_ms) * 1e3:.1f} us)")
+
+    achieved = bytes_decode / dec_s / 1e9
+    value = (bytes_decode + bytes_append) / (ms_per_step / 1e3) / 1e9
+    kernel = "decode_partition_kernel" + (" + merge_kernel" if ws_bytes else "")
+    lens_np = wl.context_lens
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.kv_dtype if s.kv_dtype == s.q_dtype else f"{s.q_dtype}+{s.kv_dtype}",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_dim": D, "block_size": 16, "q_dtype": s.q_dtype, "kv_dtype": s.kv_dtype,
+            "context_len_min": int(lens_np.min()), "context_len_max": int(lens_np.max()),
+            "context_tokens": int(lens_np.sum()), "unique_tokens": int(wl.unique_tokens),
+            "num_blocks": wl.num_blocks, "partition_tokens": P_used, "rotations": R,
+            "step": "pa_kv_append (1 token per sequence) + pa_decode",
+        },
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "decode_tokens_per_s": round(B / dec_s, 1),
+        "step_tokens_per_s": round(B / (ms_per_step / 1e3), 1),
+        "us_per_decode": round(dec_s * 1e6, 2),
+        "us_per_decode_median": round(float(np.median(decode_ms)) * 1e3, 2),
+        "bytes_per_step": {"decode": bytes_decode, "decode_logical": bytes_decode_logical,
+                           "append": bytes_append},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "kernel": kernel},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu_baseline)")
+        result["cpu_baseline"] = cpu_baseline(wl, dbytes, bytes_append)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,150 @@
+/*
+ * pa.h -- paged decode attention for AMD Instinct MI355X (gfx950): the C ABI.
+ *
+ * Two operations on a PagedAttention KV cache, as the pages state the problem:
+ *
+ *  - pa_kv_append: each generation step stores the new token's K and V rows in the cache
+ *    (Scaling Book note on notes.yuuk.io, "Transformer 推論の基礎: Prefill と Generation"; the
+ *    youngju.dev serving guide's KV-cache module).  In the paged cache the token goes to one slot
+ *    of a fixed-size block (kasblo.com vLLM explainer, "blockはrequestの成長に合わせて割り当てる").
+ *
+ *  - pa_decode: single-query attention of each sequence's new query over all of its cached
+ *    tokens, reading K/V through a per-sequence block table that maps logical blocks to
+ *    scattered physical blocks (kasblo.com, "PagedAttentionはKV Cacheをblockで管理する";
+ *    youngju.dev guide, PagedAttention block-table figure), with grouped-query heads
+ *    (Scaling Book note, "生成スループット/レイテンシ改善のテクニック") and an online softmax
+ *    (babushkai.com "GPU推論の内部構造", FlashAttention section).  Long contexts are split into
+ *    key partitions whose partial results are merged by log-sum-exp.
+ *
+ * Cache layout (one "tile" = one physical block of one KV head, contiguous in memory):
+ *   k_cache  [num_blocks][num_kv_heads][16][head_dim]   token-major: a token's K row is contiguous
+ *   v_cache  [num_blocks][num_kv_heads][head_dim][16]   dim-major: one dimension's 16 token values
+ *                                                         are contiguous
+ *   slot s   = physical_block * 16 + offset_in_block
+ *   fp8 caches store OCP e4m3fn codes; the real value is code * scale[block][kv_head], with one
+ *   fp32 scale per (physical block, KV head), separate arrays for K and V.
+ *
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Ownership and execution: every data pointer is a device pointer owned by the caller.  The
+ * library never allocates or frees memory and keeps no state besides a thread-local copy of the
+ * last HIP error.  Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream)
+ * and return without synchronising; the caller orders and synchronises.
+ *
+ * Errors: conditions the host can see (null pointers, non-positive sizes, unsupported shapes or
+ * dtype pairs, misaligned pointers, a short workspace) return a status before anything is
+ * launched.  Device-resident values are a caller contract that is not checked on the host; the
+ * kernels clamp them so that nothing is ever read or written outside the described arrays:
+ *   - a slot outside [0, num_blocks*16) is skipped by pa_kv_append;
+ *   - a context length is clamped to [0, min(max_context_len, max_blocks_per_seq*16)];
+ *   - a block-table entry outside [0, num_blocks) reads physical block 0 instead
+ *     (the result is then unspecified but the call stays in bounds).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misaligned pointer */
+  PA_ERR_UNSUPPORTED = 2,  /* head_dim, block_size, head grouping or dtype pair not implemented */
+  PA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than pa_decode_workspace_size() */
+  PA_ERR_HIP = 4           /* a kernel launch failed; pa_last_hip_error() has the hipError_t */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F16 = 0,              /* IEEE binary16 */
+  PA_BF16 = 1,             /* bfloat16 */
+  PA_FP8_E4M3 = 2          /* OCP fp8 e4m3fn (bias 7, max 448, no infinities) -- caches only */
+} pa_dtype;
+
+/* Geometry of the paged K/V pools, shared by both calls. */
+typedef struct pa_cache_desc {
+  int32_t num_blocks;      /* physical blocks in each pool, > 0 */
+  int32_t num_kv_heads;    /* KV heads per token, > 0 */
+  int32_t head_dim;        /* 64 or 128 */
+  int32_t block_size;      /* tokens per block; must be 16 */
+  int32_t kv_dtype;        /* pa_dtype of the cache elements */
+} pa_cache_desc;
+
+typedef struct pa_decode_desc {
+  pa_cache_desc cache;
+  int32_t batch;              /* sequences, > 0 */
+  int32_t num_q_heads;        /* multiple of num_kv_heads with a group size of 1..16 */
+  int32_t max_blocks_per_seq; /* row length (stride) of block_tables, > 0 */
+  int32_t max_context_len;    /* host-side upper bound on context_lens; sizes the launch without
+                                 reading device memory.  0 = max_blocks_per_seq * 16. */
+  int32_t partition_tokens;   /* split-KV key partition: a multiple of 32 in [32, 4096]; 0 = the
+                                 library chooses (pa_decode_partition_tokens reports the choice) */
+  int32_t q_dtype;            /* PA_F16 or PA_BF16; the output has the same dtype */
+} pa_decode_desc;
+
+/*
+ * pa_kv_append -- write num_tokens new K/V rows into their cache slots.
+ *
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim] elements of cache->kv_dtype, 16-byte
+ *                 aligned.  For an fp8 cache they are codes already quantised with the scale of
+ *                 the block they go to; the bytes are copied unchanged.
+ *   slot_mapping  [num_tokens] int64, 8-byte aligned: token i goes to offset slot%16 of physical
+ *                 block slot/16 for every KV head.  A negative slot skips the token (padding).
+ *   k_cache, v_cache  the pools described above, updated in place, 16-byte aligned.
+ *
+ * The copy is exact.  Two tokens with the same slot in one call race (caller error).
+ * num_tokens == 0 is a no-op that returns PA_OK.
+ */
+pa_status pa_kv_append(const pa_cache_desc* cache, int32_t num_tokens,
+                       const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       void* k_cache, void* v_cache, void* stream);
+
+/*
+ * pa_decode -- out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b for every sequence b and query
+ * head h, where K_b, V_b are the first context_lens[b] tokens of sequence b gathered through
+ * block_tables[b] from the KV head of h's group (times the block scales for fp8 caches).
+ *
+ *   q             [batch][num_q_heads][head_dim] of q_dtype, 16-byte aligned
+ *   k_cache, v_cache  pools as above, 16-byte aligned
+ *   k_scale, v_scale  [num_blocks][num_kv_heads] fp32 for fp8 caches, 4-byte aligned; must be
+ *                 NULL for f16/bf16 caches
+ *   block_tables  [batch][max_blocks_per_seq] int32: logical block j of sequence b lives in
+ *                 physical block block_tables[b][j]; only j < ceil(context_lens[b]/16) is read
+ *   context_lens  [batch] int32, tokens to attend over (including the token appended this step)
+ *   scale         softmax scale, usually 1/sqrt(head_dim)
+ *   out           [batch][num_q_heads][head_dim] of q_dtype, 16-byte aligned, written (rounded to
+ *                 nearest even from fp32); a sequence with context length 0 gets zeros
+ *   workspace     device scratch of at least pa_decode_workspace_size(desc) bytes, 16-byte
+ *                 aligned; may be NULL when that size is 0.  Its contents need no initialisation
+ *                 and are garbage afterwards.  Two calls in flight must not share it.
+ *
+ * Supported pairs (q_dtype, kv_dtype): (F16, F16), (BF16, BF16), (BF16, FP8_E4M3),
+ * (F16, FP8_E4M3).  Accumulation is fp32.  Results depend only on logical token positions, so
+ * the same data behind any physical block placement gives bit-identical output.
+ */
+pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cache,
+                    const void* v_cache, const float* k_scale, const float* v_scale,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode needs for this descriptor (0 when no sequence can span more than
+ * one key partition).  Returns 0 for an invalid descriptor as well; pa_decode reports that. */
+size_t pa_decode_workspace_size(const pa_decode_desc* desc);
+
+/* The key-partition length pa_decode will use for this descriptor, or 0 if it is invalid. */
+int32_t pa_decode_partition_tokens(const pa_decode_desc* desc);
+
+/* A static, human-readable name for a status code. */
+const char* pa_status_string(pa_status status);
+
+/* The hipError_t of the last failed launch on the calling thread (0 if none). */
+int32_t pa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

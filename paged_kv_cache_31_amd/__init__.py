@@ -1,0 +1,184 @@
+"""Python binding of libpa.so, the MI355X paged decode-attention library (see include/pa.h).
+
+Argument marshalling only: shapes and dtypes are read from torch tensors, the stream is torch's
+current stream, and every step of the computation runs in the library's HIP kernels.  There is
+no fallback: if libpa.so is missing or a call fails, a RuntimeError is raised.
+
+Cache layout:  k_cache [num_blocks][num_kv_heads][16][head_dim],
+               v_cache [num_blocks][num_kv_heads][head_dim][16];
+fp8 caches are uint8 (or float8_e4m3fn) tensors of OCP e4m3fn codes with fp32 scales
+[num_blocks][num_kv_heads] for K and for V.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+BLOCK_SIZE = 16
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("cache", CacheDesc), ("batch", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("max_context_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{fn} failed: {status_string(status)} (status {status})"
+        if status == PA_ERR_HIP:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+
+
+_lib = None
+_lock = threading.Lock()
+
+EXPORTS = ("pa_kv_append", "pa_decode", "pa_decode_workspace_size",
+           "pa_decode_partition_tokens", "pa_status_string", "pa_last_hip_error")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so (built in-tree by __graft_entry__.build()); raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+            L.pa_kv_append.argtypes = [ctypes.POINTER(CacheDesc), i32, vp, vp, vp, vp, vp, vp]
+            L.pa_kv_append.restype = i32
+            L.pa_decode.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.c_float, vp, vp, sz, vp]
+            L.pa_decode.restype = i32
+            L.pa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc)]
+            L.pa_decode_workspace_size.restype = sz
+            L.pa_decode_partition_tokens.argtypes = [ctypes.POINTER(DecodeDesc)]
+            L.pa_decode_partition_tokens.restype = i32
+            L.pa_status_string.argtypes = [i32]
+            L.pa_status_string.restype = ctypes.c_char_p
+            L.pa_last_hip_error.argtypes = []
+            L.pa_last_hip_error.restype = i32
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(status).decode()
+
+
+def _dtype_code(t: torch.Tensor, allow_fp8: bool) -> int:
+    if t.dtype == torch.float16:
+        return PA_F16
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if allow_fp8 and t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != PA_OK:
+        raise PaError(fn, status, lib().pa_last_hip_error() if status == PA_ERR_HIP else 0)
+
+
+def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+    NB, Hkv, bs, D = k_cache.shape
+    return CacheDesc(NB, Hkv, D, bs, _dtype_code(k_cache, True))
+
+
+def pa_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Scatter k_new/v_new [T][Hkv][D] into their slots (int64 [T], <0 skips)."""
+    assert k_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()
+    assert k_new.is_contiguous() and v_new.is_contiguous() and slot_mapping.is_contiguous()
+    assert slot_mapping.dtype == torch.int64
+    NB, Hkv, bs, D = k_cache.shape
+    assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
+    T = slot_mapping.shape[0]
+    assert tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D)
+    assert k_new.element_size() == k_cache.element_size()
+    st = lib().pa_kv_append(ctypes.byref(cache_desc(k_cache)), T, _ptr(k_new), _ptr(v_new),
+                            _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _stream(stream))
+    _check("pa_kv_append", st)
+
+
+def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_tokens=0) -> DecodeDesc:
+    B, Hq, D = q.shape
+    return DecodeDesc(cache_desc(k_cache), B, Hq, block_tables.shape[1], int(max_context_len),
+                      int(partition_tokens), _dtype_code(q, False))
+
+
+def pa_decode_workspace_size(desc: DecodeDesc) -> int:
+    return int(lib().pa_decode_workspace_size(ctypes.byref(desc)))
+
+
+def pa_decode_partition_tokens(desc: DecodeDesc) -> int:
+    return int(lib().pa_decode_partition_tokens(ctypes.byref(desc)))
+
+
+_workspaces: dict = {}
+
+
+def _workspace(nbytes: int, device, stream_handle: int):
+    if nbytes == 0:
+        return None
+    key = (device, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
+              v_scale=None, max_context_len=0, partition_tokens=0, workspace=None,
+              stream=None) -> torch.Tensor:
+    """out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b through the block tables; returns out."""
+    for t in (q, k_cache, v_cache, block_tables, context_lens, out):
+        assert t.is_cuda and t.is_contiguous()
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert out.shape == q.shape and out.dtype == q.dtype
+    NB, Hkv, bs, D = k_cache.shape
+    assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
+    assert q.shape[2] == D and context_lens.shape[0] == q.shape[0] == block_tables.shape[0]
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens)
+    need = pa_decode_workspace_size(desc)
+    st = _stream(stream)
+    if workspace is None:
+        workspace = _workspace(need, q.device, st.value or 0)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = lib().pa_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                             _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace),
+                             wbytes, st)
+    _check("pa_decode", status)
+    return out

@@ -1,0 +1,79 @@
+// Device-side helpers for the gfx950 paged-attention kernels: vector types, MFMA wrappers,
+// fp8 (OCP e4m3fn) widening and wave-level cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum : int { DT_F16 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// Element type fed to the matrix cores: the query's 16-bit type.
+template <int QT> struct Mfma;
+
+template <> struct Mfma<DT_BF16> {
+  typedef __bf16 elem;
+  typedef bf16x8 vec8;
+  // D = A(16x32) * B(32x16) + C.  Lane l holds A[l%16][8*(l/16)+i], B[8*(l/16)+i][l%16] and
+  // C[4*(l/16)+i][l%16].
+  static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // Two fp8 codes (the low or high 16 bits of w) widened exactly.
+  template <bool HI>
+  static __device__ __forceinline__ bf16x2 from_fp8x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  }
+};
+
+template <> struct Mfma<DT_F16> {
+  typedef _Float16 elem;
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  template <bool HI>
+  static __device__ __forceinline__ f16x2 from_fp8x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+  }
+};
+
+template <typename V8>
+__device__ __forceinline__ V8 as_vec8(uint4 u) {
+  return __builtin_bit_cast(V8, u);
+}
+
+// Eight fp8 codes (two dwords) -> eight 16-bit MFMA elements, exactly.
+template <int QT>
+__device__ __forceinline__ typename Mfma<QT>::vec8 fp8x8_to_vec8(uint32_t w0, uint32_t w1) {
+  typedef typename Mfma<QT>::vec8 V8;
+  auto a = Mfma<QT>::template from_fp8x2<false>(w0);
+  auto b = Mfma<QT>::template from_fp8x2<true>(w0);
+  auto c = Mfma<QT>::template from_fp8x2<false>(w1);
+  auto d = Mfma<QT>::template from_fp8x2<true>(w1);
+  V8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Butterfly over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_across_rows(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum_across_rows(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+}  // namespace pa

@@ -1,0 +1,190 @@
+// C ABI of the paged decode-attention library (declared in include/pa.h): host-side argument
+// validation, the split-KV partition choice, workspace sizing and kernel dispatch.  Nothing here
+// reads device memory or synchronises.
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_internal.hpp"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+pa_status check_cache(const pa_cache_desc* c) {
+  if (!c) return PA_ERR_INVALID_ARG;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (c->kv_dtype < PA_F16 || c->kv_dtype > PA_FP8_E4M3) return PA_ERR_INVALID_ARG;
+  if (c->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
+  if (c->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;   // launch grid limit
+  if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+pa_status check_decode_desc(const pa_decode_desc* d) {
+  if (!d) return PA_ERR_INVALID_ARG;
+  pa_status s = check_cache(&d->cache);
+  if (s != PA_OK) return s;
+  if (d->batch <= 0 || d->num_q_heads <= 0 || d->max_blocks_per_seq <= 0 ||
+      d->max_context_len < 0 || d->partition_tokens < 0)
+    return PA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->cache.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (d->batch > 65535 || d->num_q_heads > 65535) return PA_ERR_UNSUPPORTED;   // grid y/z limits
+  const int group = d->num_q_heads / d->cache.num_kv_heads;
+  if (group > 16) return PA_ERR_UNSUPPORTED;
+  if (d->partition_tokens != 0 &&
+      (d->partition_tokens % pa::kStepTokens != 0 || d->partition_tokens > pa::kMaxPartition))
+    return PA_ERR_INVALID_ARG;
+  if (d->q_dtype != PA_F16 && d->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  const int kv = d->cache.kv_dtype;
+  if (kv != PA_FP8_E4M3 && kv != d->q_dtype) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+// Longest context the launch covers.
+int len_cap(const pa_decode_desc* d) {
+  const int64_t table_cap = (int64_t)d->max_blocks_per_seq * pa::kBlock;
+  int64_t cap = d->max_context_len > 0 ? d->max_context_len : table_cap;
+  if (cap > table_cap) cap = table_cap;
+  if (cap > INT32_MAX) cap = INT32_MAX;
+  return (int)cap;
+}
+
+// Partition length when the caller leaves it to the library: 512 tokens (16 steps, 4 per wave).
+int choose_partition(const pa_decode_desc* d) {
+  if (d->partition_tokens > 0) return d->partition_tokens;
+  return 512;
+}
+
+int np_max_of(const pa_decode_desc* d, int partition) {
+  const int cap = len_cap(d);
+  const int np = (cap + partition - 1) / partition;
+  return np < 1 ? 1 : np;
+}
+
+size_t workspace_bytes_of(const pa_decode_desc* d) {
+  const int P = choose_partition(d);
+  const int np = np_max_of(d, P);
+  if (np == 1) return 0;
+  return pa::ws_acc_bytes(d->batch, d->num_q_heads, np, d->cache.head_dim) +
+         pa::ws_ml_bytes(d->batch, d->num_q_heads, np);
+}
+
+}  // namespace
+
+PA_EXPORT const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+PA_EXPORT int32_t pa_last_hip_error(void) { return g_last_hip_error; }
+
+PA_EXPORT pa_status pa_kv_append(const pa_cache_desc* cache, int32_t num_tokens,
+                                 const void* k_new, const void* v_new,
+                                 const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                 void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_INVALID_ARG;
+  pa::AppendArgs a;
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
+  a.slots = slot_mapping;
+  a.k_cache = static_cast<uint8_t*>(k_cache);
+  a.v_cache = static_cast<uint8_t*>(v_cache);
+  a.num_slots = (int64_t)cache->num_blocks * pa::kBlock;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  const int eb = cache->kv_dtype == PA_FP8_E4M3 ? 1 : 2;
+  hipError_t e = pa::launch_append(a, num_tokens, eb, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+PA_EXPORT size_t pa_decode_workspace_size(const pa_decode_desc* desc) {
+  if (check_decode_desc(desc) != PA_OK) return 0;
+  return workspace_bytes_of(desc);
+}
+
+PA_EXPORT int32_t pa_decode_partition_tokens(const pa_decode_desc* desc) {
+  if (check_decode_desc(desc) != PA_OK) return 0;
+  return choose_partition(desc);
+}
+
+PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cache,
+                              const void* v_cache, const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  pa_status s = check_decode_desc(desc);
+  if (s != PA_OK) return s;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  const bool fp8 = desc->cache.kv_dtype == PA_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return PA_ERR_INVALID_ARG;
+  if (!fp8 && (k_scale || v_scale)) return PA_ERR_INVALID_ARG;
+
+  const int P = choose_partition(desc);
+  const int np = np_max_of(desc, P);
+  const size_t need = workspace_bytes_of(desc);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return PA_ERR_WORKSPACE;
+
+  pa::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws_acc = nullptr;
+  a.ws_ml = nullptr;
+  if (need > 0) {
+    a.ws_acc = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(
+        static_cast<char*>(workspace) +
+        pa::ws_acc_bytes(desc->batch, desc->num_q_heads, np, desc->cache.head_dim));
+  }
+  a.batch = desc->batch;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->cache.num_kv_heads;
+  a.group = desc->num_q_heads / desc->cache.num_kv_heads;
+  a.num_blocks = desc->cache.num_blocks;
+  a.max_blocks_per_seq = desc->max_blocks_per_seq;
+  a.len_cap = len_cap(desc);
+  a.partition = P;
+  a.np_max = np;
+  a.qk_scale_log2 = scale * 1.4426950408889634f;
+
+  hipError_t e = pa::launch_decode(a, desc->cache.head_dim, desc->q_dtype, desc->cache.kv_dtype,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}

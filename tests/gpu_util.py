@@ -1,0 +1,101 @@
+"""Helpers for the GPU parity tests: move a workload to the device, run the library through its
+C ABI binding, and compare with the fp64 oracle under the stated tolerance."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_31_amd as pa
+
+ATOL = 2e-3
+RTOL = 2e-3
+TORCH_BITS = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def dev_bits(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Raw storage bits -> a device tensor of the storage dtype (fp8 stays uint8)."""
+    a = np.ascontiguousarray(arr)
+    if dtype == "fp8_e4m3":
+        return torch.from_numpy(a.view(np.uint8)).to(device)
+    return torch.from_numpy(a.view(np.int16)).view(TORCH_BITS[dtype]).to(device)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return t.view(torch.uint8).numpy().copy()
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+class Dev:
+    """A workload resident on the GPU."""
+
+    def __init__(self, wl, device="cuda"):
+        s = wl.spec
+        self.wl = wl
+        self.q = dev_bits(wl.q, s.q_dtype, device)
+        self.k_cache = dev_bits(wl.k_cache, s.kv_dtype, device)
+        self.v_cache = dev_bits(wl.v_cache, s.kv_dtype, device)
+        self.k_new = dev_bits(wl.k_new, s.kv_dtype, device)
+        self.v_new = dev_bits(wl.v_new, s.kv_dtype, device)
+        self.slots = torch.from_numpy(wl.slot_mapping).to(device)
+        self.tables = torch.from_numpy(wl.block_tables).to(device)
+        self.lens = torch.from_numpy(wl.context_lens).to(device)
+        self.k_scale = None if wl.k_scale is None else torch.from_numpy(wl.k_scale).to(device)
+        self.v_scale = None if wl.v_scale is None else torch.from_numpy(wl.v_scale).to(device)
+        self.out = torch.empty_like(self.q)
+
+    def append(self):
+        pa.pa_kv_append(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache)
+
+    def decode(self, partition_tokens=None, max_context_len=None):
+        wl = self.wl
+        P = wl.spec.partition_tokens if partition_tokens is None else partition_tokens
+        mcl = wl.max_context_len if max_context_len is None else max_context_len
+        pa.pa_decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(wl.scale),
+                     self.out, k_scale=self.k_scale, v_scale=self.v_scale,
+                     max_context_len=mcl, partition_tokens=P)
+        torch.cuda.synchronize()
+        return host_bits(self.out)
+
+
+def oracle_after_append(wl):
+    k, v = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
+    ref = oracle.decode(wl.q, k, v, wl.block_tables, wl.context_lens, wl.scale, wl.spec.q_dtype,
+                        wl.spec.kv_dtype, wl.k_scale, wl.v_scale)
+    return ref, k, v
+
+
+def half_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
+    mant = 7 if dtype == "bf16" else 10
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - mant - 1), 0.0)
+
+
+def assert_close(out_bits: np.ndarray, ref: np.ndarray, dtype: str, label: str = ""):
+    """|gpu - ref| <= 2e-3 + 2e-3 |ref| against the unrounded fp64 reference.  An element that
+    misses that bound only because the output format cannot hold ref more closely (within half
+    an output ulp, plus fp32 slack) is counted as rounding-limited instead of failing."""
+    got = oracle.to_f64(out_bits, dtype)
+    assert got.shape == ref.shape
+    err = np.abs(got - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    ok = err <= bound
+    rounding = ~ok & (err <= half_ulp(ref, dtype) + 1e-5 * np.abs(ref) + 1e-7)
+    bad = ~(ok | rounding)
+    rel = err / np.maximum(np.abs(ref), 1e-3)
+    stats = dict(max_abs=float(err.max(initial=0)), max_rel=float(rel.max(initial=0)),
+                 rounding_limited=int(rounding.sum()), n=int(err.size))
+    print(f"[parity] {label} {stats}", file=sys.stderr, flush=True)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        detail = [(tuple(i), float(got[tuple(i)]), float(ref[tuple(i)])) for i in idx]
+        raise AssertionError(f"{label}: {int(bad.sum())} elements out of tolerance, e.g. {detail}"
+                             f"; {stats}")
+    assert np.isfinite(got).all()
+    return stats
