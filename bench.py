@@ -136,7 +136,6 @@ def main() -> int:
 
     P = s.partition_tokens if args.partition is None else args.partition
     desc = pa.decode_desc(base["q"], base["k"], tables, wl.max_context_len, P)
-    P_used = pa.pa_decode_partition_tokens(desc)
     ws_bytes = pa.pa_decode_workspace_size(desc)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     scale = float(wl.scale)
@@ -174,7 +173,7 @@ def main() -> int:
 
     achieved = bytes_decode / dec_s / 1e9
     value = (bytes_decode + bytes_append) / (ms_per_step / 1e3) / 1e9
-    kernel = "decode_partition_kernel" + (" + merge_kernel" if ws_bytes else "")
+    kernel = "decode_kernel + merge_kernel"
     lens_np = wl.context_lens
     result = {
         "metric": METRIC,
@@ -194,7 +193,7 @@ def main() -> int:
             "head_dim": D, "block_size": 16, "q_dtype": s.q_dtype, "kv_dtype": s.kv_dtype,
             "context_len_min": int(lens_np.min()), "context_len_max": int(lens_np.max()),
             "context_tokens": int(lens_np.sum()), "unique_tokens": int(wl.unique_tokens),
-            "num_blocks": wl.num_blocks, "partition_tokens": P_used, "rotations": R,
+            "num_blocks": wl.num_blocks, "partition_tokens": P or "balanced", "rotations": R,
             "step": "pa_kv_append (1 token per sequence) + pa_decode",
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),

@@ -13,8 +13,9 @@
  *    scattered physical blocks (kasblo.com, "PagedAttentionはKV Cacheをblockで管理する";
  *    youngju.dev guide, PagedAttention block-table figure), with grouped-query heads
  *    (Scaling Book note, "生成スループット/レイテンシ改善のテクニック") and an online softmax
- *    (babushkai.com "GPU推論の内部構造", FlashAttention section).  Long contexts are split into
- *    key partitions whose partial results are merged by log-sum-exp.
+ *    (babushkai.com "GPU推論の内部構造", FlashAttention section).  The keys of the whole batch
+ *    are split into chunks of equal length, one per GPU wave, whatever the mix of context
+ *    lengths; a sequence cut between chunks has its partial results merged by log-sum-exp.
  *
  * Cache layout (one "tile" = one physical block of one KV head, contiguous in memory):
  *   k_cache  [num_blocks][num_kv_heads][16][head_dim]   token-major: a token's K row is contiguous
@@ -27,8 +28,8 @@
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  *
  * Ownership and execution: every data pointer is a device pointer owned by the caller.  The
- * library never allocates or frees memory and keeps no state besides a thread-local copy of the
- * last HIP error.  Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream)
+ * library never allocates or frees memory; its only state is a thread-local copy of the last HIP
+ * error and a per-device cache of the compute-unit count and kernel occupancy.  Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream)
  * and return without synchronising; the caller orders and synchronises.
  *
  * Errors: conditions the host can see (null pointers, non-positive sizes, unsupported shapes or
@@ -80,8 +81,9 @@ typedef struct pa_decode_desc {
   int32_t max_blocks_per_seq; /* row length (stride) of block_tables, > 0 */
   int32_t max_context_len;    /* host-side upper bound on context_lens; sizes the launch without
                                  reading device memory.  0 = max_blocks_per_seq * 16. */
-  int32_t partition_tokens;   /* split-KV key partition: a multiple of 32 in [32, 4096]; 0 = the
-                                 library chooses (pa_decode_partition_tokens reports the choice) */
+  int32_t partition_tokens;   /* split-KV chunk length in tokens, a multiple of 32 in [32, 65536];
+                                 0 = chunks of equal length balanced over the GPU's resident
+                                 waves (the default, best for ragged batches) */
   int32_t q_dtype;            /* PA_F16 or PA_BF16; the output has the same dtype */
 } pa_decode_desc;
 
@@ -118,24 +120,25 @@ pa_status pa_kv_append(const pa_cache_desc* cache, int32_t num_tokens,
  *   out           [batch][num_q_heads][head_dim] of q_dtype, 16-byte aligned, written (rounded to
  *                 nearest even from fp32); a sequence with context length 0 gets zeros
  *   workspace     device scratch of at least pa_decode_workspace_size(desc) bytes, 16-byte
- *                 aligned; may be NULL when that size is 0.  Its contents need no initialisation
- *                 and are garbage afterwards.  Two calls in flight must not share it.
+ *                 aligned (never NULL).  Its contents need no initialisation and are garbage
+ *                 afterwards.  Two calls in flight must not share it.
  *
  * Supported pairs (q_dtype, kv_dtype): (F16, F16), (BF16, BF16), (BF16, FP8_E4M3),
- * (F16, FP8_E4M3).  Accumulation is fp32.  Results depend only on logical token positions, so
- * the same data behind any physical block placement gives bit-identical output.
+ * (F16, FP8_E4M3).  Accumulation is fp32.  Results depend only on logical token positions and
+ * on the context lengths of the batch (which set the chunk boundaries), so the same data behind
+ * any physical block placement gives bit-identical output.  Two kernels are enqueued: the
+ * chunked attention and the log-sum-exp merge (which also writes the zero rows).
  */
 pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cache,
                     const void* v_cache, const float* k_scale, const float* v_scale,
                     const int32_t* block_tables, const int32_t* context_lens, float scale,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pa_decode needs for this descriptor (0 when no sequence can span more than
- * one key partition).  Returns 0 for an invalid descriptor as well; pa_decode reports that. */
+/* Bytes of workspace pa_decode needs for this descriptor, or 0 if the descriptor is invalid
+ * (pa_decode reports why).  It depends only on the descriptor, not on the GPU:
+ * 256 + 4*batch + chunks * 2 * group * (head_dim + 2) * 4 bytes (each part rounded up to 256),
+ * where chunks <= 8192 when partition_tokens is 0. */
 size_t pa_decode_workspace_size(const pa_decode_desc* desc);
-
-/* The key-partition length pa_decode will use for this descriptor, or 0 if it is invalid. */
-int32_t pa_decode_partition_tokens(const pa_decode_desc* desc);
 
 /* A static, human-readable name for a status code. */
 const char* pa_status_string(pa_status status);

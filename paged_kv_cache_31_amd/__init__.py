@@ -52,8 +52,8 @@ class PaError(RuntimeError):
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ("pa_kv_append", "pa_decode", "pa_decode_workspace_size",
-           "pa_decode_partition_tokens", "pa_status_string", "pa_last_hip_error")
+EXPORTS = ("pa_kv_append", "pa_decode", "pa_decode_workspace_size", "pa_status_string",
+           "pa_last_hip_error")
 
 
 def lib() -> ctypes.CDLL:
@@ -72,8 +72,6 @@ def lib() -> ctypes.CDLL:
             L.pa_decode.restype = i32
             L.pa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc)]
             L.pa_decode_workspace_size.restype = sz
-            L.pa_decode_partition_tokens.argtypes = [ctypes.POINTER(DecodeDesc)]
-            L.pa_decode_partition_tokens.restype = i32
             L.pa_status_string.argtypes = [i32]
             L.pa_status_string.restype = ctypes.c_char_p
             L.pa_last_hip_error.argtypes = []
@@ -139,10 +137,6 @@ def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_tokens=0)
 
 def pa_decode_workspace_size(desc: DecodeDesc) -> int:
     return int(lib().pa_decode_workspace_size(ctypes.byref(desc)))
-
-
-def pa_decode_partition_tokens(desc: DecodeDesc) -> int:
-    return int(lib().pa_decode_partition_tokens(ctypes.byref(desc)))
 
 
 _workspaces: dict = {}

@@ -10,27 +10,31 @@
 //
 // Design for CDNA4.  Decode attention streams every K/V byte once at about one flop per byte
 // (Scaling Book note, "Attention のボトルネック"), so the kernel is HBM-bound and is built around
-// keeping enough 16-byte loads in flight.  The matrix cores are used because they make the
-// arithmetic nearly free, not because the work is a large GEMM: one 16x16x32 MFMA covers 16
-// tokens x 32 dims for up to 16 query heads of a group, so the vector ALUs are left with the
-// softmax only.
+// keeping enough 16-byte loads in flight on every CU, whatever the length mix of the batch.
 //
-//  * Workgroup = 4 waves = one (key partition, KV head, sequence).  The partition's tokens are cut
-//    into 32-token steps (two blocks); wave w takes steps w, w+4, ...  Partials of the 4 waves are
-//    merged through LDS; partials of several partitions go to the workspace and are merged by
-//    log-sum-exp in merge_kernel.  Reduction order depends only on logical token positions.
-//  * QK: S^T = K . Q^T.  The K tile (token-major) is loaded straight into the MFMA A operand:
-//    lane (row r = lane%16, group g = lane/16) reads 16 contiguous bytes of token row r, so each
-//    instruction fetches 64 contiguous bytes of 16 token rows.  Rows of the two MFMAs of a step are
-//    assigned so that the result layout (lane holds head lane%16, rows 4g..4g+3) is directly the
-//    B operand of the P.V product -- no shuffles between QK and PV.
-//  * PV: O^T = V^T . P^T.  V tiles are stored dim-major ([d][16 tokens]), so the A operand (row d,
-//    8 consecutive tokens) is one 16-byte load and an instruction fetches 2 x 512 contiguous bytes.
-//    P is fed as a bf16 hi/lo pair (two MFMAs) so the weights keep ~16 significant bits; fp16 P is
-//    used as is.
+//  * Balanced split-KV.  The (sequence, KV head, logical block) space is flattened into W blocks
+//    and cut into equal chunks, one per wave, so every wave streams the same number of bytes
+//    regardless of how ragged the batch is, and a launch is about one wave per resident slot
+//    (no empty workgroups).  Each workgroup finds its waves' chunk starts with a prefix scan of
+//    the context lengths.  A wave walks its chunk piece by piece (a piece = the part of one
+//    (sequence, KV head) inside the chunk): a piece that is a whole sequence head is normalised
+//    and written out; a cut piece writes its running max, exp-sum and unnormalised output to the
+//    workspace, and merge_kernel combines the pieces of each sequence head by log-sum-exp in
+//    logical token order.  Nothing depends on the physical block ids, so results are identical
+//    for any block placement.
+//  * Matrix cores make the arithmetic nearly free: one 16x16x32 MFMA covers 16 tokens x 32 dims
+//    for up to 16 query heads of a group, leaving only the softmax on the vector ALUs.
+//    QK: S^T = K . Q^T with the K tile (token-major) loaded straight into the A operand: lane
+//    (row r = lane%16, group g = lane/16) reads 16 contiguous bytes of token row r.  The rows of a
+//    step's two MFMAs are assigned so that the result layout (lane holds head lane%16, rows
+//    4g..4g+3) is exactly the B operand of the P.V product.
+//    PV: O^T = V^T . P^T.  V tiles are dim-major ([d][16 tokens]), so the A operand (row d, 8
+//    consecutive tokens) is one 16-byte load.  P goes in as a bf16 hi/lo pair (two MFMAs), keeping
+//    ~16 significant bits of each weight; fp16 P is used as is.
 //  * fp8 (OCP e4m3fn) tiles are widened exactly to the MFMA type in registers; the K block scale
-//    multiplies the scores and the V block scale the weights.
-//  * Double-buffered steps: the loads of step s+4 are issued before step s is computed.
+//    multiplies the scores, the V block scale the weights.
+//  * A step is 32 tokens (two blocks); the loads of step s+1 are in flight while step s is
+//    computed, and the block ids of step s+2 are fetched with scalar loads meanwhile.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -64,8 +68,12 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   return (uint32_t)ua | ((uint32_t)ub << 16);
 }
 
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+__device__ __forceinline__ int blocks_of(int L) { return (L + kBlock - 1) / kBlock; }
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <int D, int QT, int KVT>
-__global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   typedef Mfma<QT> M;
   typedef typename M::vec8 V8;
   typedef typename M::elem E;
@@ -77,61 +85,74 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
   constexpr int KL = FP8 ? NC / 2 : NC;           // K loads per row set
   constexpr int TILE = kBlock * D * EB;           // bytes of one (block, kv head) tile
 
-  __shared__ int sm_tab[kMaxPartition / kBlock];
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ f32x4 sm_acc[kWaves][NT][64];
+  __shared__ int sm_wave_sum[kWaves];
+  __shared__ int sm_start_b[kWaves], sm_start_off[kWaves];
 
-  const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int wave = uniform(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int G = a.group, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-  const int h0 = kvh * G;
+  const int B = a.batch, Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = a.group;
+  const int cap = a.len_cap;
 
-  int L = a.context_lens[b];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int P = a.partition;
-  const int start = p * P;
-  if (L == 0) {
-    // No tokens: the output is defined as zeros (written once, by partition 0).
-    if (p == 0) {
-      E* o = reinterpret_cast<E*>(a.out) + ((size_t)b * Hq + h0) * D;
-      for (int e = tid; e < G * D; e += blockDim.x) o[e] = (E)0.0f;
-    }
-    return;
+  // ---- 1. Flattened block space and this workgroup's chunk starts.
+  // Thread t owns sequences [t*per, t*per + per); W = sum_b Hkv * blocks(L_b).
+  const int per = (B + 255) >> 8;
+  const int b_lo = tid * per;
+  int tot = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b_lo + i;
+    if (b < B) tot += Hkv * blocks_of(clamp_len(a.context_lens[b], cap));
   }
-  if (start >= L) return;
-  const int end = min(start + P, L);
-  const int np_b = (L + P - 1) / P;
-  const int nsteps = (end - start + kStepTokens - 1) / kStepTokens;
-  const int nblk_seq = (L + kBlock - 1) / kBlock;
-  const int blk0 = start / kBlock;
-
-  // Stage this partition's block ids in LDS.  Entries past the sequence's last block (the second
-  // block of a final half-step) reuse the partition's first block, so no unread table entry is
-  // ever dereferenced; ids outside the pool read block 0.
-  const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  for (int e = tid; e < 2 * nsteps; e += blockDim.x) {
-    const int lb = blk0 + e;
-    const int id = trow[lb < nblk_seq ? lb : blk0];
-    sm_tab[e] = (unsigned)id < (unsigned)a.num_blocks ? id : 0;
-  }
-
-  // Q^T as the B operand of the QK product: lane (head col, group grp) holds 8 dims per chunk.
-  // fp8 tiles pair chunks (2c, 2c+1) in one 16-byte load, which permutes which dims a lane holds
-  // for each chunk; Q is loaded with the same permutation.
-  V8 qB[NC];
-  {
-    const E* qrow = reinterpret_cast<const E*>(a.q) + ((size_t)b * Hq + h0 + col) * D;
+  int incl = tot;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int d0 = FP8 ? 64 * (c >> 1) + 16 * grp + 8 * (c & 1) : 32 * c + 8 * grp;
-      qB[c] = col < G ? as_vec8<V8>(*reinterpret_cast<const uint4*>(qrow + d0)) : zero_vec8<V8>();
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) sm_wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0, W = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = sm_wave_sum[w];
+    before += w < wave ? v : 0;
+    W += v;
+  }
+  int Cw = a.chunk_blocks;
+  if (Cw == 0) {
+    Cw = (W + a.total_waves - 1) / a.total_waves;
+    Cw = max(2, (Cw + 1) & ~1);
+  }
+  const int nch = (W + Cw - 1) / Cw;
+  const int c_first = blockIdx.x * kWaves;
+  {
+    int run = before + incl - tot;                // blocks before this thread's first sequence
+    for (int i = 0; i < per; ++i) {
+      const int b = b_lo + i;
+      if (b >= B) break;
+      const int nb = Hkv * blocks_of(clamp_len(a.context_lens[b], cap));
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const long start = (long)(c_first + w) * Cw;
+        if (start >= run && start < run + nb) {
+          sm_start_b[w] = b;
+          sm_start_off[w] = (int)(start - run);
+        }
+      }
+      if (blockIdx.x == 0) a.ws_prefix[b] = run;
+      run += nb;
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+      a.ws_hdr[0] = W;
+      a.ws_hdr[1] = Cw;
     }
   }
   __syncthreads();
 
+  const int c = c_first + wave;
+  if (c >= nch) return;
+
+  // ---- 2. This wave's chunk [a0, a1) of the flattened space, piece by piece.
   const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v_cache);
   // K row r = col of MFMA m holds token 16*(r/8) + 8*((r/4)%2) + 4*m + r%4 of the step; its block
@@ -143,245 +164,334 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
   const bool v_hi = grp >= 2;
   const int tb_lane = 16 * (grp >> 1) + 8 * (grp & 1);
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto issue = [&](StepRegs<D, FP8>& r, int s) {
-    const int pb0 = sm_tab[2 * s], pb1 = sm_tab[2 * s + 1];
-    const int kb = k_hi ? pb1 : pb0;
-    const int vb = v_hi ? pb1 : pb0;
-    const uint8_t* kp = kc + ((size_t)kb * Hkv + kvh) * TILE + k_lane_off;
-    const uint8_t* vp = vc + ((size_t)vb * Hkv + kvh) * TILE + v_lane_off;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int c = 0; c < KL; ++c)
-        r.k[m][c] = *reinterpret_cast<const uint4*>(kp + m * 4 * D * EB + c * 64);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      if constexpr (FP8)
-        r.v[i] = *reinterpret_cast<const uint2*>(vp + i * 16 * kBlock * EB);
-      else
-        r.v[i] = *reinterpret_cast<const uint4*>(vp + i * 16 * kBlock * EB);
-    }
-    if constexpr (FP8) {
-      r.ks = a.k_scale[(size_t)vb * Hkv + kvh];
-      r.vs = a.v_scale[(size_t)vb * Hkv + kvh];
-    }
-  };
-
-  auto compute = [&](StepRegs<D, FP8>& r, int s) {
-    const int t0 = start + kStepTokens * s;
-    const int tb = t0 + tb_lane;
-    const bool partial = t0 + kStepTokens > L;     // wave-uniform
-
-    // scores of 8 tokens (tb + j) for head col
-    f32x4 S[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      S[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        V8 kA;
-        if constexpr (FP8) {
-          const uint4 w = r.k[m][c >> 1];
-          kA = (c & 1) ? fp8x8_to_vec8<QT>(w.z, w.w) : fp8x8_to_vec8<QT>(w.x, w.y);
-        } else {
-          kA = as_vec8<V8>(r.k[m][c]);
-        }
-        S[m] = M::mma(kA, qB[c], S[m]);
-      }
-    }
-    float qs = a.qk_scale_log2;
-    if constexpr (FP8) qs *= r.ks;
-    float sc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sc[j] = S[j >> 2][j & 3] * qs;
-    int nval = 8;
-    if (partial) {
-      nval = min(max(L - tb, 0), 8);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j >= nval) sc[j] = -INFINITY;
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
-    mx = max_across_rows(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    float pr[8], psum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pr[j] = fast_exp2(sc[j] - m_new);
-      psum += pr[j];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) acc[i] *= alpha;
-    if constexpr (FP8) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pr[j] *= r.vs;
-    }
-
-    // P^T as the B operand: this lane's 8 weights, in token order.
-    uint4 hi_bits, lo_bits;
-    {
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        h[w] = pack2<QT>(pr[2 * w], pr[2 * w + 1]);
-        if constexpr (SPLIT_P) {
-          const V8 hv = as_vec8<V8>(make_uint4(h[w], 0u, 0u, 0u));
-          l[w] = pack2<QT>(pr[2 * w] - (float)hv[0], pr[2 * w + 1] - (float)hv[1]);
-        }
-      }
-      hi_bits = make_uint4(h[0], h[1], h[2], h[3]);
-      if constexpr (SPLIT_P) lo_bits = make_uint4(l[0], l[1], l[2], l[3]);
-    }
-    const V8 pHi = as_vec8<V8>(hi_bits);
-    V8 pLo;
-    if constexpr (SPLIT_P) pLo = as_vec8<V8>(lo_bits);
-
-    // Masked tokens contribute weight 0, but their cache slots may hold anything (NaN
-    // included), so their V elements are zeroed before the product.
-    uint32_t vm[4] = {~0u, ~0u, ~0u, ~0u};
-    if (partial) {
-      if constexpr (FP8) {
-        vm[0] = nval >= 4 ? ~0u : (nval <= 0 ? 0u : (1u << (8 * nval)) - 1u);
-        vm[1] = nval >= 8 ? ~0u : (nval <= 4 ? 0u : (1u << (8 * (nval - 4))) - 1u);
-      } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          vm[w] = (2 * w < nval ? 0x0000FFFFu : 0u) | (2 * w + 1 < nval ? 0xFFFF0000u : 0u);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      V8 vA;
-      if constexpr (FP8) {
-        vA = fp8x8_to_vec8<QT>(r.v[i].x & vm[0], r.v[i].y & vm[1]);
-      } else {
-        const uint4 u = r.v[i];
-        vA = as_vec8<V8>(make_uint4(u.x & vm[0], u.y & vm[1], u.z & vm[2], u.w & vm[3]));
-      }
-      acc[i] = M::mma(vA, pHi, acc[i]);
-      if constexpr (SPLIT_P) acc[i] = M::mma(vA, pLo, acc[i]);
-    }
-  };
-
+  const int a0 = c * Cw;
+  const int a1 = min(a0 + Cw, W);
+  int b = uniform(sm_start_b[wave]);
+  int L = clamp_len(a.context_lens[b], cap);
+  int nblk = blocks_of(L);
+  int kvh, j;
   {
-    // Steps of this wave: wave, wave+4, ...  The steady-state loop issues the next step's loads
-    // unconditionally (the tail is peeled), so the loads of step s+4 stay in flight while step s
-    // is computed.
-    StepRegs<D, FP8> r0, r1;
-    int s = wave;
-    if (s < nsteps) {
-      int rest = (nsteps - 1 - s) / kWaves;   // steps after the first one
-      issue(r0, s);
-      for (; rest >= 2; rest -= 2, s += 2 * kWaves) {
-        issue(r1, s + kWaves);
+    const int off = uniform(sm_start_off[wave]);
+    kvh = off / nblk;
+    j = off - kvh * nblk;
+  }
+  int pos = a0;
+  for (int piece = 0;; ++piece) {
+    const int j0 = j;
+    const int j1 = min(nblk, j0 + (a1 - pos));
+    const int end_tok = j1 == nblk ? L : kBlock * j1;   // tokens at or past end_tok are masked
+    const int nsteps = (j1 - j0 + 1) >> 1;
+    const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+    const int h0 = kvh * G;
+
+    // Q^T as the B operand of the QK product: lane (head col, group grp) holds 8 dims per
+    // chunk.  fp8 tiles pair chunks (2c, 2c+1) in one 16-byte load, which permutes which dims a
+    // lane holds for each chunk; Q is loaded with the same permutation.
+    V8 qB[NC];
+    {
+      const E* qrow = reinterpret_cast<const E*>(a.q) + ((size_t)b * Hq + h0 + col) * D;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const int d0 = FP8 ? 64 * (cc >> 1) + 16 * grp + 8 * (cc & 1) : 32 * cc + 8 * grp;
+        qB[cc] = col < G ? as_vec8<V8>(*reinterpret_cast<const uint4*>(qrow + d0))
+                         : zero_vec8<V8>();
+      }
+    }
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Block ids of a step: logical blocks j0+2s and j0+2s+1 (the second one repeats the first
+    // when the piece ends after one block; its tokens are masked).  Ids outside the pool read
+    // block 0.
+    auto ids_of = [&](int s, int& p0, int& p1) {
+      s = min(s, nsteps - 1);
+      const int jb = j0 + 2 * s;
+      const int jb1 = jb + 1 < j1 ? jb + 1 : jb;
+      const int i0 = trow[jb], i1 = trow[jb1];
+      p0 = (unsigned)i0 < (unsigned)a.num_blocks ? i0 : 0;
+      p1 = (unsigned)i1 < (unsigned)a.num_blocks ? i1 : 0;
+    };
+    int nid0, nid1;
+    ids_of(0, nid0, nid1);
+
+    auto issue = [&](StepRegs<D, FP8>& r, int s) {
+      const int pb0 = nid0, pb1 = nid1;
+      ids_of(s + 1, nid0, nid1);                   // prefetch the next step's block ids
+      const int kb = k_hi ? pb1 : pb0;
+      const int vb = v_hi ? pb1 : pb0;
+      const uint8_t* kp = kc + ((size_t)kb * Hkv + kvh) * TILE + k_lane_off;
+      const uint8_t* vp = vc + ((size_t)vb * Hkv + kvh) * TILE + v_lane_off;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int cc = 0; cc < KL; ++cc)
+          r.k[m][cc] = *reinterpret_cast<const uint4*>(kp + m * 4 * D * EB + cc * 64);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if constexpr (FP8)
+          r.v[i] = *reinterpret_cast<const uint2*>(vp + i * 16 * kBlock * EB);
+        else
+          r.v[i] = *reinterpret_cast<const uint4*>(vp + i * 16 * kBlock * EB);
+      }
+      if constexpr (FP8) {
+        r.ks = a.k_scale[(size_t)vb * Hkv + kvh];
+        r.vs = a.v_scale[(size_t)vb * Hkv + kvh];
+      }
+    };
+
+    auto compute = [&](StepRegs<D, FP8>& r, int s) {
+      const int t0 = kBlock * (j0 + 2 * s);
+      const int tb = t0 + tb_lane;
+      const bool partial = t0 + kStepTokens > end_tok;     // wave-uniform
+
+      // scores of 8 tokens (tb + jj) for head col
+      f32x4 S[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        S[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          V8 kA;
+          if constexpr (FP8) {
+            const uint4 w = r.k[m][cc >> 1];
+            kA = (cc & 1) ? fp8x8_to_vec8<QT>(w.z, w.w) : fp8x8_to_vec8<QT>(w.x, w.y);
+          } else {
+            kA = as_vec8<V8>(r.k[m][cc]);
+          }
+          S[m] = M::mma(kA, qB[cc], S[m]);
+        }
+      }
+      float qs = a.qk_scale_log2;
+      if constexpr (FP8) qs *= r.ks;
+      float sc[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) sc[jj] = S[jj >> 2][jj & 3] * qs;
+      int nval = 8;
+      if (partial) {
+        nval = min(max(end_tok - tb, 0), 8);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (jj >= nval) sc[jj] = -INFINITY;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
+      mx = max_across_rows(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      float pr[8], psum = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        pr[jj] = fast_exp2(sc[jj] - m_new);
+        psum += pr[jj];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[i] *= alpha;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pr[jj] *= r.vs;
+      }
+
+      // P^T as the B operand: this lane's 8 weights, in token order.
+      uint4 hi_bits, lo_bits;
+      {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          h[w] = pack2<QT>(pr[2 * w], pr[2 * w + 1]);
+          if constexpr (SPLIT_P) {
+            const V8 hv = as_vec8<V8>(make_uint4(h[w], 0u, 0u, 0u));
+            l[w] = pack2<QT>(pr[2 * w] - (float)hv[0], pr[2 * w + 1] - (float)hv[1]);
+          }
+        }
+        hi_bits = make_uint4(h[0], h[1], h[2], h[3]);
+        if constexpr (SPLIT_P) lo_bits = make_uint4(l[0], l[1], l[2], l[3]);
+      }
+      const V8 pHi = as_vec8<V8>(hi_bits);
+      V8 pLo;
+      if constexpr (SPLIT_P) pLo = as_vec8<V8>(lo_bits);
+
+      // Masked tokens get weight 0, but their cache slots may hold anything (NaN included), so
+      // their V elements are zeroed before the product.
+      uint32_t vm[4] = {~0u, ~0u, ~0u, ~0u};
+      if (partial) {
+        if constexpr (FP8) {
+          vm[0] = nval >= 4 ? ~0u : (nval <= 0 ? 0u : (1u << (8 * nval)) - 1u);
+          vm[1] = nval >= 8 ? ~0u : (nval <= 4 ? 0u : (1u << (8 * (nval - 4))) - 1u);
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            vm[w] = (2 * w < nval ? 0x0000FFFFu : 0u) | (2 * w + 1 < nval ? 0xFFFF0000u : 0u);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        V8 vA;
+        if constexpr (FP8) {
+          vA = fp8x8_to_vec8<QT>(r.v[i].x & vm[0], r.v[i].y & vm[1]);
+        } else {
+          const uint4 u = r.v[i];
+          vA = as_vec8<V8>(make_uint4(u.x & vm[0], u.y & vm[1], u.z & vm[2], u.w & vm[3]));
+        }
+        acc[i] = M::mma(vA, pHi, acc[i]);
+        if constexpr (SPLIT_P) acc[i] = M::mma(vA, pLo, acc[i]);
+      }
+    };
+
+    {
+      // The steady-state loop issues the next step's loads unconditionally (the tail is
+      // peeled), so the loads of step s+1 stay in flight while step s is computed.
+      StepRegs<D, FP8> r0, r1;
+      int s = 0, rest = nsteps - 1;
+      issue(r0, 0);
+      for (; rest >= 2; rest -= 2, s += 2) {
+        issue(r1, s + 1);
         compute(r0, s);
-        issue(r0, s + 2 * kWaves);
-        compute(r1, s + kWaves);
+        issue(r0, s + 2);
+        compute(r1, s + 1);
       }
       if (rest == 1) {
-        issue(r1, s + kWaves);
+        issue(r1, s + 1);
         compute(r0, s);
-        compute(r1, s + kWaves);
+        compute(r1, s + 1);
       } else {
         compute(r0, s);
       }
     }
-  }
 
-  // Merge the four waves' partials of this partition.
-  l_run = sum_across_rows(l_run);
-  if (grp == 0) {
-    sm_m[wave][col] = m_run;
-    sm_l[wave][col] = l_run;
-  }
-#pragma unroll
-  for (int i = 0; i < NT; ++i) sm_acc[wave][i][lane] = acc[i];
-  __syncthreads();
-
-  float wgt[kWaves], M_ = -INFINITY;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) {
-    wgt[v] = sm_m[v][col];
-    M_ = fmaxf(M_, wgt[v]);
-  }
-  float Ls = 0.0f;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) {
-    wgt[v] = wgt[v] == -INFINITY ? 0.0f : fast_exp2(wgt[v] - M_);
-    Ls += wgt[v] * sm_l[v][col];
-  }
-  const int h = h0 + col;
-  for (int i = wave; i < NT; i += kWaves) {
-    f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) o += wgt[v] * sm_acc[v][i][lane];
+    // ---- finish the piece: whole sequence head -> output; cut piece -> workspace slot
+    l_run = sum_across_rows(l_run);
     if (col < G) {
-      const int d = 16 * i + 4 * grp;
-      if (np_b == 1) {
-        E* out = reinterpret_cast<E*>(a.out) + ((size_t)b * Hq + h) * D + d;
-        *reinterpret_cast<uint2*>(out) =
-            make_uint2(pack2<QT>(o[0] / Ls, o[1] / Ls), pack2<QT>(o[2] / Ls, o[3] / Ls));
+      const int h = h0 + col;
+      if (j0 == 0 && j1 == nblk) {
+        E* out = reinterpret_cast<E*>(a.out) + ((size_t)b * Hq + h) * D + 4 * grp;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+          *reinterpret_cast<uint2*>(out + 16 * i) =
+              make_uint2(pack2<QT>(acc[i][0] / l_run, acc[i][1] / l_run),
+                         pack2<QT>(acc[i][2] / l_run, acc[i][3] / l_run));
       } else {
-        float* w = a.ws_acc + (((size_t)b * Hq + h) * a.np_max + p) * D + d;
-        *reinterpret_cast<f32x4*>(w) = o;
+        const size_t slot = ((size_t)c * 2 + (piece == 0 ? 0 : 1)) * G + col;
+        float* w = a.ws_acc + slot * D + 4 * grp;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) *reinterpret_cast<f32x4*>(w + 16 * i) = acc[i];
+        if (grp == 0) {
+          a.ws_ml[slot * 2] = m_run;
+          a.ws_ml[slot * 2 + 1] = l_run;
+        }
       }
     }
-  }
-  if (np_b > 1 && wave == 0 && grp == 0 && col < G) {
-    float* ml = a.ws_ml + (((size_t)b * Hq + h) * a.np_max + p) * 2;
-    ml[0] = M_;
-    ml[1] = Ls;
+
+    pos += j1 - j0;
+    if (pos >= a1) break;
+    // next piece: the next KV head of this sequence, else the next sequence with tokens
+    j = 0;
+    if (++kvh == Hkv) {
+      // pos < a1 <= W guarantees a later sequence with tokens; the bound on b only keeps the
+      // walk inside the lengths array should they change while the kernel runs
+      kvh = 0;
+      L = 0;
+      while (L == 0 && b + 1 < B) L = clamp_len(a.context_lens[++b], cap);
+      if (L == 0) break;
+      nblk = blocks_of(L);
+    }
   }
 }
 
-// Log-sum-exp merge of the key partitions of one (sequence, query head):
-//   out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j,  M = max_j m_j  (m in log2 units).
+// Log-sum-exp merge of the cut pieces of one (sequence, KV head), in logical token order:
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p  (m in log2 units).
+// Also writes zeros for sequences without tokens.
+// Grid: (KV head, sequence, slice of 64 four-element columns of the group's G x D outputs).
+// Thread (column, lane group q) folds pieces q, q+4, ... with its own running max, then the four
+// partial results of a column are combined through LDS in q order, so the result is fixed.
+constexpr int kMergeCols = 64;
+constexpr int kMergeSplit = 4;
+
 template <int D, int QT>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeCols * kMergeSplit) void merge_kernel(DecodeArgs a) {
   typedef typename Mfma<QT>::elem E;
-  constexpr int PER = D / 64;
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  int L = a.context_lens[b];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int P = a.partition;
-  if (L <= P) return;   // a single partition wrote its output directly
-  const int np = (L + P - 1) / P;
-  const size_t row = ((size_t)b * a.num_q_heads + h) * a.np_max;
-  float M_ = -INFINITY;
-  for (int j = 0; j < np; ++j) M_ = fmaxf(M_, a.ws_ml[(row + j) * 2]);
-  float o[PER], Ls = 0.0f;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.0f;
-  for (int j = 0; j < np; ++j) {
-    const float w = fast_exp2(a.ws_ml[(row + j) * 2] - M_);
-    Ls += w * a.ws_ml[(row + j) * 2 + 1];
-    const float* src = a.ws_acc + (row + j) * D + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] += w * src[e];
+  __shared__ float sm_m[kMergeSplit][kMergeCols], sm_l[kMergeSplit][kMergeCols];
+  __shared__ f32x4 sm_o[kMergeSplit][kMergeCols];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int G = a.group;
+  const int colx = threadIdx.x % kMergeCols, q = threadIdx.x / kMergeCols;
+  const int e = (blockIdx.z * kMergeCols + colx) * 4;      // element of the G x D rows
+  const bool live = e < G * D;
+  const int L = clamp_len(a.context_lens[b], a.len_cap);
+  const int nblk = blocks_of(L);
+  E* out = reinterpret_cast<E*>(a.out) + ((size_t)b * a.num_q_heads + kvh * G) * D + e;
+  if (nblk == 0) {
+    if (live && q == 0) *reinterpret_cast<uint2*>(out) = make_uint2(0u, 0u);
+    return;
   }
-  E* out = reinterpret_cast<E*>(a.out) + ((size_t)b * a.num_q_heads + h) * D + lane * PER;
+  const int Cw = a.ws_hdr[1];
+  const int s0 = a.ws_prefix[b] + kvh * nblk;
+  const int c0 = s0 / Cw, c1 = (s0 + nblk - 1) / Cw;
+  if (c0 == c1) return;                     // one whole piece: written by decode_kernel
+  // chunk c0 holds this piece as its first piece (slot 0) only if the piece starts the chunk
+  const int first_slot = s0 != c0 * Cw ? 1 : 0;
+  const int g = live ? e / D : 0, d = e - g * D;
+  auto slot_of = [&](int cc) {
+    return ((size_t)cc * 2 + (cc == c0 ? first_slot : 0)) * G + g;
+  };
+  float M_ = -INFINITY;
+  for (int cc = c0 + q; cc <= c1; cc += kMergeSplit) M_ = fmaxf(M_, a.ws_ml[slot_of(cc) * 2]);
+  f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float Ls = 0.0f;
+  if (live) {
+#pragma unroll 4
+    for (int cc = c0 + q; cc <= c1; cc += kMergeSplit) {
+      const size_t sl = slot_of(cc);
+      const float w = fast_exp2(a.ws_ml[sl * 2] - M_);
+      Ls += w * a.ws_ml[sl * 2 + 1];
+      o += w * *reinterpret_cast<const f32x4*>(a.ws_acc + sl * D + d);
+    }
+  }
+  sm_m[q][colx] = M_;
+  sm_l[q][colx] = Ls;
+  sm_o[q][colx] = o;
+  __syncthreads();
+  if (q != 0 || !live) return;
+  float Mt = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) out[e] = (E)(o[e] / Ls);
+  for (int k = 0; k < kMergeSplit; ++k) Mt = fmaxf(Mt, sm_m[k][colx]);
+  f32x4 ot = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float Lt = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMergeSplit; ++k) {
+    const float mk = sm_m[k][colx];
+    const float w = mk == -INFINITY ? 0.0f : fast_exp2(mk - Mt);
+    Lt += w * sm_l[k][colx];
+    ot += w * sm_o[k][colx];
+  }
+  *reinterpret_cast<uint2*>(out) =
+      make_uint2(pack2<QT>(ot[0] / Lt, ot[1] / Lt), pack2<QT>(ot[2] / Lt, ot[3] / Lt));
 }
 
 template <int D, int QT, int KVT>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_partition_kernel<D, QT, KVT>),
-                     dim3(a.np_max, a.num_kv_heads, a.batch), dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<D, QT, KVT>), dim3(a.total_waves / kWaves), dim3(64 * kWaves),
+                     0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.np_max == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<D, QT>), dim3(a.num_q_heads, a.batch), dim3(64), 0, stream, a);
+  if (e != hipSuccess) return e;
+  const int slices = (a.group * D / 4 + kMergeCols - 1) / kMergeCols;
+  hipLaunchKernelGGL((merge_kernel<D, QT>), dim3(a.num_kv_heads, a.batch, slices),
+                     dim3(kMergeCols * kMergeSplit), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, int QT, int KVT>
+static int occupancy_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, QT, KVT>, 64 * kWaves, 0)
+      != hipSuccess)
+    return 0;
+  return n;
 }
 
 template <int D>
@@ -391,6 +501,20 @@ static hipError_t launch_d(const DecodeArgs& a, int q_dtype, int kv_dtype, hipSt
   if (q_dtype == DT_BF16 && kv_dtype == DT_FP8) return launch_t<D, DT_BF16, DT_FP8>(a, stream);
   if (q_dtype == DT_F16 && kv_dtype == DT_FP8) return launch_t<D, DT_F16, DT_FP8>(a, stream);
   return hipErrorInvalidValue;
+}
+
+template <int D>
+static int occupancy_d(int q_dtype, int kv_dtype) {
+  if (q_dtype == DT_F16 && kv_dtype == DT_F16) return occupancy_t<D, DT_F16, DT_F16>();
+  if (q_dtype == DT_BF16 && kv_dtype == DT_BF16) return occupancy_t<D, DT_BF16, DT_BF16>();
+  if (q_dtype == DT_BF16 && kv_dtype == DT_FP8) return occupancy_t<D, DT_BF16, DT_FP8>();
+  if (q_dtype == DT_F16 && kv_dtype == DT_FP8) return occupancy_t<D, DT_F16, DT_FP8>();
+  return 0;
+}
+
+int decode_workgroups_per_cu(int head_dim, int q_dtype, int kv_dtype) {
+  return head_dim == 64 ? occupancy_d<64>(q_dtype, kv_dtype)
+                        : occupancy_d<128>(q_dtype, kv_dtype);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,

@@ -3,6 +3,10 @@
 // reads device memory or synchronises.
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "pa.h"
 #include "pa_internal.hpp"
 
@@ -25,6 +29,8 @@ pa_status check_cache(const pa_cache_desc* c) {
   return PA_OK;
 }
 
+int64_t blocks_upper(const pa_decode_desc* d);
+
 pa_status check_decode_desc(const pa_decode_desc* d) {
   if (!d) return PA_ERR_INVALID_ARG;
   pa_status s = check_cache(&d->cache);
@@ -39,6 +45,7 @@ pa_status check_decode_desc(const pa_decode_desc* d) {
   if (d->partition_tokens != 0 &&
       (d->partition_tokens % pa::kStepTokens != 0 || d->partition_tokens > pa::kMaxPartition))
     return PA_ERR_INVALID_ARG;
+  if (blocks_upper(d) >= INT32_MAX) return PA_ERR_UNSUPPORTED;   // flattened index is 32-bit
   if (d->q_dtype != PA_F16 && d->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   const int kv = d->cache.kv_dtype;
   if (kv != PA_FP8_E4M3 && kv != d->q_dtype) return PA_ERR_UNSUPPORTED;
@@ -54,24 +61,52 @@ int len_cap(const pa_decode_desc* d) {
   return (int)cap;
 }
 
-// Partition length when the caller leaves it to the library: 512 tokens (16 steps, 4 per wave).
-int choose_partition(const pa_decode_desc* d) {
-  if (d->partition_tokens > 0) return d->partition_tokens;
-  return 512;
+// Upper bound of the flattened (sequence, KV head, block) space.
+int64_t blocks_upper(const pa_decode_desc* d) {
+  return (int64_t)d->batch * d->cache.num_kv_heads * ((len_cap(d) + pa::kBlock - 1) / pa::kBlock);
 }
 
-int np_max_of(const pa_decode_desc* d, int partition) {
-  const int cap = len_cap(d);
-  const int np = (cap + partition - 1) / partition;
-  return np < 1 ? 1 : np;
+// Chunks (= waves) the workspace must hold.  Fixed partitions: every chunk of the upper bound.
+// Balanced mode: one chunk per launched wave, at most kMaxWaves and never more than the space
+// has two-block chunks.
+int64_t chunk_capacity(const pa_decode_desc* d) {
+  const int64_t W = blocks_upper(d);
+  int64_t n;
+  if (d->partition_tokens > 0) {
+    const int64_t cw = d->partition_tokens / pa::kBlock;
+    n = (W + cw - 1) / cw;
+  } else {
+    n = (W + 1) / 2;
+    if (n > pa::kMaxWaves) n = pa::kMaxWaves;
+  }
+  if (n < 1) n = 1;
+  return (n + pa::kWaves - 1) / pa::kWaves * pa::kWaves;
 }
 
 size_t workspace_bytes_of(const pa_decode_desc* d) {
-  const int P = choose_partition(d);
-  const int np = np_max_of(d, P);
-  if (np == 1) return 0;
-  return pa::ws_acc_bytes(d->batch, d->num_q_heads, np, d->cache.head_dim) +
-         pa::ws_ml_bytes(d->batch, d->num_q_heads, np);
+  return pa::workspace_layout(d->batch, d->num_q_heads / d->cache.num_kv_heads,
+                              d->cache.head_dim, chunk_capacity(d)).total;
+}
+
+// Resident decode waves on the current device for this kernel instance, cached per device.
+int64_t resident_waves(const pa_decode_desc* d) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int>, int64_t> cache;
+  const auto key = std::make_tuple(dev, (int)d->cache.head_dim, (int)d->q_dtype,
+                                   (int)d->cache.kv_dtype);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const int per_cu = pa::decode_workgroups_per_cu(d->cache.head_dim, d->q_dtype,
+                                                  d->cache.kv_dtype);
+  const int64_t waves = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1) * pa::kWaves;
+  cache[key] = waves;
+  return waves;
 }
 
 }  // namespace
@@ -124,11 +159,6 @@ PA_EXPORT size_t pa_decode_workspace_size(const pa_decode_desc* desc) {
   return workspace_bytes_of(desc);
 }
 
-PA_EXPORT int32_t pa_decode_partition_tokens(const pa_decode_desc* desc) {
-  if (check_decode_desc(desc) != PA_OK) return 0;
-  return choose_partition(desc);
-}
-
 PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cache,
                               const void* v_cache, const float* k_scale, const float* v_scale,
                               const int32_t* block_tables, const int32_t* context_lens,
@@ -146,11 +176,20 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
     return PA_ERR_INVALID_ARG;
   if (!fp8 && (k_scale || v_scale)) return PA_ERR_INVALID_ARG;
 
-  const int P = choose_partition(desc);
-  const int np = np_max_of(desc, P);
   const size_t need = workspace_bytes_of(desc);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
-    return PA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return PA_ERR_WORKSPACE;
+
+  const int64_t cap_chunks = chunk_capacity(desc);
+  int64_t waves = cap_chunks;
+  if (desc->partition_tokens == 0) {
+    const int64_t resident = resident_waves(desc);
+    if (resident > 0 && resident < waves) waves = resident / pa::kWaves * pa::kWaves;
+    if (waves < pa::kWaves) waves = pa::kWaves;
+  }
+  const pa::WorkspaceLayout lay =
+      pa::workspace_layout(desc->batch, desc->num_q_heads / desc->cache.num_kv_heads,
+                           desc->cache.head_dim, cap_chunks);
+  char* ws = static_cast<char*>(workspace);
 
   pa::DecodeArgs a;
   a.q = q;
@@ -161,14 +200,10 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  a.ws_acc = nullptr;
-  a.ws_ml = nullptr;
-  if (need > 0) {
-    a.ws_acc = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float*>(
-        static_cast<char*>(workspace) +
-        pa::ws_acc_bytes(desc->batch, desc->num_q_heads, np, desc->cache.head_dim));
-  }
+  a.ws_hdr = reinterpret_cast<int*>(ws);
+  a.ws_prefix = reinterpret_cast<int*>(ws + lay.prefix);
+  a.ws_acc = reinterpret_cast<float*>(ws + lay.acc);
+  a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
   a.batch = desc->batch;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->cache.num_kv_heads;
@@ -176,8 +211,8 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   a.num_blocks = desc->cache.num_blocks;
   a.max_blocks_per_seq = desc->max_blocks_per_seq;
   a.len_cap = len_cap(desc);
-  a.partition = P;
-  a.np_max = np;
+  a.chunk_blocks = desc->partition_tokens / pa::kBlock;
+  a.total_waves = (int)waves;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
 
   hipError_t e = pa::launch_decode(a, desc->cache.head_dim, desc->q_dtype, desc->cache.kv_dtype,

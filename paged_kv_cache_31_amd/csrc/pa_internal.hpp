@@ -10,7 +10,7 @@ namespace pa {
 constexpr int kBlock = 16;          // tokens per physical KV block
 constexpr int kStepTokens = 32;     // tokens one wave consumes per step (two blocks)
 constexpr int kWaves = 4;           // waves per decode workgroup
-constexpr int kMaxPartition = 4096; // largest key partition (block ids staged in LDS)
+constexpr int kMaxPartition = 65536; // largest fixed key partition (tokens)
 
 struct AppendArgs {
   const uint8_t* k_new;
@@ -32,8 +32,10 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* ws_acc;        // [batch][num_q_heads][np_max][head_dim]
-  float* ws_ml;         // [batch][num_q_heads][np_max][2]: running max (log2 units), exp-sum
+  int* ws_hdr;          // [0] flattened blocks W, [1] chunk length in blocks
+  int* ws_prefix;       // [batch]: flattened blocks before sequence b (num_kv_heads per block)
+  float* ws_acc;        // [chunks][2][group][head_dim]: unnormalised output of a cut piece
+  float* ws_ml;         // [chunks][2][group][2]: running max (log2 units), exp-sum
   int batch;
   int num_q_heads;
   int num_kv_heads;
@@ -41,23 +43,33 @@ struct DecodeArgs {
   int num_blocks;
   int max_blocks_per_seq;
   int len_cap;          // context lengths are clamped to [0, len_cap]
-  int partition;        // key-partition length in tokens (multiple of 32)
-  int np_max;           // partitions launched per (sequence, kv head)
+  int chunk_blocks;     // fixed chunk length in blocks (even), or 0: balanced over total_waves
+  int total_waves;      // waves launched (4 per workgroup); chunk c is wave c's
   float qk_scale_log2;  // scale * log2(e)
 };
 
-// Workspace split: acc floats first, then (m, l) pairs, each 256-byte aligned.
-inline size_t ws_acc_bytes(int batch, int hq, int np_max, int head_dim) {
-  size_t b = (size_t)batch * hq * np_max * head_dim * sizeof(float);
-  return (b + 255) & ~(size_t)255;
+// Workspace: header, per-sequence prefix, then two partial slots per chunk; each part 256-byte
+// aligned.
+struct WorkspaceLayout {
+  size_t prefix, acc, ml, total;
+};
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline WorkspaceLayout workspace_layout(int batch, int group, int head_dim, long chunks) {
+  WorkspaceLayout w;
+  w.prefix = 256;
+  w.acc = w.prefix + align256((size_t)batch * sizeof(int));
+  w.ml = w.acc + align256((size_t)chunks * 2 * group * head_dim * sizeof(float));
+  w.total = w.ml + align256((size_t)chunks * 2 * group * 2 * sizeof(float));
+  return w;
 }
-inline size_t ws_ml_bytes(int batch, int hq, int np_max) {
-  size_t b = (size_t)batch * hq * np_max * 2 * sizeof(float);
-  return (b + 255) & ~(size_t)255;
-}
+
+// Waves launched by the balanced mode never exceed this (a workspace bound known without a GPU).
+constexpr long kMaxWaves = 8192;
 
 hipError_t launch_append(const AppendArgs& a, int num_tokens, int elem_bytes, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
                          hipStream_t stream);
+// Resident decode workgroups per CU for this kernel instance (0 if the query fails).
+int decode_workgroups_per_cu(int head_dim, int q_dtype, int kv_dtype);
 
 }  // namespace pa

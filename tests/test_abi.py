@@ -61,7 +61,7 @@ def _decode(desc, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, tab=FAKE, lens=FAKE,
     (dict(num_q_heads=34), pa.PA_ERR_UNSUPPORTED),         # group of 17
     (dict(batch=0), pa.PA_ERR_INVALID_ARG),
     (dict(partition_tokens=48), pa.PA_ERR_INVALID_ARG),    # not a multiple of 32
-    (dict(partition_tokens=8192), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=65568), pa.PA_ERR_INVALID_ARG),
     (dict(q_dtype=pa.PA_FP8_E4M3), pa.PA_ERR_UNSUPPORTED),
     (dict(kv_dtype=pa.PA_F16), pa.PA_ERR_UNSUPPORTED),     # bf16 q with f16 cache
     (dict(kv_dtype=7), pa.PA_ERR_INVALID_ARG),
@@ -70,7 +70,6 @@ def test_decode_rejects_descriptor(kw, status):
     d = _desc(**kw)
     assert _decode(d) == status
     assert pa.pa_decode_workspace_size(d) == 0
-    assert pa.pa_decode_partition_tokens(d) == 0
 
 
 def test_decode_rejects_pointers():
@@ -83,22 +82,31 @@ def test_decode_rejects_pointers():
     assert _decode(d8) == pa.PA_ERR_INVALID_ARG                                # fp8 w/o scales
 
 
+def _r(x):
+    return (x + 255) // 256 * 256
+
+
 def test_workspace_size_and_check():
-    d = _desc(max_context_len=100)                     # one partition of 512: no workspace
-    assert pa.pa_decode_workspace_size(d) == 0
-    assert pa.pa_decode_partition_tokens(d) == 512
+    # fixed chunks of 32 tokens (2 blocks): the upper bound of the flattened space is
+    # 4 sequences x 2 kv heads x ceil(100/16)=7 blocks = 56 blocks -> 28 chunks
     d = _desc(max_context_len=100, partition_tokens=32)
-    np_ = 4                                             # ceil(100 / 32)
-    acc = 4 * 8 * np_ * 64 * 4
-    ml = 4 * 8 * np_ * 2 * 4
-    r = lambda x: (x + 255) // 256 * 256
-    assert pa.pa_decode_workspace_size(d) == r(acc) + r(ml)
+    chunks = 28
+    expect = 256 + _r(4 * 4) + _r(chunks * 2 * 4 * 64 * 4) + _r(chunks * 2 * 4 * 2 * 4)
+    assert pa.pa_decode_workspace_size(d) == expect
+    # balanced chunks: one per two-block slice of the space, rounded up to whole workgroups
+    d = _desc(max_context_len=100)
+    chunks = 28
+    expect = 256 + _r(4 * 4) + _r(chunks * 2 * 4 * 64 * 4) + _r(chunks * 2 * 4 * 2 * 4)
+    assert pa.pa_decode_workspace_size(d) == expect
     assert _decode(d) == pa.PA_ERR_WORKSPACE
     assert _decode(d, ws=FAKE, wsb=100) == pa.PA_ERR_WORKSPACE
-    # a longer hint never shrinks the workspace; the table bounds the launch
-    sizes = [pa.pa_decode_workspace_size(_desc(max_context_len=L, partition_tokens=32))
-             for L in (32, 64, 100, 112, 500)]
-    assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]    # capped at 7 blocks = 112 tokens
+    # a longer hint never shrinks the workspace; the table row (7 blocks) caps it
+    sizes = [pa.pa_decode_workspace_size(_desc(max_context_len=L)) for L in (32, 64, 100, 112, 500)]
+    assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]
+    # balanced mode never needs more than 8192 chunks
+    big = _desc(batch=4096, num_blocks=1 << 20, max_blocks_per_seq=4096)
+    cap = 256 + _r(4096 * 4) + _r(8192 * 2 * 4 * 64 * 4) + _r(8192 * 2 * 4 * 2 * 4)
+    assert pa.pa_decode_workspace_size(big) == cap
 
 
 def test_append_rejects():
