@@ -137,7 +137,7 @@ def main() -> int:
     P = s.partition_tokens if args.partition is None else args.partition
     desc = pa.decode_desc(base["q"], base["k"], tables, wl.max_context_len, P)
     ws_bytes = pa.pa_decode_workspace_size(desc)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    workspace = pa.new_workspace(ws_bytes, dev)
     scale = float(wl.scale)
     mcl = wl.max_context_len
 
@@ -173,7 +173,7 @@ def main() -> int:
 
     achieved = bytes_decode / dec_s / 1e9
     value = (bytes_decode + bytes_append) / (ms_per_step / 1e3) / 1e9
-    kernel = "decode_kernel + merge_kernel"
+    kernel = "decode_kernel"
     lens_np = wl.context_lens
     result = {
         "metric": METRIC,

@@ -120,14 +120,15 @@ pa_status pa_kv_append(const pa_cache_desc* cache, int32_t num_tokens,
  *   out           [batch][num_q_heads][head_dim] of q_dtype, 16-byte aligned, written (rounded to
  *                 nearest even from fp32); a sequence with context length 0 gets zeros
  *   workspace     device scratch of at least pa_decode_workspace_size(desc) bytes, 16-byte
- *                 aligned (never NULL).  Its contents need no initialisation and are garbage
- *                 afterwards.  Two calls in flight must not share it.
+ *                 aligned (never NULL), zero-filled once before its first use.  Its first
+ *                 256 KiB hold arrival counters that every call leaves at zero again, so one
+ *                 workspace serves any later call whatever its descriptor; the rest is scratch.
+ *                 Calls that share a workspace must not overlap (same stream, or synchronised).
  *
  * Supported pairs (q_dtype, kv_dtype): (F16, F16), (BF16, BF16), (BF16, FP8_E4M3),
  * (F16, FP8_E4M3).  Accumulation is fp32.  Results depend only on logical token positions and
  * on the context lengths of the batch (which set the chunk boundaries), so the same data behind
- * any physical block placement gives bit-identical output.  Two kernels are enqueued: the
- * chunked attention and the log-sum-exp merge (which also writes the zero rows).
+ * any physical block placement gives bit-identical output.  One kernel is enqueued.
  */
 pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cache,
                     const void* v_cache, const float* k_scale, const float* v_scale,
@@ -136,8 +137,8 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
 
 /* Bytes of workspace pa_decode needs for this descriptor, or 0 if the descriptor is invalid
  * (pa_decode reports why).  It depends only on the descriptor, not on the GPU:
- * 256 + 4*batch + chunks * 2 * group * (head_dim + 2) * 4 bytes (each part rounded up to 256),
- * where chunks <= 8192 when partition_tokens is 0. */
+ * 262144 + workgroups * 2 * group * (head_dim + 2) * 4 bytes (each part rounded up to 256),
+ * with workgroups <= 2048 when partition_tokens is 0. */
 size_t pa_decode_workspace_size(const pa_decode_desc* desc);
 
 /* A static, human-readable name for a status code. */

@@ -142,13 +142,16 @@ def pa_decode_workspace_size(desc: DecodeDesc) -> int:
 _workspaces: dict = {}
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A pa_decode workspace: zero-filled once (the kernel keeps its counters at zero)."""
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def _workspace(nbytes: int, device, stream_handle: int):
-    if nbytes == 0:
-        return None
     key = (device, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = new_workspace(nbytes, device)
         _workspaces[key] = ws
     return ws
 

@@ -18,10 +18,16 @@
 //    (no empty workgroups).  Each workgroup finds its waves' chunk starts with a prefix scan of
 //    the context lengths.  A wave walks its chunk piece by piece (a piece = the part of one
 //    (sequence, KV head) inside the chunk): a piece that is a whole sequence head is normalised
-//    and written out; a cut piece writes its running max, exp-sum and unnormalised output to the
-//    workspace, and merge_kernel combines the pieces of each sequence head by log-sum-exp in
-//    logical token order.  Nothing depends on the physical block ids, so results are identical
-//    for any block placement.
+//    and written out; a cut piece keeps its running max, exp-sum and unnormalised output.
+//  * Log-sum-exp merge in two levels, inside this one kernel.  The four waves of a workgroup own
+//    four consecutive chunks; their cut pieces meet in LDS and are merged in chunk order, so a
+//    sequence head that ends inside the workgroup is written out there.  A piece cut at a
+//    workgroup boundary is published to the workspace with device-coherent stores, and an atomic
+//    counter per boundary elects the last workgroup to arrive, which reads all parts of that
+//    sequence head back with device-coherent loads, merges them in logical order and resets the
+//    counter.  (A device-scope fence would write back or invalidate the whole L2 of the XCD,
+//    which costs far more than the merge itself.)  Nothing depends on the physical
+//    block ids, so results are identical for any block placement.
 //  * Matrix cores make the arithmetic nearly free: one 16x16x32 MFMA covers 16 tokens x 32 dims
 //    for up to 16 query heads of a group, leaving only the softmax on the vector ALUs.
 //    QK: S^T = K . Q^T with the K tile (token-major) loaded straight into the A operand: lane
@@ -72,6 +78,11 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 __device__ __forceinline__ int blocks_of(int L) { return (L + kBlock - 1) / kBlock; }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// A cut piece parked in LDS for the workgroup-level merge.
+struct PieceMeta {
+  int b, kvh, j0, j1, nblk, s0;   // s0: flattened index of the sequence head's first block
+};
+
 template <int D, int QT, int KVT>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   typedef Mfma<QT> M;
@@ -85,8 +96,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   constexpr int KL = FP8 ? NC / 2 : NC;           // K loads per row set
   constexpr int TILE = kBlock * D * EB;           // bytes of one (block, kv head) tile
 
+  static_assert(NT % kWaves == 0, "the merge phase gives each wave NT/4 tiles");
+  constexpr int TPW = NT / kWaves;
+
   __shared__ int sm_wave_sum[kWaves];
   __shared__ int sm_start_b[kWaves], sm_start_off[kWaves];
+  __shared__ PieceMeta sm_meta[kWaves][2];          // [wave][first / last cut piece]
+  __shared__ float sm_pm[kWaves][2][16], sm_pl[kWaves][2][16];
+  __shared__ f32x4 sm_pacc[kWaves][2][NT][64];
+  __shared__ int sm_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -139,18 +157,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
           sm_start_off[w] = (int)(start - run);
         }
       }
-      if (blockIdx.x == 0) a.ws_prefix[b] = run;
+      if (nb == 0 && blockIdx.x == 0) {           // no tokens: the output rows are zeros
+        uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<E*>(a.out) + (size_t)b * Hq * D);
+        for (int k = 0; k < Hq * D / 8; ++k) o[k] = make_uint4(0u, 0u, 0u, 0u);
+      }
       run += nb;
     }
-    if (blockIdx.x == 0 && tid == 0) {
-      a.ws_hdr[0] = W;
-      a.ws_hdr[1] = Cw;
-    }
   }
+  if (tid < 2 * kWaves) sm_meta[tid >> 1][tid & 1].b = -1;
   __syncthreads();
 
   const int c = c_first + wave;
-  if (c >= nch) return;
 
   // ---- 2. This wave's chunk [a0, a1) of the flattened space, piece by piece.
   const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k_cache);
@@ -166,17 +183,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
   const int a0 = c * Cw;
   const int a1 = min(a0 + Cw, W);
-  int b = uniform(sm_start_b[wave]);
-  int L = clamp_len(a.context_lens[b], cap);
-  int nblk = blocks_of(L);
-  int kvh, j;
-  {
+  int b = 0, L = 0, nblk = 0, kvh = 0, j = 0;
+  if (c < nch) {
+    b = uniform(sm_start_b[wave]);
+    L = clamp_len(a.context_lens[b], cap);
+    nblk = blocks_of(L);
     const int off = uniform(sm_start_off[wave]);
     kvh = off / nblk;
     j = off - kvh * nblk;
   }
   int pos = a0;
-  for (int piece = 0;; ++piece) {
+  for (int piece = 0; c < nch; ++piece) {
     const int j0 = j;
     const int j1 = min(nblk, j0 + (a1 - pos));
     const int end_tok = j1 == nblk ? L : kBlock * j1;   // tokens at or past end_tok are masked
@@ -364,27 +381,26 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- finish the piece: whole sequence head -> output; cut piece -> workspace slot
+    // ---- finish the piece: whole sequence head -> output; cut piece -> LDS slot
     l_run = sum_across_rows(l_run);
-    if (col < G) {
-      const int h = h0 + col;
-      if (j0 == 0 && j1 == nblk) {
-        E* out = reinterpret_cast<E*>(a.out) + ((size_t)b * Hq + h) * D + 4 * grp;
+    if (j0 == 0 && j1 == nblk) {
+      if (col < G) {
+        E* out = reinterpret_cast<E*>(a.out) + ((size_t)b * Hq + h0 + col) * D + 4 * grp;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
           *reinterpret_cast<uint2*>(out + 16 * i) =
               make_uint2(pack2<QT>(acc[i][0] / l_run, acc[i][1] / l_run),
                          pack2<QT>(acc[i][2] / l_run, acc[i][3] / l_run));
-      } else {
-        const size_t slot = ((size_t)c * 2 + (piece == 0 ? 0 : 1)) * G + col;
-        float* w = a.ws_acc + slot * D + 4 * grp;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) *reinterpret_cast<f32x4*>(w + 16 * i) = acc[i];
-        if (grp == 0) {
-          a.ws_ml[slot * 2] = m_run;
-          a.ws_ml[slot * 2 + 1] = l_run;
-        }
       }
+    } else {
+      const int sl = piece == 0 ? 0 : 1;          // only a chunk's first and last can be cut
+      if (lane == 0) sm_meta[wave][sl] = PieceMeta{b, kvh, j0, j1, nblk, pos - j0};
+      if (grp == 0) {
+        sm_pm[wave][sl][col] = m_run;
+        sm_pl[wave][sl][col] = l_run;
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) sm_pacc[wave][sl][i][lane] = acc[i];
     }
 
     pos += j1 - j0;
@@ -401,87 +417,118 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       nblk = blocks_of(L);
     }
   }
-}
+  __syncthreads();
 
-// Log-sum-exp merge of the cut pieces of one (sequence, KV head), in logical token order:
-//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p  (m in log2 units).
-// Also writes zeros for sequences without tokens.
-// Grid: (KV head, sequence, slice of 64 four-element columns of the group's G x D outputs).
-// Thread (column, lane group q) folds pieces q, q+4, ... with its own running max, then the four
-// partial results of a column are combined through LDS in q order, so the result is fixed.
-constexpr int kMergeCols = 64;
-constexpr int kMergeSplit = 4;
+  // ---- 3. Merge the cut pieces of the four chunks, in chunk order.  Each wave now handles
+  // tiles wave, wave+4, ... of every piece.  A group of parts of one sequence head that covers
+  // all its blocks is written out; a group cut at the workgroup boundary is published and the
+  // last workgroup to publish a part of that sequence head merges all of them.
+  const int WGB = kWaves * Cw;                      // blocks per workgroup range
+  int gb = -1, gkvh = 0, gj0 = 0, gj1 = 0, gnblk = 0, gs0 = 0;
+  float gm = -INFINITY, gl = 0.0f;
+  f32x4 go[TPW];
 
-template <int D, int QT>
-__global__ __launch_bounds__(kMergeCols * kMergeSplit) void merge_kernel(DecodeArgs a) {
-  typedef typename Mfma<QT>::elem E;
-  __shared__ float sm_m[kMergeSplit][kMergeCols], sm_l[kMergeSplit][kMergeCols];
-  __shared__ f32x4 sm_o[kMergeSplit][kMergeCols];
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int G = a.group;
-  const int colx = threadIdx.x % kMergeCols, q = threadIdx.x / kMergeCols;
-  const int e = (blockIdx.z * kMergeCols + colx) * 4;      // element of the G x D rows
-  const bool live = e < G * D;
-  const int L = clamp_len(a.context_lens[b], a.len_cap);
-  const int nblk = blocks_of(L);
-  E* out = reinterpret_cast<E*>(a.out) + ((size_t)b * a.num_q_heads + kvh * G) * D + e;
-  if (nblk == 0) {
-    if (live && q == 0) *reinterpret_cast<uint2*>(out) = make_uint2(0u, 0u);
-    return;
-  }
-  const int Cw = a.ws_hdr[1];
-  const int s0 = a.ws_prefix[b] + kvh * nblk;
-  const int c0 = s0 / Cw, c1 = (s0 + nblk - 1) / Cw;
-  if (c0 == c1) return;                     // one whole piece: written by decode_kernel
-  // chunk c0 holds this piece as its first piece (slot 0) only if the piece starts the chunk
-  const int first_slot = s0 != c0 * Cw ? 1 : 0;
-  const int g = live ? e / D : 0, d = e - g * D;
-  auto slot_of = [&](int cc) {
-    return ((size_t)cc * 2 + (cc == c0 ? first_slot : 0)) * G + g;
-  };
-  float M_ = -INFINITY;
-  for (int cc = c0 + q; cc <= c1; cc += kMergeSplit) M_ = fmaxf(M_, a.ws_ml[slot_of(cc) * 2]);
-  f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float Ls = 0.0f;
-  if (live) {
+  auto merge_published = [&](int c0, int c1) {
+    // parts of sequence head (gb, gkvh) published by workgroups c0..c1; workgroup c0 holds it as
+    // its first group (slot 0) only if the sequence head starts exactly at its range
+    const int first_slot = gs0 != c0 * WGB ? 1 : 0;
+    E* rows = reinterpret_cast<E*>(a.out) + ((size_t)gb * Hq + gkvh * G) * D;
+    for (int e = tid * 4; e < G * D; e += blockDim.x * 4) {
+      const int g = e / D, d = e - g * D;
+      auto slot_of = [&](int cc) {
+        return ((size_t)cc * 2 + (cc == c0 ? first_slot : 0)) * G + g;
+      };
+      float M_ = -INFINITY;
+      for (int cc = c0; cc <= c1; ++cc) M_ = fmaxf(M_, load_coherent(a.ws_ml + slot_of(cc) * 2));
+      f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      float Ls = 0.0f;
 #pragma unroll 4
-    for (int cc = c0 + q; cc <= c1; cc += kMergeSplit) {
-      const size_t sl = slot_of(cc);
-      const float w = fast_exp2(a.ws_ml[sl * 2] - M_);
-      Ls += w * a.ws_ml[sl * 2 + 1];
-      o += w * *reinterpret_cast<const f32x4*>(a.ws_acc + sl * D + d);
+      for (int cc = c0; cc <= c1; ++cc) {
+        const size_t sl = slot_of(cc);
+        const float w = fast_exp2(load_coherent(a.ws_ml + sl * 2) - M_);
+        Ls += w * load_coherent(a.ws_ml + sl * 2 + 1);
+        o += w * load_coherent4(a.ws_acc + sl * D + d);
+      }
+      *reinterpret_cast<uint2*>(rows + e) =
+          make_uint2(pack2<QT>(o[0] / Ls, o[1] / Ls), pack2<QT>(o[2] / Ls, o[3] / Ls));
+    }
+  };
+
+  auto emit = [&]() {
+    if (gj0 == 0 && gj1 == gnblk) {
+      if (col < G) {
+        E* out = reinterpret_cast<E*>(a.out) + ((size_t)gb * Hq + gkvh * G + col) * D + 4 * grp;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          *reinterpret_cast<uint2*>(out + 16 * (wave + kWaves * t)) =
+              make_uint2(pack2<QT>(go[t][0] / gl, go[t][1] / gl),
+                         pack2<QT>(go[t][2] / gl, go[t][3] / gl));
+      }
+    } else {
+      // slot 1 holds the group whose sequence head starts strictly inside this workgroup's
+      // range (it runs past the end); slot 0 the one that started at or before the range start
+      const int wslot = gs0 > (int)blockIdx.x * WGB ? 1 : 0;
+      const size_t ps = ((size_t)blockIdx.x * 2 + wslot) * G + col;
+      // publish with device-coherent stores, wait for them to complete, then count the part;
+      // the counter's last arrival reads the parts back with device-coherent loads
+      if (col < G) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          store_coherent(a.ws_acc + ps * D + 16 * (wave + kWaves * t) + 4 * grp, go[t]);
+        if (wave == 0 && grp == 0) {
+          store_coherent(a.ws_ml + ps * 2, gm);
+          store_coherent(a.ws_ml + ps * 2 + 1, gl);
+        }
+      }
+      wait_memory_ops();
+      __syncthreads();
+      const int c0 = gs0 / WGB, c1 = (gs0 + gnblk - 1) / WGB;
+      if (tid == 0)
+        sm_last = __hip_atomic_fetch_add(a.ws_cnt + c1, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == c1 - c0;
+      __syncthreads();
+      if (sm_last) {
+        merge_published(c0, c1);
+        if (tid == 0)                                 // ready for the next call
+          __hip_atomic_store(a.ws_cnt + c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+
+  for (int k = 0; k < 2 * kWaves; ++k) {
+    const PieceMeta mt = sm_meta[k >> 1][k & 1];
+    if (mt.b < 0) continue;
+    const float pm = sm_pm[k >> 1][k & 1][col], pl = sm_pl[k >> 1][k & 1][col];
+    if (mt.b == gb && mt.kvh == gkvh) {
+      const float M_ = fmaxf(gm, pm);
+      const float x = fast_exp2(gm - M_), y = fast_exp2(pm - M_);
+      gl = gl * x + pl * y;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        go[t] = go[t] * x + sm_pacc[k >> 1][k & 1][wave + kWaves * t][lane] * y;
+      gm = M_;
+      gj1 = mt.j1;
+    } else {
+      if (gb >= 0) emit();
+      gb = mt.b;
+      gkvh = mt.kvh;
+      gj0 = mt.j0;
+      gj1 = mt.j1;
+      gnblk = mt.nblk;
+      gs0 = mt.s0;
+      gm = pm;
+      gl = pl;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) go[t] = sm_pacc[k >> 1][k & 1][wave + kWaves * t][lane];
     }
   }
-  sm_m[q][colx] = M_;
-  sm_l[q][colx] = Ls;
-  sm_o[q][colx] = o;
-  __syncthreads();
-  if (q != 0 || !live) return;
-  float Mt = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kMergeSplit; ++k) Mt = fmaxf(Mt, sm_m[k][colx]);
-  f32x4 ot = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float Lt = 0.0f;
-#pragma unroll
-  for (int k = 0; k < kMergeSplit; ++k) {
-    const float mk = sm_m[k][colx];
-    const float w = mk == -INFINITY ? 0.0f : fast_exp2(mk - Mt);
-    Lt += w * sm_l[k][colx];
-    ot += w * sm_o[k][colx];
-  }
-  *reinterpret_cast<uint2*>(out) =
-      make_uint2(pack2<QT>(ot[0] / Lt, ot[1] / Lt), pack2<QT>(ot[2] / Lt, ot[3] / Lt));
+  if (gb >= 0) emit();
 }
 
 template <int D, int QT, int KVT>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<D, QT, KVT>), dim3(a.total_waves / kWaves), dim3(64 * kWaves),
                      0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int slices = (a.group * D / 4 + kMergeCols - 1) / kMergeCols;
-  hipLaunchKernelGGL((merge_kernel<D, QT>), dim3(a.num_kv_heads, a.batch, slices),
-                     dim3(kMergeCols * kMergeSplit), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -66,6 +66,34 @@ __device__ __forceinline__ typename Mfma<QT>::vec8 fp8x8_to_vec8(uint32_t w0, ui
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Device-coherent stores and loads (agent-scope relaxed atomics: the L2 is bypassed for
+// visibility across XCDs) for results one workgroup publishes and another reads in the same
+// kernel, without a whole-L2 writeback or invalidate.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float* p, f32x4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_coherent4(const float* p) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+  const f32x2 a = __builtin_bit_cast(
+      f32x2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const f32x2 b = __builtin_bit_cast(
+      f32x2, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return f32x4{a[0], a[1], b[0], b[1]};
+}
+// Wait until this wave's memory operations have completed (stores acknowledged).
+__device__ __forceinline__ void wait_memory_ops() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Butterfly over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float max_across_rows(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));

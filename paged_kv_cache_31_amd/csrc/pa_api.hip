@@ -30,6 +30,7 @@ pa_status check_cache(const pa_cache_desc* c) {
 }
 
 int64_t blocks_upper(const pa_decode_desc* d);
+int64_t chunk_capacity(const pa_decode_desc* d);
 
 pa_status check_decode_desc(const pa_decode_desc* d) {
   if (!d) return PA_ERR_INVALID_ARG;
@@ -46,6 +47,7 @@ pa_status check_decode_desc(const pa_decode_desc* d) {
       (d->partition_tokens % pa::kStepTokens != 0 || d->partition_tokens > pa::kMaxPartition))
     return PA_ERR_INVALID_ARG;
   if (blocks_upper(d) >= INT32_MAX) return PA_ERR_UNSUPPORTED;   // flattened index is 32-bit
+  if (chunk_capacity(d) > pa::kMaxWorkgroups * pa::kWaves) return PA_ERR_UNSUPPORTED;
   if (d->q_dtype != PA_F16 && d->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   const int kv = d->cache.kv_dtype;
   if (kv != PA_FP8_E4M3 && kv != d->q_dtype) return PA_ERR_UNSUPPORTED;
@@ -84,8 +86,8 @@ int64_t chunk_capacity(const pa_decode_desc* d) {
 }
 
 size_t workspace_bytes_of(const pa_decode_desc* d) {
-  return pa::workspace_layout(d->batch, d->num_q_heads / d->cache.num_kv_heads,
-                              d->cache.head_dim, chunk_capacity(d)).total;
+  return pa::workspace_layout(d->num_q_heads / d->cache.num_kv_heads, d->cache.head_dim,
+                              chunk_capacity(d) / pa::kWaves).total;
 }
 
 // Resident decode waves on the current device for this kernel instance, cached per device.
@@ -187,8 +189,8 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
     if (waves < pa::kWaves) waves = pa::kWaves;
   }
   const pa::WorkspaceLayout lay =
-      pa::workspace_layout(desc->batch, desc->num_q_heads / desc->cache.num_kv_heads,
-                           desc->cache.head_dim, cap_chunks);
+      pa::workspace_layout(desc->num_q_heads / desc->cache.num_kv_heads, desc->cache.head_dim,
+                           cap_chunks / pa::kWaves);
   char* ws = static_cast<char*>(workspace);
 
   pa::DecodeArgs a;
@@ -200,8 +202,7 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  a.ws_hdr = reinterpret_cast<int*>(ws);
-  a.ws_prefix = reinterpret_cast<int*>(ws + lay.prefix);
+  a.ws_cnt = reinterpret_cast<int*>(ws);
   a.ws_acc = reinterpret_cast<float*>(ws + lay.acc);
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
   a.batch = desc->batch;

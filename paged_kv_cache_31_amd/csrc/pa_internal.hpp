@@ -32,10 +32,9 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  int* ws_hdr;          // [0] flattened blocks W, [1] chunk length in blocks
-  int* ws_prefix;       // [batch]: flattened blocks before sequence b (num_kv_heads per block)
-  float* ws_acc;        // [chunks][2][group][head_dim]: unnormalised output of a cut piece
-  float* ws_ml;         // [chunks][2][group][2]: running max (log2 units), exp-sum
+  int* ws_cnt;          // [kMaxWorkgroups] arrival counters, zero between calls
+  float* ws_acc;        // [workgroups][2][group][head_dim]: unnormalised output of a cut group
+  float* ws_ml;         // [workgroups][2][group][2]: running max (log2 units), exp-sum
   int batch;
   int num_q_heads;
   int num_kv_heads;
@@ -48,18 +47,19 @@ struct DecodeArgs {
   float qk_scale_log2;  // scale * log2(e)
 };
 
-// Workspace: header, per-sequence prefix, then two partial slots per chunk; each part 256-byte
-// aligned.
+// Workspace: a fixed region of arrival counters (so that their place never depends on the
+// descriptor and a workspace zero-filled once stays valid for every call), then two published
+// partial results per workgroup; each part 256-byte aligned.
+constexpr long kMaxWorkgroups = 65536;
 struct WorkspaceLayout {
-  size_t prefix, acc, ml, total;
+  size_t acc, ml, total;
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline WorkspaceLayout workspace_layout(int batch, int group, int head_dim, long chunks) {
+inline WorkspaceLayout workspace_layout(int group, int head_dim, long workgroups) {
   WorkspaceLayout w;
-  w.prefix = 256;
-  w.acc = w.prefix + align256((size_t)batch * sizeof(int));
-  w.ml = w.acc + align256((size_t)chunks * 2 * group * head_dim * sizeof(float));
-  w.total = w.ml + align256((size_t)chunks * 2 * group * 2 * sizeof(float));
+  w.acc = align256((size_t)kMaxWorkgroups * sizeof(int));
+  w.ml = w.acc + align256((size_t)workgroups * 2 * group * head_dim * sizeof(float));
+  w.total = w.ml + align256((size_t)workgroups * 2 * group * 2 * sizeof(float));
   return w;
 }
 

@@ -86,27 +86,32 @@ def _r(x):
     return (x + 255) // 256 * 256
 
 
+COUNTERS = 65536 * 4
+
+
 def test_workspace_size_and_check():
     # fixed chunks of 32 tokens (2 blocks): the upper bound of the flattened space is
-    # 4 sequences x 2 kv heads x ceil(100/16)=7 blocks = 56 blocks -> 28 chunks
+    # 4 sequences x 2 kv heads x ceil(100/16)=7 blocks = 56 blocks -> 28 chunks -> 7 workgroups
     d = _desc(max_context_len=100, partition_tokens=32)
-    chunks = 28
-    expect = 256 + _r(4 * 4) + _r(chunks * 2 * 4 * 64 * 4) + _r(chunks * 2 * 4 * 2 * 4)
+    wgs = 7
+    expect = COUNTERS + _r(wgs * 2 * 4 * 64 * 4) + _r(wgs * 2 * 4 * 2 * 4)
     assert pa.pa_decode_workspace_size(d) == expect
-    # balanced chunks: one per two-block slice of the space, rounded up to whole workgroups
+    # balanced chunks: at most one per two-block slice of the space
     d = _desc(max_context_len=100)
-    chunks = 28
-    expect = 256 + _r(4 * 4) + _r(chunks * 2 * 4 * 64 * 4) + _r(chunks * 2 * 4 * 2 * 4)
     assert pa.pa_decode_workspace_size(d) == expect
     assert _decode(d) == pa.PA_ERR_WORKSPACE
     assert _decode(d, ws=FAKE, wsb=100) == pa.PA_ERR_WORKSPACE
     # a longer hint never shrinks the workspace; the table row (7 blocks) caps it
     sizes = [pa.pa_decode_workspace_size(_desc(max_context_len=L)) for L in (32, 64, 100, 112, 500)]
     assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]
-    # balanced mode never needs more than 8192 chunks
+    # balanced mode never launches more than 8192 waves = 2048 workgroups
     big = _desc(batch=4096, num_blocks=1 << 20, max_blocks_per_seq=4096)
-    cap = 256 + _r(4096 * 4) + _r(8192 * 2 * 4 * 64 * 4) + _r(8192 * 2 * 4 * 2 * 4)
+    cap = COUNTERS + _r(2048 * 2 * 4 * 64 * 4) + _r(2048 * 2 * 4 * 2 * 4)
     assert pa.pa_decode_workspace_size(big) == cap
+    # fixed partitions beyond 65536 workgroups are refused
+    huge = _desc(batch=4096, num_blocks=1 << 20, max_blocks_per_seq=4096, partition_tokens=32)
+    assert pa.pa_decode_workspace_size(huge) == 0
+    assert _decode(huge) == pa.PA_ERR_UNSUPPORTED
 
 
 def test_append_rejects():
