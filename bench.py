@@ -66,6 +66,42 @@ def cpu_baseline(wl, decode_bytes_fn, append_bytes, min_s: float = 10.0,
                       f"float64 on 1 thread; same byte model as the GPU figure"}
 
 
+def traffic_record(workload: str):
+    """HBM bytes per decode launch measured with rocprofv3 PMC counters (profiles/), reported
+    only while the kernel sources still hash to what they were when the counters were taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!-- traffic-record (\{.*?\}) -->", open(path).read())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device_common.hpp", "pa_internal.hpp"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_31_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_probe(dev) -> int:
+    """A plain device copy of 1 GiB, five times: its HBM byte counters per dispatch, compared
+    with the 1 GiB read and 1 GiB written, give the scale factor for FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,6 +112,8 @@ def main() -> int:
                     help="key-partition tokens (default: the workload's, else the library's)")
     ap.add_argument("--rotations", type=int, default=0, help="pool copies cycled (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -93,6 +131,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        return copy_probe(dev)
     pa.lib()
 
     t0 = time.perf_counter()
@@ -141,37 +181,42 @@ def main() -> int:
     scale = float(wl.scale)
     mcl = wl.max_context_len
 
-    def step(r, ev=None):
-        x = rots[r]
-        pa.pa_kv_append(x["k_new"], x["v_new"], slots, x["k"], x["v"])
-        if ev is not None:
-            ev[0].record()
-        pa.pa_decode(x["q"], x["k"], x["v"], tables, lens, scale, x["out"], k_scale=k_scale,
-                     v_scale=v_scale, max_context_len=mcl, partition_tokens=P,
-                     workspace=workspace)
-        if ev is not None:
-            ev[1].record()
+    appends = [pa.AppendCall(x["k_new"], x["v_new"], slots, x["k"], x["v"]) for x in rots]
+    decodes = [pa.DecodeCall(x["q"], x["k"], x["v"], tables, lens, scale, x["out"],
+                             k_scale=k_scale, v_scale=v_scale, max_context_len=mcl,
+                             partition_tokens=P, workspace=workspace) for x in rots]
+
+    def step(r):
+        appends[r]()
+        decodes[r]()
 
     for i in range(args.warmup):
         step(i % R)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i % R, evs[i])
+        step(i % R)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    decode_ms = np.array([a.elapsed_time(b) for a, b in evs])
     ms_per_step = wall * 1e3 / args.steps
-    dec_s = float(decode_ms.mean()) / 1e3
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, decode "
-        f"{dec_s * 1e6:.1f} us (median {np.median(decode_ms) * 1e3:.1f} us)")
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
-    achieved = bytes_decode / dec_s / 1e9
+    # Per-launch duration of the decode kernel: the same decode calls back to back on the same
+    # stream between two events (per-call events above also count the dispatch latency).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        decodes[i % R]()
+    e1.record()
+    torch.cuda.synchronize()
+    launch_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    log(f"{args.steps} back-to-back decode launches: {launch_s * 1e6:.1f} us each")
+
+    achieved = bytes_decode / launch_s / 1e9
     value = (bytes_decode + bytes_append) / (ms_per_step / 1e3) / 1e9
     kernel = "decode_kernel"
     lens_np = wl.context_lens
@@ -197,15 +242,16 @@ def main() -> int:
             "step": "pa_kv_append (1 token per sequence) + pa_decode",
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
-        "decode_tokens_per_s": round(B / dec_s, 1),
+        "decode_tokens_per_s": round(B / launch_s, 1),
         "step_tokens_per_s": round(B / (ms_per_step / 1e3), 1),
-        "us_per_decode": round(dec_s * 1e6, 2),
-        "us_per_decode_median": round(float(np.median(decode_ms)) * 1e3, 2),
+        "us_per_decode_launch": round(launch_s * 1e6, 2),
         "bytes_per_step": {"decode": bytes_decode, "decode_logical": bytes_decode_logical,
                            "append": bytes_append},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
-                     "kernel": kernel},
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic_record(args.workload),
+                     "kernel": kernel, "bytes_per_launch": bytes_decode,
+                     "duration_us": round(launch_s * 1e6, 2)},
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")

@@ -114,19 +114,33 @@ def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     return CacheDesc(NB, Hkv, D, bs, _dtype_code(k_cache, True))
 
 
+class AppendCall:
+    """pa_kv_append with its arguments marshalled once; calling it only enqueues the kernel."""
+
+    def __init__(self, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None):
+        assert k_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()
+        assert k_new.is_contiguous() and v_new.is_contiguous() and slot_mapping.is_contiguous()
+        assert slot_mapping.dtype == torch.int64
+        NB, Hkv, bs, D = k_cache.shape
+        assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
+        T = slot_mapping.shape[0]
+        assert tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D)
+        assert k_new.element_size() == k_cache.element_size()
+        self._keep = (k_new, v_new, slot_mapping, k_cache, v_cache)
+        self._desc = cache_desc(k_cache)
+        self._fn = lib().pa_kv_append
+        self._args = (ctypes.byref(self._desc), T, _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                      _ptr(k_cache), _ptr(v_cache), _stream(stream))
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check("pa_kv_append", st)
+
+
 def pa_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """Scatter k_new/v_new [T][Hkv][D] into their slots (int64 [T], <0 skips)."""
-    assert k_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()
-    assert k_new.is_contiguous() and v_new.is_contiguous() and slot_mapping.is_contiguous()
-    assert slot_mapping.dtype == torch.int64
-    NB, Hkv, bs, D = k_cache.shape
-    assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
-    T = slot_mapping.shape[0]
-    assert tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D)
-    assert k_new.element_size() == k_cache.element_size()
-    st = lib().pa_kv_append(ctypes.byref(cache_desc(k_cache)), T, _ptr(k_new), _ptr(v_new),
-                            _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _stream(stream))
-    _check("pa_kv_append", st)
+    AppendCall(k_new, v_new, slot_mapping, k_cache, v_cache, stream)()
 
 
 def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_tokens=0) -> DecodeDesc:
@@ -156,26 +170,42 @@ def _workspace(nbytes: int, device, stream_handle: int):
     return ws
 
 
+class DecodeCall:
+    """pa_decode with its arguments marshalled once; calling it only enqueues the kernel."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
+                 v_scale=None, max_context_len=0, partition_tokens=0, workspace=None,
+                 stream=None):
+        for t in (q, k_cache, v_cache, block_tables, context_lens, out):
+            assert t.is_cuda and t.is_contiguous()
+        assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+        assert out.shape == q.shape and out.dtype == q.dtype
+        NB, Hkv, bs, D = k_cache.shape
+        assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
+        assert q.shape[2] == D and context_lens.shape[0] == q.shape[0] == block_tables.shape[0]
+        self._desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens)
+        need = pa_decode_workspace_size(self._desc)
+        st = _stream(stream)
+        if workspace is None:
+            workspace = _workspace(need, q.device, st.value or 0)
+        wbytes = workspace.numel() * workspace.element_size()
+        self._keep = (q, k_cache, v_cache, block_tables, context_lens, out, k_scale, v_scale,
+                      workspace)
+        self._fn = lib().pa_decode
+        self._args = (ctypes.byref(self._desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                      _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+                      ctypes.c_float(scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(wbytes), st)
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check("pa_decode", st)
+
+
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
               v_scale=None, max_context_len=0, partition_tokens=0, workspace=None,
               stream=None) -> torch.Tensor:
     """out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b through the block tables; returns out."""
-    for t in (q, k_cache, v_cache, block_tables, context_lens, out):
-        assert t.is_cuda and t.is_contiguous()
-    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
-    assert out.shape == q.shape and out.dtype == q.dtype
-    NB, Hkv, bs, D = k_cache.shape
-    assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
-    assert q.shape[2] == D and context_lens.shape[0] == q.shape[0] == block_tables.shape[0]
-    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens)
-    need = pa_decode_workspace_size(desc)
-    st = _stream(stream)
-    if workspace is None:
-        workspace = _workspace(need, q.device, st.value or 0)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    status = lib().pa_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                             _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
-                             _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace),
-                             wbytes, st)
-    _check("pa_decode", status)
+    DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
+               max_context_len, partition_tokens, workspace, stream)()
     return out
