@@ -78,6 +78,9 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 __device__ __forceinline__ int blocks_of(int L) { return (L + kBlock - 1) / kBlock; }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Published parts a merging workgroup stages in LDS at once (more are folded in batches).
+constexpr int kMergeStage = 64;
+
 // A cut piece parked in LDS for the workgroup-level merge.
 struct PieceMeta {
   int b, kvh, j0, j1, nblk, s0;   // s0: flattened index of the sequence head's first block
@@ -105,6 +108,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __shared__ float sm_pm[kWaves][2][16], sm_pl[kWaves][2][16];
   __shared__ f32x4 sm_pacc[kWaves][2][NT][64];
   __shared__ int sm_last;
+  __shared__ int sm_start_L[kWaves];
+  __shared__ float sm_mw[kMergeStage][16], sm_ml[kMergeStage][16];   // published parts: m, l
+  __shared__ float sm_hm[16], sm_hl[16];                              // per head: max, exp-sum
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -155,6 +161,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         if (start >= run && start < run + nb) {
           sm_start_b[w] = b;
           sm_start_off[w] = (int)(start - run);
+          sm_start_L[w] = clamp_len(a.context_lens[b], cap);
         }
       }
       if (nb == 0 && blockIdx.x == 0) {           // no tokens: the output rows are zeros
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   int b = 0, L = 0, nblk = 0, kvh = 0, j = 0;
   if (c < nch) {
     b = uniform(sm_start_b[wave]);
-    L = clamp_len(a.context_lens[b], cap);
+    L = uniform(sm_start_L[wave]);
     nblk = blocks_of(L);
     const int off = uniform(sm_start_off[wave]);
     kvh = off / nblk;
@@ -430,27 +437,72 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
   auto merge_published = [&](int c0, int c1) {
     // parts of sequence head (gb, gkvh) published by workgroups c0..c1; workgroup c0 holds it as
-    // its first group (slot 0) only if the sequence head starts exactly at its range
+    // its first group (slot 0) only if the sequence head starts exactly at its range.  Batches of
+    // up to kMergeStage parts: their (max, exp-sum) pairs are staged in LDS with one round of
+    // loads, then every thread loads all its output columns of the batch at once.
     const int first_slot = gs0 != c0 * WGB ? 1 : 0;
+    auto slot_of = [&](int cc, int g) {
+      return ((size_t)cc * 2 + (cc == c0 ? first_slot : 0)) * G + g;
+    };
     E* rows = reinterpret_cast<E*>(a.out) + ((size_t)gb * Hq + gkvh * G) * D;
-    for (int e = tid * 4; e < G * D; e += blockDim.x * 4) {
-      const int g = e / D, d = e - g * D;
-      auto slot_of = [&](int cc) {
-        return ((size_t)cc * 2 + (cc == c0 ? first_slot : 0)) * G + g;
-      };
-      float M_ = -INFINITY;
-      for (int cc = c0; cc <= c1; ++cc) M_ = fmaxf(M_, load_coherent(a.ws_ml + slot_of(cc) * 2));
-      f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      float Ls = 0.0f;
-#pragma unroll 4
-      for (int cc = c0; cc <= c1; ++cc) {
-        const size_t sl = slot_of(cc);
-        const float w = fast_exp2(load_coherent(a.ws_ml + sl * 2) - M_);
-        Ls += w * load_coherent(a.ws_ml + sl * 2 + 1);
-        o += w * load_coherent4(a.ws_acc + sl * D + d);
+    constexpr int EPT = 16 * D / 4 / (64 * kWaves);          // float4 columns per thread (G=16)
+    f32x4 o[EPT > 0 ? EPT : 1];
+#pragma unroll
+    for (int x = 0; x < (EPT > 0 ? EPT : 1); ++x) o[x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (tid < 16) { sm_hm[tid] = -INFINITY; sm_hl[tid] = 0.0f; }
+    for (int cb = c0; cb <= c1; cb += kMergeStage) {
+      const int n = min(kMergeStage, c1 - cb + 1);
+      __syncthreads();
+      for (int t = tid; t < n * G; t += blockDim.x) {
+        const size_t sl = slot_of(cb + t / G, t % G);
+        sm_mw[t / G][t % G] = load_coherent(a.ws_ml + sl * 2);
+        sm_ml[t / G][t % G] = load_coherent(a.ws_ml + sl * 2 + 1);
       }
+      __syncthreads();
+      // per head: new running max; rescale of what is already accumulated
+      if (tid < G) {
+        float M_ = sm_hm[tid];
+        for (int k = 0; k < n; ++k) M_ = fmaxf(M_, sm_mw[k][tid]);
+        const float r = M_ == sm_hm[tid] ? 1.0f : fast_exp2(sm_hm[tid] - M_);
+        float Ls = sm_hl[tid] * r;
+        for (int k = 0; k < n; ++k) {
+          const float w = fast_exp2(sm_mw[k][tid] - M_);
+          sm_mw[k][tid] = w;
+          Ls += w * sm_ml[k][tid];
+        }
+        sm_ml[0][tid] = r;          // rescale factor for this batch (read below)
+        sm_hm[tid] = M_;
+        sm_hl[tid] = Ls;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int x = 0; x < (EPT > 0 ? EPT : 1); ++x) {
+        const int e = (tid + x * blockDim.x) * 4;
+        if (e >= G * D) break;
+        const int g = e / D, d = e - g * D;
+        f32x4 acc_b = o[x] * sm_ml[0][g];
+        f32x4 part[kMergeStage / 4];
+        for (int k0 = 0; k0 < n; k0 += kMergeStage / 4) {
+          const int m = min(kMergeStage / 4, n - k0);
+#pragma unroll
+          for (int k = 0; k < kMergeStage / 4; ++k)
+            if (k < m) part[k] = load_coherent4(a.ws_acc + slot_of(cb + k0 + k, g) * D + d);
+#pragma unroll
+          for (int k = 0; k < kMergeStage / 4; ++k)
+            if (k < m) acc_b += sm_mw[k0 + k][g] * part[k];
+        }
+        o[x] = acc_b;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < (EPT > 0 ? EPT : 1); ++x) {
+      const int e = (tid + x * blockDim.x) * 4;
+      if (e >= G * D) break;
+      const int g = e / D;
+      const float Ls = sm_hl[g];
       *reinterpret_cast<uint2*>(rows + e) =
-          make_uint2(pack2<QT>(o[0] / Ls, o[1] / Ls), pack2<QT>(o[2] / Ls, o[3] / Ls));
+          make_uint2(pack2<QT>(o[x][0] / Ls, o[x][1] / Ls), pack2<QT>(o[x][2] / Ls, o[x][3] / Ls));
     }
   };
 

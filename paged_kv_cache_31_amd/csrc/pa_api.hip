@@ -12,6 +12,11 @@
 
 #define PA_EXPORT extern "C" __attribute__((visibility("default")))
 
+// Balanced mode launches this many waves per resident wave slot.
+#ifndef PA_WAVE_ROUNDS
+#define PA_WAVE_ROUNDS 1
+#endif
+
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
@@ -184,7 +189,7 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   const int64_t cap_chunks = chunk_capacity(desc);
   int64_t waves = cap_chunks;
   if (desc->partition_tokens == 0) {
-    const int64_t resident = resident_waves(desc);
+    const int64_t resident = resident_waves(desc) * PA_WAVE_ROUNDS;
     if (resident > 0 && resident < waves) waves = resident / pa::kWaves * pa::kWaves;
     if (waves < pa::kWaves) waves = pa::kWaves;
   }
