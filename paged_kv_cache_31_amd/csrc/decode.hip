@@ -40,7 +40,8 @@
 //  * fp8 (OCP e4m3fn) tiles are widened exactly to the MFMA type in registers; the K block scale
 //    multiplies the scores, the V block scale the weights.
 //  * A step is 32 tokens (two blocks); the loads of step s+1 are in flight while step s is
-//    computed, and the block ids of step s+2 are fetched with scalar loads meanwhile.
+//    computed, and the block ids of step s+2 are fetched with scalar loads meanwhile.  K/V loads
+//    are non-temporal: each byte is read once per launch.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -251,14 +252,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int cc = 0; cc < KL; ++cc)
-          r.k[m][cc] = *reinterpret_cast<const uint4*>(kp + m * 4 * D * EB + cc * 64);
+        for (int cc = 0; cc < KL; ++cc) r.k[m][cc] = load_stream16(kp + m * 4 * D * EB + cc * 64);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if constexpr (FP8)
-          r.v[i] = *reinterpret_cast<const uint2*>(vp + i * 16 * kBlock * EB);
+          r.v[i] = load_stream8(vp + i * 16 * kBlock * EB);
         else
-          r.v[i] = *reinterpret_cast<const uint4*>(vp + i * 16 * kBlock * EB);
+          r.v[i] = load_stream16(vp + i * 16 * kBlock * EB);
       }
       if constexpr (FP8) {
         r.ks = a.k_scale[(size_t)vb * Hkv + kvh];
