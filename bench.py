@@ -149,7 +149,7 @@ def main() -> int:
     bytes_append = workloads.append_bytes(B, Hkv, D, s.kv_dtype)
     pool_bytes = wl.k_cache.nbytes + wl.v_cache.nbytes
     R = args.rotations or max(2, math.ceil(2 * 2**30 / bytes_decode))
-    R = max(1, min(R, int(48 * 2**30 // pool_bytes)))
+    R = max(1, min(R, 64, int(48 * 2**30 // pool_bytes)))
 
     def to_dev(bits, dtype):
         a = np.ascontiguousarray(bits)
