@@ -111,6 +111,8 @@ def main() -> int:
     ap.add_argument("--partition", type=int, default=None,
                     help="key-partition tokens (default: the workload's, else the library's)")
     ap.add_argument("--rotations", type=int, default=0, help="pool copies cycled (0: auto)")
+    ap.add_argument("--no-shared-prefixes", action="store_true",
+                    help="decode a workload with a shared prefix without the prefix plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -175,7 +177,9 @@ def main() -> int:
     log(f"uploaded: {R} pool copies of {pool_bytes / 2**30:.2f} GiB")
 
     P = s.partition_tokens if args.partition is None else args.partition
-    desc = pa.decode_desc(base["q"], base["k"], tables, wl.max_context_len, P)
+    # a batch whose sequences share a prefix is decoded with the shared-prefix plan
+    share = s.prefix is not None and not args.no_shared_prefixes
+    desc = pa.decode_desc(base["q"], base["k"], tables, wl.max_context_len, P, share)
     ws_bytes = pa.pa_decode_workspace_size(desc)
     workspace = pa.new_workspace(ws_bytes, dev)
     scale = float(wl.scale)
@@ -184,7 +188,8 @@ def main() -> int:
     appends = [pa.AppendCall(x["k_new"], x["v_new"], slots, x["k"], x["v"]) for x in rots]
     decodes = [pa.DecodeCall(x["q"], x["k"], x["v"], tables, lens, scale, x["out"],
                              k_scale=k_scale, v_scale=v_scale, max_context_len=mcl,
-                             partition_tokens=P, workspace=workspace) for x in rots]
+                             partition_tokens=P, workspace=workspace, shared_prefixes=share)
+               for x in rots]
 
     def step(r):
         appends[r]()
@@ -218,7 +223,8 @@ def main() -> int:
 
     achieved = bytes_decode / launch_s / 1e9
     value = (bytes_decode + bytes_append) / (ms_per_step / 1e3) / 1e9
-    kernel = "decode_kernel"
+    # the decode call is one kernel, or the plan, prefix and decode kernels with shared prefixes
+    kernel = "plan_kernel+prefix_kernel+decode_kernel" if share else "decode_kernel"
     lens_np = wl.context_lens
     result = {
         "metric": METRIC,
@@ -239,6 +245,7 @@ def main() -> int:
             "context_len_min": int(lens_np.min()), "context_len_max": int(lens_np.max()),
             "context_tokens": int(lens_np.sum()), "unique_tokens": int(wl.unique_tokens),
             "num_blocks": wl.num_blocks, "partition_tokens": P or "balanced", "rotations": R,
+            "shared_prefixes": share,
             "step": "pa_kv_append (1 token per sequence) + pa_decode",
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),

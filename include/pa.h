@@ -85,6 +85,13 @@ typedef struct pa_decode_desc {
                                  0 = chunks of equal length balanced over the GPU's resident
                                  waves (the default, best for ragged batches) */
   int32_t q_dtype;            /* PA_F16 or PA_BF16; the output has the same dtype */
+  int32_t shared_prefixes;    /* 0 or 1.  1: sequences whose block tables start with the same
+                                 physical blocks (a prefix cache shares blocks this way: youngju.dev
+                                 LLM inference guide, PagedAttention "主な特性" and its prefix-
+                                 caching example; Scaling Book note, "プレフィックスキャッシュ") read
+                                 those blocks once per group of up to 16/group sequences instead of
+                                 once each.  Taken when group <= 8 and batch <= 1024, else ignored.
+                                 The result is the same attention up to rounding order. */
 } pa_decode_desc;
 
 /*
@@ -128,7 +135,15 @@ pa_status pa_kv_append(const pa_cache_desc* cache, int32_t num_tokens,
  * Supported pairs (q_dtype, kv_dtype): (F16, F16), (BF16, BF16), (BF16, FP8_E4M3),
  * (F16, FP8_E4M3).  Accumulation is fp32.  Results depend only on logical token positions and
  * on the context lengths of the batch (which set the chunk boundaries), so the same data behind
- * any physical block placement gives bit-identical output.  One kernel is enqueued.
+ * any physical block placement gives bit-identical output (with shared_prefixes 0).  One kernel
+ * is enqueued; with shared prefixes taken, a planning and a prefix kernel run before it.
+ *
+ * Shared prefixes: a planning pass groups the sequences whose first block-table entries are
+ * equal; the shared length of a group is the number of leading entries every member has in
+ * common with the group's first sequence, stops before the block that holds any member's last
+ * token and is at most 256 blocks; groups sharing fewer than two blocks are not used.  The shared
+ * blocks' partial softmax results are merged into each member's own with the log-sum-exp rule.
+ * Results then also depend on the grouping (not on which member gets which MFMA column).
  */
 pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cache,
                     const void* v_cache, const float* k_scale, const float* v_scale,
@@ -138,7 +153,10 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
 /* Bytes of workspace pa_decode needs for this descriptor, or 0 if the descriptor is invalid
  * (pa_decode reports why).  It depends only on the descriptor, not on the GPU:
  * 262144 + workgroups * 2 * group * (head_dim + 2) * 4 bytes (each part rounded up to 256),
- * with workgroups <= 2048 when partition_tokens is 0. */
+ * with workgroups <= 2048 when partition_tokens is 0.  Shared prefixes, when taken, add a plan
+ * of (5 + batch + 19 * T) * 4 bytes with T = max(1, floor(2 * batch / 3)), and
+ * batch * num_q_heads * P * (head_dim + 2) * 4 bytes of partial results with
+ * P = ceil(min(max_blocks_per_seq, 256) / 16) (each part rounded up to 256). */
 size_t pa_decode_workspace_size(const pa_decode_desc* desc);
 
 /* A static, human-readable name for a status code. */

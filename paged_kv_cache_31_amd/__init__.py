@@ -36,7 +36,7 @@ class DecodeDesc(ctypes.Structure):
     _fields_ = [("cache", CacheDesc), ("batch", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("max_context_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
-                ("q_dtype", ctypes.c_int32)]
+                ("q_dtype", ctypes.c_int32), ("shared_prefixes", ctypes.c_int32)]
 
 
 class PaError(RuntimeError):
@@ -143,10 +143,11 @@ def pa_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> N
     AppendCall(k_new, v_new, slot_mapping, k_cache, v_cache, stream)()
 
 
-def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_tokens=0) -> DecodeDesc:
+def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_tokens=0,
+                shared_prefixes=False) -> DecodeDesc:
     B, Hq, D = q.shape
     return DecodeDesc(cache_desc(k_cache), B, Hq, block_tables.shape[1], int(max_context_len),
-                      int(partition_tokens), _dtype_code(q, False))
+                      int(partition_tokens), _dtype_code(q, False), int(bool(shared_prefixes)))
 
 
 def pa_decode_workspace_size(desc: DecodeDesc) -> int:
@@ -175,7 +176,7 @@ class DecodeCall:
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
                  v_scale=None, max_context_len=0, partition_tokens=0, workspace=None,
-                 stream=None):
+                 stream=None, shared_prefixes=False):
         for t in (q, k_cache, v_cache, block_tables, context_lens, out):
             assert t.is_cuda and t.is_contiguous()
         assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
@@ -183,7 +184,8 @@ class DecodeCall:
         NB, Hkv, bs, D = k_cache.shape
         assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
         assert q.shape[2] == D and context_lens.shape[0] == q.shape[0] == block_tables.shape[0]
-        self._desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens)
+        self._desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens,
+                                 shared_prefixes)
         need = pa_decode_workspace_size(self._desc)
         st = _stream(stream)
         if workspace is None:
@@ -204,8 +206,11 @@ class DecodeCall:
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
               v_scale=None, max_context_len=0, partition_tokens=0, workspace=None,
-              stream=None) -> torch.Tensor:
-    """out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b through the block tables; returns out."""
+              stream=None, shared_prefixes=False) -> torch.Tensor:
+    """out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b through the block tables; returns out.
+
+    shared_prefixes: read blocks that several sequences' tables start with once per group of
+    sequences (see pa_decode_desc.shared_prefixes)."""
     DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
-               max_context_len, partition_tokens, workspace, stream)()
+               max_context_len, partition_tokens, workspace, stream, shared_prefixes)()
     return out

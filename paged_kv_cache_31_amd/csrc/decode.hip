@@ -26,22 +26,32 @@
 //    counter per boundary elects the last workgroup to arrive, which reads all parts of that
 //    sequence head back with device-coherent loads, merges them in logical order and resets the
 //    counter.  (A device-scope fence would write back or invalidate the whole L2 of the XCD,
-//    which costs far more than the merge itself.)  Nothing depends on the physical
-//    block ids, so results are identical for any block placement.
+//    which costs far more than the merge itself.)  Nothing depends on the physical block ids, so
+//    results are identical for any block placement.
+//  * Shared prefixes (opt-in).  Sequences whose block tables start with the same physical blocks
+//    (a prefix cache shares blocks this way: youngju.dev guide, PagedAttention "主な特性"; Scaling
+//    Book note, "プレフィックスキャッシュ") are grouped by plan_kernel, and prefix_kernel reads
+//    each shared block once per tile of up to 16/group members (their query heads fill the 16
+//    columns of an MFMA tile) instead of once per sequence.  It leaves every member's partial
+//    results (running max, exp-sum, unnormalised output) over the shared blocks in the
+//    workspace; decode_kernel then covers only each member's own blocks and folds the partial
+//    results in with the same log-sum-exp rule before normalising.
 //  * Matrix cores make the arithmetic nearly free: one 16x16x32 MFMA covers 16 tokens x 32 dims
-//    for up to 16 query heads of a group, leaving only the softmax on the vector ALUs.
+//    for up to 16 query columns, leaving only the softmax on the vector ALUs.
 //    QK: S^T = K . Q^T with the K tile (token-major) loaded straight into the A operand: lane
 //    (row r = lane%16, group g = lane/16) reads 16 contiguous bytes of token row r.  The rows of a
-//    step's two MFMAs are assigned so that the result layout (lane holds head lane%16, rows
+//    step's two MFMAs are assigned so that the result layout (lane holds column lane%16, rows
 //    4g..4g+3) is exactly the B operand of the P.V product.
 //    PV: O^T = V^T . P^T.  V tiles are dim-major ([d][16 tokens]), so the A operand (row d, 8
 //    consecutive tokens) is one 16-byte load.  P goes in as a bf16 hi/lo pair (two MFMAs), keeping
 //    ~16 significant bits of each weight; fp16 P is used as is.
 //  * fp8 (OCP e4m3fn) tiles are widened exactly to the MFMA type in registers; the K block scale
 //    multiplies the scores, the V block scale the weights.
-//  * A step is 32 tokens (two blocks); the loads of step s+1 are in flight while step s is
-//    computed, and the block ids of step s+2 are fetched with scalar loads meanwhile.  K/V loads
-//    are non-temporal: each byte is read once per launch.
+//  * A step is 32 tokens (two blocks); the loads of the next step are in flight while a step is
+//    computed, and the block ids of the step after are fetched with scalar loads meanwhile.  K/V
+//    loads are non-temporal: each byte is read once per launch.
+#include <limits.h>
+
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -79,172 +89,113 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 __device__ __forceinline__ int blocks_of(int L) { return (L + kBlock - 1) / kBlock; }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Published parts a merging workgroup stages in LDS at once (more are folded in batches).
-constexpr int kMergeStage = 64;
+// Leading blocks of sequence b that prefix_kernel covers (0 when shared prefixes are off).  The
+// plan never takes the block holding a sequence's last token, so at least one block is left;
+// the clamp only keeps indexing in range.
+__device__ __forceinline__ int skip_of(const DecodeArgs& a, int b, int nblk) {
+  if (!a.ws_plan) return 0;
+  const int s = a.ws_plan[kPlanHeader + b];
+  return max(0, min(s, nblk - 1));
+}
 
 // A cut piece parked in LDS for the workgroup-level merge.
 struct PieceMeta {
-  int b, kvh, j0, j1, nblk, s0;   // s0: flattened index of the sequence head's first block
+  int b, kvh, j0, j1, nblk, skip;
+  int s0;   // flattened index of the sequence head's first block (after the skipped ones)
 };
 
-template <int D, int QT, int KVT>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
+// Published parts a merging workgroup stages in LDS at once (more are folded in batches).
+constexpr int kMergeStage = 64;
+
+// The streaming core shared by decode_kernel and prefix_kernel: one wave, one query column per
+// lane column (lane%16), online softmax over a range of logical blocks of one table row.  K/V
+// loads are non-temporal (STREAM) where each byte is read once per launch, and cached where
+// several workgroups read the same blocks.
+template <int D, int QT, int KVT, bool STREAM = true>
+struct Stepper {
   typedef Mfma<QT> M;
   typedef typename M::vec8 V8;
   typedef typename M::elem E;
-  constexpr bool FP8 = KVT == DT_FP8;
-  constexpr bool SPLIT_P = QT == DT_BF16;
-  constexpr int EB = FP8 ? 1 : 2;                 // bytes per cache element
-  constexpr int NC = D / 32;                      // 32-dim chunks (QK)
-  constexpr int NT = D / 16;                      // 16-dim tiles (PV)
-  constexpr int KL = FP8 ? NC / 2 : NC;           // K loads per row set
-  constexpr int TILE = kBlock * D * EB;           // bytes of one (block, kv head) tile
+  static constexpr bool FP8 = KVT == DT_FP8;
+  static constexpr bool SPLIT_P = QT == DT_BF16;
+  static constexpr int EB = FP8 ? 1 : 2;          // bytes per cache element
+  static constexpr int NC = D / 32;               // 32-dim chunks (QK)
+  static constexpr int NT = D / 16;               // 16-dim tiles (PV)
+  static constexpr int KL = FP8 ? NC / 2 : NC;    // K loads per row set
+  static constexpr int TILE = kBlock * D * EB;    // bytes of one (block, kv head) tile
 
-  static_assert(NT % kWaves == 0, "the merge phase gives each wave NT/4 tiles");
-  constexpr int TPW = NT / kWaves;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const float* ksc;
+  const float* vsc;
+  int Hkv, num_blocks;
+  float qk_scale_log2;
+  int col, grp, k_lane_off, v_lane_off, tb_lane;
+  bool k_hi, v_hi;
 
-  __shared__ int sm_wave_sum[kWaves];
-  __shared__ int sm_start_b[kWaves], sm_start_off[kWaves];
-  __shared__ PieceMeta sm_meta[kWaves][2];          // [wave][first / last cut piece]
-  __shared__ float sm_pm[kWaves][2][16], sm_pl[kWaves][2][16];
-  __shared__ f32x4 sm_pacc[kWaves][2][NT][64];
-  __shared__ int sm_last;
-  __shared__ int sm_start_L[kWaves];
-  __shared__ float sm_mw[kMergeStage][16], sm_ml[kMergeStage][16];   // published parts: m, l
-  __shared__ float sm_hm[16], sm_hl[16];                              // per head: max, exp-sum
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int B = a.batch, Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = a.group;
-  const int cap = a.len_cap;
-
-  // ---- 1. Flattened block space and this workgroup's chunk starts.
-  // Thread t owns sequences [t*per, t*per + per); W = sum_b Hkv * blocks(L_b).
-  const int per = (B + 255) >> 8;
-  const int b_lo = tid * per;
-  int tot = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = b_lo + i;
-    if (b < B) tot += Hkv * blocks_of(clamp_len(a.context_lens[b], cap));
+  __device__ __forceinline__ Stepper(const DecodeArgs& a, int lane)
+      : kc(reinterpret_cast<const uint8_t*>(a.k_cache)),
+        vc(reinterpret_cast<const uint8_t*>(a.v_cache)),
+        ksc(a.k_scale), vsc(a.v_scale), Hkv(a.num_kv_heads), num_blocks(a.num_blocks),
+        qk_scale_log2(a.qk_scale_log2) {
+    col = lane & 15;
+    grp = lane >> 4;
+    // K row r = col of MFMA m holds token 16*(r/8) + 8*((r/4)%2) + 4*m + r%4 of the step; its
+    // block is r/8.  Result row 4*grp+i of MFMA m is then token tb + 4*m + i with
+    // tb = 16*(grp/2) + 8*(grp%2), which is exactly the token order the PV operands use.
+    k_lane_off = (8 * ((col >> 2) & 1) + (col & 3)) * D * EB + 16 * grp;
+    v_lane_off = (col * kBlock + 8 * (grp & 1)) * EB;
+    k_hi = col >= 8;
+    v_hi = grp >= 2;
+    tb_lane = 16 * (grp >> 1) + 8 * (grp & 1);
   }
-  int incl = tot;
+
+  static __device__ __forceinline__ uint4 load16(const uint8_t* p) {
+    if constexpr (STREAM) return load_stream16(p);
+    else return *reinterpret_cast<const uint4*>(p);
+  }
+  static __device__ __forceinline__ uint2 load8(const uint8_t* p) {
+    if constexpr (STREAM) return load_stream8(p);
+    else return *reinterpret_cast<const uint2*>(p);
+  }
+
+  // Q^T as the B operand of the QK product for this lane's query row (nullptr: zeros).  Lane
+  // (column col, group grp) holds 8 dims per chunk; fp8 tiles pair chunks (2c, 2c+1) in one
+  // 16-byte load, which permutes which dims a lane holds for each chunk, and Q follows suit.
+  __device__ __forceinline__ void load_q(V8 (&qB)[NC], const E* qrow) const {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) sm_wave_sum[wave] = incl;
-  __syncthreads();
-  int before = 0, W = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int v = sm_wave_sum[w];
-    before += w < wave ? v : 0;
-    W += v;
-  }
-  int Cw = a.chunk_blocks;
-  if (Cw == 0) {
-    Cw = (W + a.total_waves - 1) / a.total_waves;
-    Cw = max(2, (Cw + 1) & ~1);
-  }
-  const int nch = (W + Cw - 1) / Cw;
-  const int c_first = blockIdx.x * kWaves;
-  {
-    int run = before + incl - tot;                // blocks before this thread's first sequence
-    for (int i = 0; i < per; ++i) {
-      const int b = b_lo + i;
-      if (b >= B) break;
-      const int nb = Hkv * blocks_of(clamp_len(a.context_lens[b], cap));
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const long start = (long)(c_first + w) * Cw;
-        if (start >= run && start < run + nb) {
-          sm_start_b[w] = b;
-          sm_start_off[w] = (int)(start - run);
-          sm_start_L[w] = clamp_len(a.context_lens[b], cap);
-        }
-      }
-      if (nb == 0 && blockIdx.x == 0) {           // no tokens: the output rows are zeros
-        uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<E*>(a.out) + (size_t)b * Hq * D);
-        for (int k = 0; k < Hq * D / 8; ++k) o[k] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      run += nb;
+    for (int cc = 0; cc < NC; ++cc) {
+      const int d0 = FP8 ? 64 * (cc >> 1) + 16 * grp + 8 * (cc & 1) : 32 * cc + 8 * grp;
+      qB[cc] = qrow ? as_vec8<V8>(*reinterpret_cast<const uint4*>(qrow + d0)) : zero_vec8<V8>();
     }
   }
-  if (tid < 2 * kWaves) sm_meta[tid >> 1][tid & 1].b = -1;
-  __syncthreads();
 
-  const int c = c_first + wave;
-
-  // ---- 2. This wave's chunk [a0, a1) of the flattened space, piece by piece.
-  const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k_cache);
-  const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v_cache);
-  // K row r = col of MFMA m holds token 16*(r/8) + 8*((r/4)%2) + 4*m + r%4 of the step; its block
-  // is r/8.  Result row 4*grp+i of MFMA m is then token tb + 4*m + i with
-  // tb = 16*(grp/2) + 8*(grp%2), which is exactly the token order the PV operands use.
-  const int k_lane_off = (8 * ((col >> 2) & 1) + (col & 3)) * D * EB + 16 * grp;
-  const int v_lane_off = (col * kBlock + 8 * (grp & 1)) * EB;
-  const bool k_hi = col >= 8;
-  const bool v_hi = grp >= 2;
-  const int tb_lane = 16 * (grp >> 1) + 8 * (grp & 1);
-
-  const int a0 = c * Cw;
-  const int a1 = min(a0 + Cw, W);
-  int b = 0, L = 0, nblk = 0, kvh = 0, j = 0;
-  if (c < nch) {
-    b = uniform(sm_start_b[wave]);
-    L = uniform(sm_start_L[wave]);
-    nblk = blocks_of(L);
-    const int off = uniform(sm_start_off[wave]);
-    kvh = off / nblk;
-    j = off - kvh * nblk;
-  }
-  int pos = a0;
-  for (int piece = 0; c < nch; ++piece) {
-    const int j0 = j;
-    const int j1 = min(nblk, j0 + (a1 - pos));
-    const int end_tok = j1 == nblk ? L : kBlock * j1;   // tokens at or past end_tok are masked
+  // Online-softmax attention over logical blocks [j0, j1) of table row trow for KV head kvh
+  // (tokens at or past end_tok are masked), taking the steps s_first, s_first + stride, ... of
+  // the range, into the running (m_run, l_run, acc).
+  __device__ __forceinline__ void run(const V8 (&qB)[NC], const int32_t* trow, int kvh, int j0,
+                                      int j1, int end_tok, int s_first, int stride,
+                                      float& m_run, float& l_run, f32x4 (&acc)[NT]) const {
     const int nsteps = (j1 - j0 + 1) >> 1;
-    const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-    const int h0 = kvh * G;
-
-    // Q^T as the B operand of the QK product: lane (head col, group grp) holds 8 dims per
-    // chunk.  fp8 tiles pair chunks (2c, 2c+1) in one 16-byte load, which permutes which dims a
-    // lane holds for each chunk; Q is loaded with the same permutation.
-    V8 qB[NC];
-    {
-      const E* qrow = reinterpret_cast<const E*>(a.q) + ((size_t)b * Hq + h0 + col) * D;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        const int d0 = FP8 ? 64 * (cc >> 1) + 16 * grp + 8 * (cc & 1) : 32 * cc + 8 * grp;
-        qB[cc] = col < G ? as_vec8<V8>(*reinterpret_cast<const uint4*>(qrow + d0))
-                         : zero_vec8<V8>();
-      }
-    }
-
-    float m_run = -INFINITY, l_run = 0.0f;
-    f32x4 acc[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (s_first >= nsteps) return;
 
     // Block ids of a step: logical blocks j0+2s and j0+2s+1 (the second one repeats the first
-    // when the piece ends after one block; its tokens are masked).  Ids outside the pool read
+    // when the range ends after one block; its tokens are masked).  Ids outside the pool read
     // block 0.
     auto ids_of = [&](int s, int& p0, int& p1) {
       s = min(s, nsteps - 1);
       const int jb = j0 + 2 * s;
       const int jb1 = jb + 1 < j1 ? jb + 1 : jb;
       const int i0 = trow[jb], i1 = trow[jb1];
-      p0 = (unsigned)i0 < (unsigned)a.num_blocks ? i0 : 0;
-      p1 = (unsigned)i1 < (unsigned)a.num_blocks ? i1 : 0;
+      p0 = (unsigned)i0 < (unsigned)num_blocks ? i0 : 0;
+      p1 = (unsigned)i1 < (unsigned)num_blocks ? i1 : 0;
     };
     int nid0, nid1;
-    ids_of(0, nid0, nid1);
+    ids_of(s_first, nid0, nid1);
 
     auto issue = [&](StepRegs<D, FP8>& r, int s) {
       const int pb0 = nid0, pb1 = nid1;
-      ids_of(s + 1, nid0, nid1);                   // prefetch the next step's block ids
+      ids_of(s + stride, nid0, nid1);              // prefetch the next step's block ids
       const int kb = k_hi ? pb1 : pb0;
       const int vb = v_hi ? pb1 : pb0;
       const uint8_t* kp = kc + ((size_t)kb * Hkv + kvh) * TILE + k_lane_off;
@@ -252,17 +203,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int cc = 0; cc < KL; ++cc) r.k[m][cc] = load_stream16(kp + m * 4 * D * EB + cc * 64);
+        for (int cc = 0; cc < KL; ++cc) r.k[m][cc] = load16(kp + m * 4 * D * EB + cc * 64);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if constexpr (FP8)
-          r.v[i] = load_stream8(vp + i * 16 * kBlock * EB);
+          r.v[i] = load8(vp + i * 16 * kBlock * EB);
         else
-          r.v[i] = load_stream16(vp + i * 16 * kBlock * EB);
+          r.v[i] = load16(vp + i * 16 * kBlock * EB);
       }
       if constexpr (FP8) {
-        r.ks = a.k_scale[(size_t)vb * Hkv + kvh];
-        r.vs = a.v_scale[(size_t)vb * Hkv + kvh];
+        r.ks = ksc[(size_t)vb * Hkv + kvh];
+        r.vs = vsc[(size_t)vb * Hkv + kvh];
       }
     };
 
@@ -288,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
           S[m] = M::mma(kA, qB[cc], S[m]);
         }
       }
-      float qs = a.qk_scale_log2;
+      float qs = qk_scale_log2;
       if constexpr (FP8) qs *= r.ks;
       float sc[8];
 #pragma unroll
@@ -367,32 +318,185 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       }
     };
 
-    {
-      // The steady-state loop issues the next step's loads unconditionally (the tail is
-      // peeled), so the loads of step s+1 stay in flight while step s is computed.
-      StepRegs<D, FP8> r0, r1;
-      int s = 0, rest = nsteps - 1;
-      issue(r0, 0);
-      for (; rest >= 2; rest -= 2, s += 2) {
-        issue(r1, s + 1);
-        compute(r0, s);
-        issue(r0, s + 2);
-        compute(r1, s + 1);
-      }
-      if (rest == 1) {
-        issue(r1, s + 1);
-        compute(r0, s);
-        compute(r1, s + 1);
-      } else {
-        compute(r0, s);
-      }
+
+    // The steady-state loop issues the next step's loads unconditionally (the tail is peeled),
+    // so the loads of one step stay in flight while the previous step is computed.
+    StepRegs<D, FP8> r0, r1;
+    int s = s_first, rest = (nsteps - 1 - s_first) / stride;
+    issue(r0, s);
+    for (; rest >= 2; rest -= 2, s += 2 * stride) {
+      issue(r1, s + stride);
+      compute(r0, s);
+      issue(r0, s + 2 * stride);
+      compute(r1, s + stride);
     }
+    if (rest == 1) {
+      issue(r1, s + stride);
+      compute(r0, s);
+      compute(r1, s + stride);
+    } else {
+      compute(r0, s);
+    }
+  }
+};
+
+// Parts (partial results over kUnitBlocks shared blocks each) that cover `skip` shared blocks.
+__device__ __forceinline__ int prefix_parts(int skip) { return (skip + kUnitBlocks - 1) / kUnitBlocks; }
+
+// Folds the prefix partial results of query row `row` (written by prefix_kernel) into a running
+// (m, l, acc) whose tile t holds this lane's column at dims 16 * (t0 + tstride * t) + 4 * grp.
+template <int D, int NTL>
+__device__ __forceinline__ void fold_prefix(const DecodeArgs& a, size_t row, int nparts, int grp,
+                                            int t0, int tstride, float& m, float& l,
+                                            f32x4 (&acc)[NTL]) {
+  for (int k = 0; k < nparts; ++k) {
+    const size_t part = row * a.prefix_parts + k;
+    const float pm = a.gp_ml[part * 2], pl = a.gp_ml[part * 2 + 1];
+    const float M_ = fmaxf(pm, m);
+    const float x = fast_exp2(pm - M_), y = fast_exp2(m - M_);
+    l = pl * x + l * y;
+    m = M_;
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const f32x4 p =
+          *reinterpret_cast<const f32x4*>(a.gp_acc + part * D + 16 * (t0 + tstride * t) + 4 * grp);
+      acc[t] = p * x + acc[t] * y;
+    }
+  }
+}
+
+template <int D, int QT, int KVT>
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
+  typedef Stepper<D, QT, KVT> St;
+  typedef typename St::V8 V8;
+  typedef typename St::E E;
+  constexpr int NC = St::NC;
+  constexpr int NT = St::NT;
+  static_assert(NT % kWaves == 0, "the merge phase gives each wave NT/4 tiles");
+  constexpr int TPW = NT / kWaves;
+
+  __shared__ int sm_wave_sum[kWaves];
+  __shared__ int sm_start_b[kWaves], sm_start_off[kWaves], sm_start_L[kWaves];
+  __shared__ int sm_start_skip[kWaves];
+  __shared__ PieceMeta sm_meta[kWaves][2];          // [wave][first / last cut piece]
+  __shared__ float sm_pm[kWaves][2][16], sm_pl[kWaves][2][16];
+  __shared__ f32x4 sm_pacc[kWaves][2][NT][64];
+  __shared__ int sm_last;
+  __shared__ float sm_mw[kMergeStage][16], sm_ml[kMergeStage][16];   // staged parts: m, l
+  __shared__ float sm_hm[16], sm_hl[16];                              // per head: max, exp-sum
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int B = a.batch, Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = a.group;
+  const int cap = a.len_cap;
+
+  // ---- 1. Flattened block space and this workgroup's chunk starts.  A sequence head (b, kvh)
+  // takes its blocks [skip_b, blocks(L_b)) there.  Thread t owns sequences [t*per, t*per + per);
+  // W = sum_b Hkv * (blocks(L_b) - skip_b).
+  const int per = (B + 255) >> 8;
+  const int b_lo = tid * per;
+  int tot = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b_lo + i;
+    if (b < B) {
+      const int nblk = blocks_of(clamp_len(a.context_lens[b], cap));
+      tot += Hkv * (nblk - skip_of(a, b, nblk));
+    }
+  }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) sm_wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0, W = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = sm_wave_sum[w];
+    before += w < wave ? v : 0;
+    W += v;
+  }
+  int Cw = a.chunk_blocks;
+  if (Cw == 0) {
+    Cw = (W + a.total_waves - 1) / a.total_waves;
+    Cw = max(2, (Cw + 1) & ~1);
+  }
+  const int nch = (W + Cw - 1) / Cw;
+  const int c_first = blockIdx.x * kWaves;
+  {
+    int run = before + incl - tot;                // blocks before this thread's first sequence
+    for (int i = 0; i < per; ++i) {
+      const int b = b_lo + i;
+      if (b >= B) break;
+      const int L = clamp_len(a.context_lens[b], cap);
+      const int nblk = blocks_of(L);
+      const int sk = skip_of(a, b, nblk);
+      const int nb = Hkv * (nblk - sk);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const long start = (long)(c_first + w) * Cw;
+        if (start >= run && start < run + nb) {
+          sm_start_b[w] = b;
+          sm_start_off[w] = (int)(start - run);
+          sm_start_L[w] = L;
+          sm_start_skip[w] = sk;
+        }
+      }
+      if (nb == 0 && blockIdx.x == 0) {           // no tokens: the output rows are zeros
+        uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<E*>(a.out) + (size_t)b * Hq * D);
+        for (int k = 0; k < Hq * D / 8; ++k) o[k] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      run += nb;
+    }
+  }
+  if (tid < 2 * kWaves) sm_meta[tid >> 1][tid & 1].b = -1;
+  __syncthreads();
+
+  const int c = c_first + wave;
+
+  // ---- 2. This wave's chunk [a0, a1) of the flattened space, piece by piece.
+  const St st(a, lane);
+  const int a0 = c * Cw;
+  const int a1 = min(a0 + Cw, W);
+  int b = 0, L = 0, nblk = 0, sk = 0, kvh = 0, j = 0;
+  int pos = a0;                                     // flattened index of the next block
+  bool more = false;
+  if (c < nch) {
+    b = uniform(sm_start_b[wave]);
+    L = uniform(sm_start_L[wave]);
+    sk = uniform(sm_start_skip[wave]);
+    nblk = blocks_of(L);
+    const int off = uniform(sm_start_off[wave]);
+    kvh = off / (nblk - sk);
+    j = sk + off - kvh * (nblk - sk);
+    more = true;
+  }
+  for (int piece = 0; more; ++piece) {
+    const int j0 = j;
+    const int j1 = min(nblk, j0 + (a1 - pos));
+    const int end_tok = j1 == nblk ? L : kBlock * j1;   // tokens at or past end_tok are masked
+    const int h0 = kvh * G;
+
+    V8 qB[NC];
+    st.load_q(qB, col < G ? reinterpret_cast<const E*>(a.q) + ((size_t)b * Hq + h0 + col) * D
+                          : nullptr);
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.run(qB, a.block_tables + (size_t)b * a.max_blocks_per_seq, kvh, j0, j1, end_tok, 0, 1,
+           m_run, l_run, acc);
 
     // ---- finish the piece: whole sequence head -> output; cut piece -> LDS slot
     l_run = sum_across_rows(l_run);
-    if (j0 == 0 && j1 == nblk) {
+    if (j0 == sk && j1 == nblk) {
       if (col < G) {
-        E* out = reinterpret_cast<E*>(a.out) + ((size_t)b * Hq + h0 + col) * D + 4 * grp;
+        const size_t row = (size_t)b * Hq + h0 + col;
+        if (sk > 0) fold_prefix<D>(a, row, prefix_parts(sk), grp, 0, 1, m_run, l_run, acc);
+        E* out = reinterpret_cast<E*>(a.out) + row * D + 4 * grp;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
           *reinterpret_cast<uint2*>(out + 16 * i) =
@@ -401,7 +505,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       }
     } else {
       const int sl = piece == 0 ? 0 : 1;          // only a chunk's first and last can be cut
-      if (lane == 0) sm_meta[wave][sl] = PieceMeta{b, kvh, j0, j1, nblk, pos - j0};
+      if (lane == 0) sm_meta[wave][sl] = PieceMeta{b, kvh, j0, j1, nblk, sk, pos - (j0 - sk)};
       if (grp == 0) {
         sm_pm[wave][sl][col] = m_run;
         sm_pl[wave][sl][col] = l_run;
@@ -413,7 +517,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     pos += j1 - j0;
     if (pos >= a1) break;
     // next piece: the next KV head of this sequence, else the next sequence with tokens
-    j = 0;
     if (++kvh == Hkv) {
       // pos < a1 <= W guarantees a later sequence with tokens; the bound on b only keeps the
       // walk inside the lengths array should they change while the kernel runs
@@ -422,7 +525,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       while (L == 0 && b + 1 < B) L = clamp_len(a.context_lens[++b], cap);
       if (L == 0) break;
       nblk = blocks_of(L);
+      sk = skip_of(a, b, nblk);
     }
+    j = sk;
   }
   __syncthreads();
 
@@ -431,32 +536,42 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   // all its blocks is written out; a group cut at the workgroup boundary is published and the
   // last workgroup to publish a part of that sequence head merges all of them.
   const int WGB = kWaves * Cw;                      // blocks per workgroup range
-  int gb = -1, gkvh = 0, gj0 = 0, gj1 = 0, gnblk = 0, gs0 = 0;
+  int gb = -1, gkvh = 0, gj0 = 0, gj1 = 0, gnblk = 0, gskip = 0, gs0 = 0;
   float gm = -INFINITY, gl = 0.0f;
   f32x4 go[TPW];
 
   auto merge_published = [&](int c0, int c1) {
-    // parts of sequence head (gb, gkvh) published by workgroups c0..c1; workgroup c0 holds it as
-    // its first group (slot 0) only if the sequence head starts exactly at its range.  Batches of
-    // up to kMergeStage parts: their (max, exp-sum) pairs are staged in LDS with one round of
-    // loads, then every thread loads all its output columns of the batch at once.
+    // The parts of sequence head (gb, gkvh): its prefix parts (if any), then the parts published
+    // by workgroups c0..c1.  Workgroup c0 holds it as its first group (slot 0) only if the
+    // sequence head starts exactly at its range.  Batches of up to kMergeStage parts: their
+    // (max, exp-sum) pairs are staged in LDS with one round of loads, then every thread loads
+    // all its output columns of the batch at once.
     const int first_slot = gs0 != c0 * WGB ? 1 : 0;
-    auto slot_of = [&](int cc, int g) {
+    const int npre = gskip > 0 ? prefix_parts(gskip) : 0;
+    const size_t row0 = (size_t)gb * Hq + gkvh * G;
+    auto part_of = [&](int pi, int g) -> size_t {   // index of part pi of head g in its array
+      if (pi < npre) return (row0 + g) * a.prefix_parts + pi;
+      const int cc = c0 + pi - npre;
       return ((size_t)cc * 2 + (cc == c0 ? first_slot : 0)) * G + g;
     };
-    E* rows = reinterpret_cast<E*>(a.out) + ((size_t)gb * Hq + gkvh * G) * D;
+    auto ml_of = [&](int pi, int g) { return (pi < npre ? a.gp_ml : a.ws_ml) + part_of(pi, g) * 2; };
+    auto acc_of = [&](int pi, int g) {
+      return (pi < npre ? a.gp_acc : a.ws_acc) + part_of(pi, g) * D;
+    };
+    const int nparts = npre + c1 - c0 + 1;
+    E* rows = reinterpret_cast<E*>(a.out) + row0 * D;
     constexpr int EPT = 16 * D / 4 / (64 * kWaves);          // float4 columns per thread (G=16)
     f32x4 o[EPT > 0 ? EPT : 1];
 #pragma unroll
     for (int x = 0; x < (EPT > 0 ? EPT : 1); ++x) o[x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (tid < 16) { sm_hm[tid] = -INFINITY; sm_hl[tid] = 0.0f; }
-    for (int cb = c0; cb <= c1; cb += kMergeStage) {
-      const int n = min(kMergeStage, c1 - cb + 1);
+    for (int pb = 0; pb < nparts; pb += kMergeStage) {
+      const int n = min(kMergeStage, nparts - pb);
       __syncthreads();
       for (int t = tid; t < n * G; t += blockDim.x) {
-        const size_t sl = slot_of(cb + t / G, t % G);
-        sm_mw[t / G][t % G] = load_coherent(a.ws_ml + sl * 2);
-        sm_ml[t / G][t % G] = load_coherent(a.ws_ml + sl * 2 + 1);
+        const float* ml = ml_of(pb + t / G, t % G);
+        sm_mw[t / G][t % G] = load_coherent(ml);
+        sm_ml[t / G][t % G] = load_coherent(ml + 1);
       }
       __syncthreads();
       // per head: new running max; rescale of what is already accumulated
@@ -486,7 +601,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
           const int m = min(kMergeStage / 4, n - k0);
 #pragma unroll
           for (int k = 0; k < kMergeStage / 4; ++k)
-            if (k < m) part[k] = load_coherent4(a.ws_acc + slot_of(cb + k0 + k, g) * D + d);
+            if (k < m) part[k] = load_coherent4(acc_of(pb + k0 + k, g) + d);
 #pragma unroll
           for (int k = 0; k < kMergeStage / 4; ++k)
             if (k < m) acc_b += sm_mw[k0 + k][g] * part[k];
@@ -507,9 +622,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   };
 
   auto emit = [&]() {
-    if (gj0 == 0 && gj1 == gnblk) {
+    if (gj0 == gskip && gj1 == gnblk) {
       if (col < G) {
-        E* out = reinterpret_cast<E*>(a.out) + ((size_t)gb * Hq + gkvh * G + col) * D + 4 * grp;
+        const size_t row = (size_t)gb * Hq + gkvh * G + col;
+        if (gskip > 0) fold_prefix<D>(a, row, prefix_parts(gskip), grp, wave, kWaves, gm, gl, go);
+        E* out = reinterpret_cast<E*>(a.out) + row * D + 4 * grp;
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
           *reinterpret_cast<uint2*>(out + 16 * (wave + kWaves * t)) =
@@ -534,7 +651,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       }
       wait_memory_ops();
       __syncthreads();
-      const int c0 = gs0 / WGB, c1 = (gs0 + gnblk - 1) / WGB;
+      const int c0 = gs0 / WGB, c1 = (gs0 + (gnblk - gskip) - 1) / WGB;
       if (tid == 0)
         sm_last = __hip_atomic_fetch_add(a.ws_cnt + c1, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT) == c1 - c0;
@@ -567,6 +684,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       gj0 = mt.j0;
       gj1 = mt.j1;
       gnblk = mt.nblk;
+      gskip = mt.skip;
       gs0 = mt.s0;
       gm = pm;
       gl = pl;
@@ -577,8 +695,284 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   if (gb >= 0) emit();
 }
 
+// ---- Shared prefixes.
+//
+// plan_kernel (one workgroup, one thread per sequence) groups the sequences whose block tables
+// start with the same physical block, finds how many leading entries every member shares with
+// the group's first sequence (its leader), and lays the groups out as tiles of up to 16/group
+// members.  The shared length stops before the block that holds a member's last token, so every
+// sequence keeps at least one block of its own, and is capped at kMaxSharedBlocks.  Which tile
+// and column a member gets depends on the order of LDS atomics, but the columns of an MFMA tile
+// never mix, so results do not.
+
+// Exclusive prefix sum over the workgroup's kPlanThreads threads; `total` gets the sum.
+__device__ __forceinline__ int plan_scan(int v, int* sm, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sm[w] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanThreads / 64; ++i) {
+    const int x = sm[i];
+    before += i < w ? x : 0;
+    total += x;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
+  constexpr int HS = 2048;                          // hash slots: more than twice the batch
+  static_assert(HS == 2 * kPlanThreads && kPlanThreads >= kPlanMaxBatch, "plan sizes");
+  __shared__ int h_key[HS], h_lead[HS], h_cnt[HS], h_p[HS], h_ub[HS];
+  __shared__ int s_full[kPlanThreads], s_rank[kPlanThreads], s_slot[kPlanThreads];
+  __shared__ int s_off[kPlanThreads], s_cmp[kPlanThreads];
+  __shared__ int s_scan[kPlanThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int B = a.batch, MB = a.max_blocks_per_seq, S = 16 / a.group;
+  const PlanLayout pl(B, a.plan_tiles);
+  int* plan = a.ws_plan;
+  for (int i = tid; i < HS; i += kPlanThreads) {
+    h_key[i] = -1;
+    h_lead[i] = INT_MAX;
+    h_cnt[i] = 0;
+    h_p[i] = INT_MAX;
+  }
+  __syncthreads();
+
+  // 1. Candidates (two or more whole blocks before the one with the last token), hashed by
+  // their first physical block; the leader is the smallest sequence index of a group.
+  const int b = tid;
+  int slot = -1, full = 0;
+  if (b < B) {
+    const int L = clamp_len(a.context_lens[b], a.len_cap);
+    const int key = a.block_tables[(size_t)b * MB];
+    full = L > 0 ? min((L - 1) / kBlock, kMaxSharedBlocks) : 0;
+    if (full >= 2 && (unsigned)key < (unsigned)a.num_blocks) {
+      unsigned h = ((unsigned)key * 2654435761u) >> 21;
+      for (;;) {                                    // ends: fewer keys than slots
+        const int prev = atomicCAS(&h_key[h], -1, key);
+        if (prev == -1 || prev == key) break;
+        h = (h + 1) & (HS - 1);
+      }
+      slot = (int)h;
+      atomicMin(&h_lead[slot], b);
+      s_rank[b] = atomicAdd(&h_cnt[slot], 1);
+    }
+  }
+  s_full[tid] = full;
+  s_slot[tid] = slot;
+  __syncthreads();
+
+  // 2. Shared length of a group: the first table entry where a member differs from the leader,
+  // at most the shorter of their whole-block counts.  The comparisons go in runs of 8 entries,
+  // spread over all threads.
+  int nrun = 0, cmp = 0;
+  if (slot >= 0) {
+    const int lead = h_lead[slot];
+    cmp = min(full, s_full[lead]);
+    atomicMin(&h_p[slot], cmp);
+    if (b != lead) nrun = (cmp - 1 + 7) / 8;        // entries 1 .. cmp-1; entry 0 is the key
+  }
+  s_cmp[tid] = cmp;
+  int nruns;
+  s_off[tid] = plan_scan(nrun, s_scan, nruns);
+  __syncthreads();
+  for (int i = tid; i < nruns; i += kPlanThreads) {
+    int lo = 0, hi = kPlanThreads - 1;              // last thread whose runs start at or before i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int m = lo, sl = s_slot[m];
+    const int j0 = 1 + 8 * (i - s_off[m]), j1 = min(j0 + 8, s_cmp[m]);
+    const int32_t* rm = a.block_tables + (size_t)m * MB;
+    const int32_t* rl = a.block_tables + (size_t)h_lead[sl] * MB;
+    int x[8], y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      x[u] = j0 + u < j1 ? rm[j0 + u] : 0;
+      y[u] = j0 + u < j1 ? rl[j0 + u] : 0;
+    }
+    int first = INT_MAX;
+#pragma unroll
+    for (int u = 7; u >= 0; --u)
+      if (x[u] != y[u]) first = j0 + u;
+    if (first != INT_MAX) atomicMin(&h_p[sl], first);
+  }
+  __syncthreads();
+
+  // 3. Tiles and units of each group (two hash slots per thread), numbered by prefix sums.
+  int nt[2], nu[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int s = 2 * tid + k;
+    const int cnt = h_cnt[s], p = h_p[s];
+    const bool ok = cnt >= 2 && p >= 2;
+    nt[k] = ok ? (cnt + S - 1) / S : 0;
+    nu[k] = ok ? nt[k] * a.num_kv_heads * prefix_parts(p) : 0;
+  }
+  int T, U;
+  const int tb = plan_scan(nt[0] + nt[1], s_scan, T);
+  const int ub = plan_scan(nu[0] + nu[1], s_scan, U);
+  h_key[2 * tid] = tb;                              // h_key now holds each slot's first tile
+  h_key[2 * tid + 1] = tb + nt[0];
+  h_ub[2 * tid] = ub;
+  h_ub[2 * tid + 1] = ub + nu[0];
+  __syncthreads();
+  const bool fits = T <= a.plan_tiles;              // always, by the tile bound; else no sharing
+
+  // 4. Members: column in their tile; shared blocks to skip.
+  if (b < B) {
+    int sk = 0;
+    if (fits && slot >= 0 && h_cnt[slot] >= 2 && h_p[slot] >= 2) {
+      const int r = s_rank[b];
+      plan[pl.mem + (size_t)(h_key[slot] + r / S) * 16 + r % S] = b;
+      sk = h_p[slot];
+    }
+    plan[pl.skip + b] = sk;
+  }
+  // 5. Tiles: table row read, shared length, first unit, unused columns.
+  if (fits) {
+    for (int t = tid; t < T; t += kPlanThreads) {
+      int lo = 0, hi = HS - 1;                      // last slot whose first tile is <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (h_key[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int s = lo, i = t - h_key[s], p = h_p[s];
+      plan[pl.lead + t] = h_lead[s];
+      plan[pl.p + t] = p;
+      plan[pl.ubase + t] = h_ub[s] + i * a.num_kv_heads * prefix_parts(p);
+      for (int r = min(S, h_cnt[s] - i * S); r < 16; ++r) plan[pl.mem + (size_t)t * 16 + r] = -1;
+    }
+  }
+  if (tid == 0) {
+    plan[0] = fits ? T : 0;
+    plan[1] = fits ? U : 0;
+    plan[pl.ubase + (fits ? T : 0)] = fits ? U : 0;
+  }
+}
+
+// One workgroup per unit: the shared blocks [16k, min(p, 16k + 16)) of one KV head, read once
+// for all members of a tile (column r*group + g = query head g of member r).  The four waves
+// take the unit's 32-token steps in turn and merge in LDS; the unnormalised result and its
+// (max, exp-sum) are left for decode_kernel as part k of each member's query rows.
 template <int D, int QT, int KVT>
-static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+__global__ __launch_bounds__(256, 2) void prefix_kernel(DecodeArgs a) {
+  typedef Stepper<D, QT, KVT, false> St;
+  typedef typename St::V8 V8;
+  typedef typename St::E E;
+  constexpr int NC = St::NC;
+  constexpr int NT = St::NT;
+  constexpr int TPW = NT / kWaves;
+  constexpr int kMaxTiles = 2 * kPlanMaxBatch / 3;
+
+  __shared__ int sm_ub[kMaxTiles + 1], sm_lead[kMaxTiles], sm_p[kMaxTiles];
+  __shared__ int sm_tu[2];
+  __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
+  __shared__ f32x4 sm_acc[kWaves][NT][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int Hq = a.num_q_heads, G = a.group, S = 16 / G;
+  const int* plan = a.ws_plan;
+  const PlanLayout pl(a.batch, a.plan_tiles);
+  // the plan's tile arrays, read whole in one round (entries past the tile count are unused)
+  if (tid < 2) sm_tu[tid] = plan[tid];
+  for (int t = tid; t <= a.plan_tiles; t += blockDim.x) {
+    sm_ub[t] = plan[pl.ubase + t];
+    if (t < a.plan_tiles) {
+      sm_lead[t] = plan[pl.lead + t];
+      sm_p[t] = plan[pl.p + t];
+    }
+  }
+  __syncthreads();
+  const int T = sm_tu[0], U = sm_tu[1];
+
+  const St st(a, lane);
+  const int r = col / G, g = col - r * G;
+  for (int u = blockIdx.x; u < U; u += gridDim.x) {
+    int lo = 0, hi = T - 1;                         // tile of unit u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm_ub[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    const int t = lo;
+    const int lead = sm_lead[t], p = sm_p[t];
+    const int ks = prefix_parts(p);
+    const int rem = u - sm_ub[t];
+    const int kvh = rem / ks, k = rem - kvh * ks;
+    const int j0 = k * kUnitBlocks, j1 = min(p, j0 + kUnitBlocks);
+    const int member = r < S ? plan[pl.mem + (size_t)t * 16 + r] : -1;
+    const size_t row = (size_t)member * Hq + kvh * G + g;
+
+    V8 qB[NC];
+    st.load_q(qB, member >= 0 ? reinterpret_cast<const E*>(a.q) + row * D : nullptr);
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.run(qB, a.block_tables + (size_t)lead * a.max_blocks_per_seq, kvh, j0, j1, kBlock * j1,
+           wave, kWaves, m_run, l_run, acc);
+    l_run = sum_across_rows(l_run);
+
+    if (grp == 0) {
+      sm_m[wave][col] = m_run;
+      sm_l[wave][col] = l_run;
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) sm_acc[wave][i][lane] = acc[i];
+    __syncthreads();
+    // wave 0 always has a step, so the maximum is finite; waves without steps weigh 0
+    float M_ = sm_m[0][col];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M_ = fmaxf(M_, sm_m[w][col]);
+    float wt[kWaves], L_ = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      wt[w] = fast_exp2(sm_m[w][col] - M_);
+      L_ += wt[w] * sm_l[w][col];
+    }
+    if (member >= 0) {
+      const size_t part = row * a.prefix_parts + k;
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int ti = wave + kWaves * tt;
+        f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) o += sm_acc[w][ti][lane] * wt[w];
+        *reinterpret_cast<f32x4*>(a.gp_acc + part * D + 16 * ti + 4 * grp) = o;
+      }
+      if (wave == 0 && grp == 0) {
+        a.gp_ml[part * 2] = M_;
+        a.gp_ml[part * 2 + 1] = L_;
+      }
+    }
+    __syncthreads();                                // LDS is reused by the next unit
+  }
+}
+
+template <int D, int QT, int KVT>
+static hipError_t launch_t(const DecodeArgs& a, int prefix_wgs, hipStream_t stream) {
+  if (a.ws_plan) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefix_kernel<D, QT, KVT>), dim3(prefix_wgs), dim3(64 * kWaves), 0,
+                       stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((decode_kernel<D, QT, KVT>), dim3(a.total_waves / kWaves), dim3(64 * kWaves),
                      0, stream, a);
   return hipGetLastError();
@@ -594,11 +988,16 @@ static int occupancy_t() {
 }
 
 template <int D>
-static hipError_t launch_d(const DecodeArgs& a, int q_dtype, int kv_dtype, hipStream_t stream) {
-  if (q_dtype == DT_F16 && kv_dtype == DT_F16) return launch_t<D, DT_F16, DT_F16>(a, stream);
-  if (q_dtype == DT_BF16 && kv_dtype == DT_BF16) return launch_t<D, DT_BF16, DT_BF16>(a, stream);
-  if (q_dtype == DT_BF16 && kv_dtype == DT_FP8) return launch_t<D, DT_BF16, DT_FP8>(a, stream);
-  if (q_dtype == DT_F16 && kv_dtype == DT_FP8) return launch_t<D, DT_F16, DT_FP8>(a, stream);
+static hipError_t launch_d(const DecodeArgs& a, int q_dtype, int kv_dtype, int prefix_wgs,
+                           hipStream_t stream) {
+  if (q_dtype == DT_F16 && kv_dtype == DT_F16)
+    return launch_t<D, DT_F16, DT_F16>(a, prefix_wgs, stream);
+  if (q_dtype == DT_BF16 && kv_dtype == DT_BF16)
+    return launch_t<D, DT_BF16, DT_BF16>(a, prefix_wgs, stream);
+  if (q_dtype == DT_BF16 && kv_dtype == DT_FP8)
+    return launch_t<D, DT_BF16, DT_FP8>(a, prefix_wgs, stream);
+  if (q_dtype == DT_F16 && kv_dtype == DT_FP8)
+    return launch_t<D, DT_F16, DT_FP8>(a, prefix_wgs, stream);
   return hipErrorInvalidValue;
 }
 
@@ -617,9 +1016,9 @@ int decode_workgroups_per_cu(int head_dim, int q_dtype, int kv_dtype) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
-                         hipStream_t stream) {
-  if (head_dim == 64) return launch_d<64>(a, q_dtype, kv_dtype, stream);
-  if (head_dim == 128) return launch_d<128>(a, q_dtype, kv_dtype, stream);
+                         int prefix_wgs, hipStream_t stream) {
+  if (head_dim == 64) return launch_d<64>(a, q_dtype, kv_dtype, prefix_wgs, stream);
+  if (head_dim == 128) return launch_d<128>(a, q_dtype, kv_dtype, prefix_wgs, stream);
   return hipErrorInvalidValue;
 }
 

@@ -53,6 +53,7 @@ pa_status check_decode_desc(const pa_decode_desc* d) {
     return PA_ERR_INVALID_ARG;
   if (blocks_upper(d) >= INT32_MAX) return PA_ERR_UNSUPPORTED;   // flattened index is 32-bit
   if (chunk_capacity(d) > pa::kMaxWorkgroups * pa::kWaves) return PA_ERR_UNSUPPORTED;
+  if (d->shared_prefixes != 0 && d->shared_prefixes != 1) return PA_ERR_INVALID_ARG;
   if (d->q_dtype != PA_F16 && d->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   const int kv = d->cache.kv_dtype;
   if (kv != PA_FP8_E4M3 && kv != d->q_dtype) return PA_ERR_UNSUPPORTED;
@@ -90,10 +91,21 @@ int64_t chunk_capacity(const pa_decode_desc* d) {
   return (n + pa::kWaves - 1) / pa::kWaves * pa::kWaves;
 }
 
-size_t workspace_bytes_of(const pa_decode_desc* d) {
-  return pa::workspace_layout(d->num_q_heads / d->cache.num_kv_heads, d->cache.head_dim,
-                              chunk_capacity(d) / pa::kWaves).total;
+// Shared prefixes are planned when asked for, when a tile holds at least two members
+// (group <= 8) and when the batch fits one planning workgroup.
+bool sharing_active(const pa_decode_desc* d) {
+  return d->shared_prefixes == 1 && d->num_q_heads / d->cache.num_kv_heads <= 8 &&
+         d->batch <= pa::kPlanMaxBatch;
 }
+
+pa::WorkspaceLayout layout_of(const pa_decode_desc* d) {
+  const bool share = sharing_active(d);
+  return pa::workspace_layout(d->num_q_heads / d->cache.num_kv_heads, d->cache.head_dim,
+                              chunk_capacity(d) / pa::kWaves, d->batch, d->num_q_heads,
+                              share ? pa::prefix_parts_of(d->max_blocks_per_seq) : 0);
+}
+
+size_t workspace_bytes_of(const pa_decode_desc* d) { return layout_of(d).total; }
 
 // Resident decode waves on the current device for this kernel instance, cached per device.
 int64_t resident_waves(const pa_decode_desc* d) {
@@ -193,10 +205,9 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
     if (resident > 0 && resident < waves) waves = resident / pa::kWaves * pa::kWaves;
     if (waves < pa::kWaves) waves = pa::kWaves;
   }
-  const pa::WorkspaceLayout lay =
-      pa::workspace_layout(desc->num_q_heads / desc->cache.num_kv_heads, desc->cache.head_dim,
-                           cap_chunks / pa::kWaves);
+  const pa::WorkspaceLayout lay = layout_of(desc);
   char* ws = static_cast<char*>(workspace);
+  const bool share = sharing_active(desc);
 
   pa::DecodeArgs a;
   a.q = q;
@@ -210,6 +221,11 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   a.ws_cnt = reinterpret_cast<int*>(ws);
   a.ws_acc = reinterpret_cast<float*>(ws + lay.acc);
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
+  a.ws_plan = share ? reinterpret_cast<int*>(ws + lay.plan) : nullptr;
+  a.gp_acc = share ? reinterpret_cast<float*>(ws + lay.gp_acc) : nullptr;
+  a.gp_ml = share ? reinterpret_cast<float*>(ws + lay.gp_ml) : nullptr;
+  a.plan_tiles = pa::plan_tiles_of(desc->batch);
+  a.prefix_parts = share ? pa::prefix_parts_of(desc->max_blocks_per_seq) : 0;
   a.batch = desc->batch;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->cache.num_kv_heads;
@@ -221,8 +237,16 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   a.total_waves = (int)waves;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
 
+  // prefix workgroups: one per resident slot, never more than the plan can have units
+  int64_t prefix_wgs = 0;
+  if (share) {
+    const int64_t units = (int64_t)a.plan_tiles * a.num_kv_heads * a.prefix_parts;
+    prefix_wgs = resident_waves(desc) / pa::kWaves;
+    if (prefix_wgs < 1) prefix_wgs = 1;
+    if (prefix_wgs > units) prefix_wgs = units;
+  }
   hipError_t e = pa::launch_decode(a, desc->cache.head_dim, desc->q_dtype, desc->cache.kv_dtype,
-                                   static_cast<hipStream_t>(stream));
+                                   (int)prefix_wgs, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_hip_error = (int32_t)e;
     return PA_ERR_HIP;

@@ -52,13 +52,13 @@ class Dev:
     def append(self):
         pa.pa_kv_append(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache)
 
-    def decode(self, partition_tokens=None, max_context_len=None):
+    def decode(self, partition_tokens=None, max_context_len=None, shared_prefixes=False):
         wl = self.wl
         P = wl.spec.partition_tokens if partition_tokens is None else partition_tokens
         mcl = wl.max_context_len if max_context_len is None else max_context_len
         pa.pa_decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(wl.scale),
                      self.out, k_scale=self.k_scale, v_scale=self.v_scale,
-                     max_context_len=mcl, partition_tokens=P)
+                     max_context_len=mcl, partition_tokens=P, shared_prefixes=shared_prefixes)
         torch.cuda.synchronize()
         return host_bits(self.out)
 

@@ -65,6 +65,7 @@ def _decode(desc, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, tab=FAKE, lens=FAKE,
     (dict(q_dtype=pa.PA_FP8_E4M3), pa.PA_ERR_UNSUPPORTED),
     (dict(kv_dtype=pa.PA_F16), pa.PA_ERR_UNSUPPORTED),     # bf16 q with f16 cache
     (dict(kv_dtype=7), pa.PA_ERR_INVALID_ARG),
+    (dict(shared_prefixes=2), pa.PA_ERR_INVALID_ARG),
 ])
 def test_decode_rejects_descriptor(kw, status):
     d = _desc(**kw)
@@ -127,3 +128,24 @@ def test_append_rejects():
     assert lib.pa_kv_append(ctypes.byref(c), 1, *mis) == pa.PA_ERR_INVALID_ARG
     c2 = pa.CacheDesc(64, 2, 80, 16, pa.PA_BF16)
     assert lib.pa_kv_append(ctypes.byref(c2), 1, *args) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_workspace_with_shared_prefixes():
+    """Shared prefixes add the plan and the prefix partial results when they are taken (group
+    <= 8, batch <= 1024) and nothing otherwise."""
+    d = _desc(max_context_len=100)
+    base = pa.pa_decode_workspace_size(d)
+    s = _desc(max_context_len=100, shared_prefixes=1)
+    B, Hq, D, MB = 4, 8, 64, 7
+    T = max(1, 2 * B // 3)
+    P = -(-min(MB, 256) // 16)
+    plan = _r((5 + B + 19 * T) * 4)
+    parts = _r(B * Hq * P * D * 4) + _r(B * Hq * P * 2 * 4)
+    assert pa.pa_decode_workspace_size(s) == base + plan + parts
+    # group 16 and batches over 1024 run without a plan
+    g16 = dict(num_kv_heads=1, num_q_heads=16)
+    assert (pa.pa_decode_workspace_size(_desc(shared_prefixes=1, **g16))
+            == pa.pa_decode_workspace_size(_desc(**g16)))
+    big = dict(batch=1025, num_blocks=1 << 16)
+    assert (pa.pa_decode_workspace_size(_desc(shared_prefixes=1, **big))
+            == pa.pa_decode_workspace_size(_desc(**big)))

@@ -240,8 +240,9 @@ def test_short_workspace_is_rejected():
 
 @pytest.mark.parametrize("name", workloads.spec_names())
 def test_full_size_workload(name):
-    """Each workload at full size, in the launch configuration the benchmark times: the append is
-    bit-exact over the whole pool and every output element is within tolerance."""
+    """Each workload at full size, in the launch configuration the benchmark times (shared
+    prefixes on for the workload with a shared prefix, and off as well): the append is bit-exact
+    over the whole pool and every output element is within tolerance."""
     wl = workloads.make(name)
     dev = Dev(wl)
     dev.append()
@@ -249,5 +250,6 @@ def test_full_size_workload(name):
     ref, k_ref, v_ref = oracle_after_append(wl)
     assert np.array_equal(host_bits(dev.k_cache), k_ref)
     assert np.array_equal(host_bits(dev.v_cache), v_ref)
-    out = dev.decode()
-    assert_close(out, ref, wl.spec.q_dtype, label=name)
+    for share in ((False, True) if wl.spec.prefix is not None else (False,)):
+        out = dev.decode(shared_prefixes=share)
+        assert_close(out, ref, wl.spec.q_dtype, label=f"{name} shared_prefixes={share}")

@@ -1,0 +1,139 @@
+"""pa_decode with shared_prefixes on, against the fp64 oracle.
+
+Sequences whose block tables start with the same physical blocks share those blocks' K/V (the
+youngju.dev guide, PagedAttention "主な特性", and the Scaling Book note, "プレフィックスキャッシュ").
+The oracle gathers every sequence through its own table row, so it knows nothing of the grouping;
+these cases build tables with groups of every shape the plan distinguishes (shared length odd or
+capped, a member that diverges early, identical rows, members whose last token sits right after
+the shared part, tiles of 1..16 columns, batches where the plan is skipped) and check that the
+result is the same attention within tolerance, and bitwise equal to the unshared path where the
+plan is not taken."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import Dev, assert_close, dev_bits
+from workloads.generate import Spec
+
+pytestmark = pytest.mark.gpu
+BLOCK = 16
+
+
+def _setup(q_dtype, kv_dtype, hkv, g, d, lens, seed):
+    spec = Spec("share", len(lens), hkv * g, hkv, d, q_dtype, kv_dtype, ("list", tuple(lens)),
+                pool=("times", 2), seed=seed)
+    wl = workloads.make(spec)
+    k, v = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
+    return wl, k, v
+
+
+def _share(tables, leader, members, nblocks):
+    for b in members:
+        tables[b, :nblocks] = tables[leader, :nblocks]
+
+
+def _run(wl, k, v, tables, label, P=0, share=True, lens=None):
+    s = wl.spec
+    lens = wl.context_lens if lens is None else np.asarray(lens, dtype=np.int32)
+    dev = Dev(wl)
+    dev.k_cache, dev.v_cache = dev_bits(k, s.kv_dtype), dev_bits(v, s.kv_dtype)
+    dev.tables = torch.from_numpy(np.ascontiguousarray(tables)).cuda()
+    dev.lens = torch.from_numpy(lens).cuda()
+    out = dev.decode(partition_tokens=P, max_context_len=0, shared_prefixes=share)
+    ref = oracle.decode(wl.q, k, v, tables, lens, wl.scale, s.q_dtype, s.kv_dtype, wl.k_scale,
+                        wl.v_scale)
+    assert_close(out, ref, s.q_dtype, label)
+    return out
+
+
+LENS = (700, 1500, 1201, 977, 33, 1300, 48, 49, 2000, 640, 641, 1100, 0, 17, 900, 1024)
+
+GROUPED = [
+    # (q dtype, kv dtype, kv heads, group, head_dim, partition)
+    ("bf16", "bf16", 2, 8, 128, 0),
+    ("bf16", "bf16", 2, 4, 128, 0),
+    ("bf16", "bf16", 2, 4, 128, 64),
+    ("bf16", "bf16", 2, 2, 64, 0),
+    ("bf16", "bf16", 4, 1, 128, 0),
+    ("bf16", "bf16", 2, 3, 128, 0),
+    ("f16", "f16", 2, 4, 128, 0),
+    ("f16", "f16", 2, 8, 64, 512),
+    ("bf16", "fp8_e4m3", 2, 4, 128, 0),
+    ("f16", "fp8_e4m3", 2, 8, 128, 128),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=lambda c: f"{c[0]}-{c[1]}-kv{c[2]}g{c[3]}d{c[4]}"
+                         f"-P{c[5]}")
+def test_groups_of_every_shape(case):
+    qd, kvd, hkv, g, d, P = case
+    wl, k, v = _setup(qd, kvd, hkv, g, d, LENS, seed=61 + GROUPED.index(case))
+    t = wl.block_tables.copy()
+    # group A, leader 1 (94 blocks): 2, 3, 5, 8, 11, 14 share 40 blocks, but 11 diverges at
+    # block 33 -> a shared length of 33 (odd) for the whole group
+    _share(t, 1, (2, 3, 5, 8, 11, 14), 40)
+    t[11, 33:40] = t[9, 33:40]
+    # group B: 9 and 10 share all their blocks; 9 has 640 tokens (40 whole blocks), so the last
+    # one is its own and the shared length is 39
+    _share(t, 9, (10,), 40)
+    # group C: shortest usable group, 48 and 49 tokens share 2 blocks
+    _share(t, 6, (7,), 3)
+    # not a group: 17 tokens share one block with 4 (33 tokens); 15 shares only its first block
+    _share(t, 4, (13,), 1)
+    _share(t, 0, (15,), 1)
+    _run(wl, k, v, t, f"groups {case}", P=P)
+
+
+def test_shared_length_is_capped_and_members_keep_their_last_block():
+    # 0 and 1 have identical rows of 313 blocks and 2 (4097 tokens) shares 257: the shared part
+    # stops at 256 blocks, so 2 keeps the block of its last token.  3 (4096 tokens) and 4 (300)
+    # share 19 blocks, of which 4 keeps the last one: 18 are shared.
+    lens = (5000, 5000, 4097, 4096, 300)
+    wl, k, v = _setup("bf16", "bf16", 2, 4, 128, lens, seed=71)
+    t = wl.block_tables.copy()
+    _share(t, 0, (1,), 313)
+    _share(t, 0, (2,), 257)
+    _share(t, 3, (4,), 19)
+    _run(wl, k, v, t, "cap 256")
+
+
+def test_many_members_fill_several_tiles():
+    # group of 1 (MHA): 16 members per tile -> tiles of 16, 16, 8; a second group of 3
+    lens = [800 + 37 * i for i in range(44)]
+    wl, k, v = _setup("bf16", "bf16", 2, 1, 128, lens, seed=72)
+    t = wl.block_tables.copy()
+    _share(t, 3, [b for b in range(40) if b != 3], 48)
+    _share(t, 40, (41, 42), 20)
+    _run(wl, k, v, t, "tiles of 16")
+    # group of 8: two members per tile -> 4 tiles for 7 members
+    lens = [500 + 11 * i for i in range(9)]
+    wl, k, v = _setup("bf16", "bf16", 2, 8, 128, lens, seed=73)
+    t = wl.block_tables.copy()
+    _share(t, 0, range(1, 7), 30)
+    _run(wl, k, v, t, "tiles of 2")
+
+
+def test_repeat_runs_bitwise_identical_with_sharing():
+    wl, k, v = _setup("bf16", "bf16", 2, 4, 128, LENS, seed=74)
+    t = wl.block_tables.copy()
+    _share(t, 1, (2, 3, 5, 8, 11, 14), 40)
+    first = _run(wl, k, v, t, "repeat")
+    for _ in range(3):
+        assert np.array_equal(_run(wl, k, v, t, "repeat"), first)
+
+
+@pytest.mark.parametrize("g,batch", [(16, 8), (4, 1100)])
+def test_plan_not_taken_is_the_unshared_path(g, batch):
+    """group 16 (one member per tile) and batches over 1024 are run without a plan: bitwise the
+    same output as with shared_prefixes off."""
+    rng = np.random.default_rng(75)
+    lens = rng.integers(40, 400 if batch > 100 else 2000, size=batch)
+    wl, k, v = _setup("bf16", "bf16", 1, g, 128, lens, seed=75)
+    t = wl.block_tables.copy()
+    _share(t, 0, range(1, batch // 2), 2)
+    on = _run(wl, k, v, t, f"g{g} b{batch} on", share=True)
+    off = _run(wl, k, v, t, f"g{g} b{batch} off", share=False)
+    assert np.array_equal(on, off)
