@@ -153,7 +153,9 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
 /* Bytes of workspace pa_decode needs for this descriptor, or 0 if the descriptor is invalid
  * (pa_decode reports why).  It depends only on the descriptor, not on the GPU:
  * 262144 + workgroups * 2 * group * (head_dim + 2) * 4 bytes (each part rounded up to 256),
- * with workgroups <= 2048 when partition_tokens is 0.  Shared prefixes, when taken, add a plan
+ * where workgroups = ceil(chunks / 8): at most 1024 when partition_tokens is 0, else the
+ * chunks of partition_tokens / 16 blocks that cover batch * num_kv_heads *
+ * ceil(max_context_len / 16) blocks.  Shared prefixes, when taken, add a plan
  * of (5 + batch + 19 * T) * 4 bytes with T = max(1, floor(2 * batch / 3)), and
  * batch * num_q_heads * P * (head_dim + 2) * 4 bytes of partial results with
  * P = ceil(min(max_blocks_per_seq, 256) / 16) (each part rounded up to 256). */

@@ -15,12 +15,15 @@
 //  * Balanced split-KV.  The (sequence, KV head, logical block) space is flattened into W blocks
 //    and cut into equal chunks, one per wave, so every wave streams the same number of bytes
 //    regardless of how ragged the batch is, and a launch is about one wave per resident slot
-//    (no empty workgroups).  Each workgroup finds its waves' chunk starts with a prefix scan of
-//    the context lengths.  A wave walks its chunk piece by piece (a piece = the part of one
+//    (no empty workgroups).  A workgroup is eight waves and fills its CU: the waves of one
+//    workgroup start together and progress at the same rate, while two workgroups sharing a CU
+//    were measured to finish far apart (the later one starts its stream later and streams
+//    slower), leaving a tail.  Each workgroup finds its waves' chunk starts with a prefix scan
+//    of the context lengths.  A wave walks its chunk piece by piece (a piece = the part of one
 //    (sequence, KV head) inside the chunk): a piece that is a whole sequence head is normalised
 //    and written out; a cut piece keeps its running max, exp-sum and unnormalised output.
-//  * Log-sum-exp merge in two levels, inside this one kernel.  The four waves of a workgroup own
-//    four consecutive chunks; their cut pieces meet in LDS and are merged in chunk order, so a
+//  * Log-sum-exp merge in two levels, inside this one kernel.  The eight waves of a workgroup
+//    own eight consecutive chunks; their cut pieces meet in LDS and are merged in chunk order, so a
 //    sequence head that ends inside the workgroup is written out there.  A piece cut at a
 //    workgroup boundary is published to the workspace with device-coherent stores, and an atomic
 //    counter per boundary elects the last workgroup to arrive, which reads all parts of that
@@ -365,15 +368,158 @@ __device__ __forceinline__ void fold_prefix(const DecodeArgs& a, size_t row, int
   }
 }
 
+// Parts merged with one round of loads per thread (more are staged through LDS in batches).
+constexpr int kMergeDirect = 16;
+
+// Merges all parts of sequence head (b, kvh) and writes its normalised output rows: the prefix
+// partial results (if any shared blocks were skipped), then the parts published by workgroups
+// c0..c1 (workgroup c0 holds it in its slot 0 only if the head starts exactly at its range).
+// Called by every thread of the workgroup.
+template <int D, int QT>
+__device__ __forceinline__ void merge_published(const DecodeArgs& a, int b, int kvh, int skip,
+                                                int s0, int c0,
+                                int c1, int WGB, float (&sm_mw)[kMergeStage][16],
+                                float (&sm_ml)[kMergeStage][16], float* sm_hm, float* sm_hl) {
+  typedef typename Mfma<QT>::elem E;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int G = a.group;
+  const int first_slot = s0 != c0 * WGB ? 1 : 0;
+  const int npre = skip > 0 ? prefix_parts(skip) : 0;
+  const size_t row0 = (size_t)b * a.num_q_heads + kvh * G;
+  // part pi of head g: a prefix partial result (pi < npre) or a published part
+  auto published = [&](int pi, int g) -> size_t {
+    const int cc = c0 + pi - npre;
+    return ((size_t)cc * 2 + (cc == c0 ? first_slot : 0)) * G + g;
+  };
+  // Both kinds of parts live in the workspace: address them from one base (a select between
+  // two base pointers here makes the compiler keep them in scratch memory).
+  const ptrdiff_t gp_ml_off = npre > 0 ? a.gp_ml - a.ws_ml : 0;
+  const ptrdiff_t gp_acc_off = npre > 0 ? a.gp_acc - a.ws_acc : 0;
+  auto load_ml = [&](int pi, int g) {
+    const ptrdiff_t off = pi < npre
+                              ? gp_ml_off + (ptrdiff_t)((row0 + g) * a.prefix_parts + pi) * 2
+                              : (ptrdiff_t)published(pi, g) * 2;
+    return load_coherent2(a.ws_ml + off);
+  };
+  auto load_acc = [&](int pi, int g, int d) {
+    const ptrdiff_t off = pi < npre
+                              ? gp_acc_off + (ptrdiff_t)((row0 + g) * a.prefix_parts + pi) * D
+                              : (ptrdiff_t)published(pi, g) * D;
+    return load_coherent4(a.ws_acc + off + d);
+  };
+  const int nparts = npre + c1 - c0 + 1;
+  E* rows = reinterpret_cast<E*>(a.out) + row0 * D;
+  constexpr int EPT = 16 * D / 4 / (64 * kWaves) > 0 ? 16 * D / 4 / (64 * kWaves) : 1;
+
+  if (nparts <= kMergeDirect) {
+    // each thread loads every part's (max, exp-sum) for its head and its four output columns
+    // at once and merges them on its own
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int e = (tid + x * nthr) * 4;
+      if (e >= G * D) break;
+      const int g = e / D, d = e - g * D;
+      f32x2 ml[kMergeDirect];
+      f32x4 part[kMergeDirect];
+#pragma unroll
+      for (int k = 0; k < kMergeDirect; ++k)
+        if (k < nparts) {
+          ml[k] = load_ml(k, g);
+          part[k] = load_acc(k, g, d);
+        }
+      float M_ = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kMergeDirect; ++k)
+        if (k < nparts) M_ = fmaxf(M_, ml[k][0]);
+      float Ls = 0.0f;
+      f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < kMergeDirect; ++k)
+        if (k < nparts) {
+          const float w = fast_exp2(ml[k][0] - M_);
+          Ls += w * ml[k][1];
+          o += w * part[k];
+        }
+      *reinterpret_cast<uint2*>(rows + e) =
+          make_uint2(pack2<QT>(o[0] / Ls, o[1] / Ls), pack2<QT>(o[2] / Ls, o[3] / Ls));
+    }
+    return;
+  }
+
+  // Many parts: batches of up to kMergeStage; their (max, exp-sum) pairs are staged in LDS with
+  // one round of loads, then every thread loads all its output columns of the batch at once.
+  f32x4 o[EPT];
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) o[x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (tid < 16) {
+    sm_hm[tid] = -INFINITY;
+    sm_hl[tid] = 0.0f;
+  }
+  for (int pb = 0; pb < nparts; pb += kMergeStage) {
+    const int n = min(kMergeStage, nparts - pb);
+    __syncthreads();
+    for (int t = tid; t < n * G; t += nthr) {
+      const f32x2 ml = load_ml(pb + t / G, t % G);
+      sm_mw[t / G][t % G] = ml[0];
+      sm_ml[t / G][t % G] = ml[1];
+    }
+    __syncthreads();
+    // per head: new running max; rescale of what is already accumulated
+    if (tid < G) {
+      float M_ = sm_hm[tid];
+      for (int k = 0; k < n; ++k) M_ = fmaxf(M_, sm_mw[k][tid]);
+      const float r = M_ == sm_hm[tid] ? 1.0f : fast_exp2(sm_hm[tid] - M_);
+      float Ls = sm_hl[tid] * r;
+      for (int k = 0; k < n; ++k) {
+        const float w = fast_exp2(sm_mw[k][tid] - M_);
+        sm_mw[k][tid] = w;
+        Ls += w * sm_ml[k][tid];
+      }
+      sm_ml[0][tid] = r;          // rescale factor for this batch (read below)
+      sm_hm[tid] = M_;
+      sm_hl[tid] = Ls;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int e = (tid + x * nthr) * 4;
+      if (e >= G * D) break;
+      const int g = e / D, d = e - g * D;
+      f32x4 acc_b = o[x] * sm_ml[0][g];
+      f32x4 part[kMergeStage / 4];
+      for (int k0 = 0; k0 < n; k0 += kMergeStage / 4) {
+        const int m = min(kMergeStage / 4, n - k0);
+#pragma unroll
+        for (int k = 0; k < kMergeStage / 4; ++k)
+          if (k < m) part[k] = load_acc(pb + k0 + k, g, d);
+#pragma unroll
+        for (int k = 0; k < kMergeStage / 4; ++k)
+          if (k < m) acc_b += sm_mw[k0 + k][g] * part[k];
+      }
+      o[x] = acc_b;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    const int e = (tid + x * nthr) * 4;
+    if (e >= G * D) break;
+    const int g = e / D;
+    const float Ls = sm_hl[g];
+    *reinterpret_cast<uint2*>(rows + e) =
+        make_uint2(pack2<QT>(o[x][0] / Ls, o[x][1] / Ls), pack2<QT>(o[x][2] / Ls, o[x][3] / Ls));
+  }
+}
+
 template <int D, int QT, int KVT>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeArgs a) {
   typedef Stepper<D, QT, KVT> St;
   typedef typename St::V8 V8;
   typedef typename St::E E;
   constexpr int NC = St::NC;
   constexpr int NT = St::NT;
-  static_assert(NT % kWaves == 0, "the merge phase gives each wave NT/4 tiles");
-  constexpr int TPW = NT / kWaves;
+  // the merge phase gives wave w the 16-dim tiles w, w + kWaves, ... (none when w >= NT)
+  constexpr int TPW = (NT + kWaves - 1) / kWaves;
 
   __shared__ int sm_wave_sum[kWaves];
   __shared__ int sm_start_b[kWaves], sm_start_off[kWaves], sm_start_L[kWaves];
@@ -381,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __shared__ PieceMeta sm_meta[kWaves][2];          // [wave][first / last cut piece]
   __shared__ float sm_pm[kWaves][2][16], sm_pl[kWaves][2][16];
   __shared__ f32x4 sm_pacc[kWaves][2][NT][64];
-  __shared__ int sm_last;
+  __shared__ int sm_last[2];
   __shared__ float sm_mw[kMergeStage][16], sm_ml[kMergeStage][16];   // staged parts: m, l
   __shared__ float sm_hm[16], sm_hl[16];                              // per head: max, exp-sum
 
@@ -531,136 +677,64 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- 3. Merge the cut pieces of the four chunks, in chunk order.  Each wave now handles
-  // tiles wave, wave+4, ... of every piece.  A group of parts of one sequence head that covers
-  // all its blocks is written out; a group cut at the workgroup boundary is published and the
-  // last workgroup to publish a part of that sequence head merges all of them.
+  // ---- 3. Merge the cut pieces of the workgroup's chunks, in chunk order.  Each wave now
+  // handles tiles wave, wave + kWaves, ... of every piece.  A group of parts of one sequence
+  // head that covers all its blocks is written out.  A group cut at the workgroup boundary (at
+  // most two: one continuing from before the range, one running past its end) is published;
+  // then, after one wait and one round of arrival counts for both, the last workgroup to publish
+  // a part of a sequence head merges all of them.
   const int WGB = kWaves * Cw;                      // blocks per workgroup range
   int gb = -1, gkvh = 0, gj0 = 0, gj1 = 0, gnblk = 0, gskip = 0, gs0 = 0;
   float gm = -INFINITY, gl = 0.0f;
   f32x4 go[TPW];
+  auto tile_of = [&](int t) { return wave + kWaves * t; };   // < NT: this wave's t-th tile
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) go[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto merge_published = [&](int c0, int c1) {
-    // The parts of sequence head (gb, gkvh): its prefix parts (if any), then the parts published
-    // by workgroups c0..c1.  Workgroup c0 holds it as its first group (slot 0) only if the
-    // sequence head starts exactly at its range.  Batches of up to kMergeStage parts: their
-    // (max, exp-sum) pairs are staged in LDS with one round of loads, then every thread loads
-    // all its output columns of the batch at once.
-    const int first_slot = gs0 != c0 * WGB ? 1 : 0;
-    const int npre = gskip > 0 ? prefix_parts(gskip) : 0;
-    const size_t row0 = (size_t)gb * Hq + gkvh * G;
-    auto part_of = [&](int pi, int g) -> size_t {   // index of part pi of head g in its array
-      if (pi < npre) return (row0 + g) * a.prefix_parts + pi;
-      const int cc = c0 + pi - npre;
-      return ((size_t)cc * 2 + (cc == c0 ? first_slot : 0)) * G + g;
-    };
-    auto ml_of = [&](int pi, int g) { return (pi < npre ? a.gp_ml : a.ws_ml) + part_of(pi, g) * 2; };
-    auto acc_of = [&](int pi, int g) {
-      return (pi < npre ? a.gp_acc : a.ws_acc) + part_of(pi, g) * D;
-    };
-    const int nparts = npre + c1 - c0 + 1;
-    E* rows = reinterpret_cast<E*>(a.out) + row0 * D;
-    constexpr int EPT = 16 * D / 4 / (64 * kWaves);          // float4 columns per thread (G=16)
-    f32x4 o[EPT > 0 ? EPT : 1];
-#pragma unroll
-    for (int x = 0; x < (EPT > 0 ? EPT : 1); ++x) o[x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (tid < 16) { sm_hm[tid] = -INFINITY; sm_hl[tid] = 0.0f; }
-    for (int pb = 0; pb < nparts; pb += kMergeStage) {
-      const int n = min(kMergeStage, nparts - pb);
-      __syncthreads();
-      for (int t = tid; t < n * G; t += blockDim.x) {
-        const float* ml = ml_of(pb + t / G, t % G);
-        sm_mw[t / G][t % G] = load_coherent(ml);
-        sm_ml[t / G][t % G] = load_coherent(ml + 1);
-      }
-      __syncthreads();
-      // per head: new running max; rescale of what is already accumulated
-      if (tid < G) {
-        float M_ = sm_hm[tid];
-        for (int k = 0; k < n; ++k) M_ = fmaxf(M_, sm_mw[k][tid]);
-        const float r = M_ == sm_hm[tid] ? 1.0f : fast_exp2(sm_hm[tid] - M_);
-        float Ls = sm_hl[tid] * r;
-        for (int k = 0; k < n; ++k) {
-          const float w = fast_exp2(sm_mw[k][tid] - M_);
-          sm_mw[k][tid] = w;
-          Ls += w * sm_ml[k][tid];
-        }
-        sm_ml[0][tid] = r;          // rescale factor for this batch (read below)
-        sm_hm[tid] = M_;
-        sm_hl[tid] = Ls;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int x = 0; x < (EPT > 0 ? EPT : 1); ++x) {
-        const int e = (tid + x * blockDim.x) * 4;
-        if (e >= G * D) break;
-        const int g = e / D, d = e - g * D;
-        f32x4 acc_b = o[x] * sm_ml[0][g];
-        f32x4 part[kMergeStage / 4];
-        for (int k0 = 0; k0 < n; k0 += kMergeStage / 4) {
-          const int m = min(kMergeStage / 4, n - k0);
-#pragma unroll
-          for (int k = 0; k < kMergeStage / 4; ++k)
-            if (k < m) part[k] = load_coherent4(acc_of(pb + k0 + k, g) + d);
-#pragma unroll
-          for (int k = 0; k < kMergeStage / 4; ++k)
-            if (k < m) acc_b += sm_mw[k0 + k][g] * part[k];
-        }
-        o[x] = acc_b;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < (EPT > 0 ? EPT : 1); ++x) {
-      const int e = (tid + x * blockDim.x) * 4;
-      if (e >= G * D) break;
-      const int g = e / D;
-      const float Ls = sm_hl[g];
-      *reinterpret_cast<uint2*>(rows + e) =
-          make_uint2(pack2<QT>(o[x][0] / Ls, o[x][1] / Ls), pack2<QT>(o[x][2] / Ls, o[x][3] / Ls));
-    }
-  };
+  // the cut groups this workgroup publishes (at most two), field by field in registers
+  int npub = 0, pb_b[2] = {0, 0}, pb_kvh[2] = {0, 0}, pb_skip[2] = {0, 0}, pb_s0[2] = {0, 0};
+  int pb_c0[2] = {0, 0}, pb_c1[2] = {0, 0};
 
   auto emit = [&]() {
     if (gj0 == gskip && gj1 == gnblk) {
-      if (col < G) {
+      if (col < G && wave < NT) {
         const size_t row = (size_t)gb * Hq + gkvh * G + col;
         if (gskip > 0) fold_prefix<D>(a, row, prefix_parts(gskip), grp, wave, kWaves, gm, gl, go);
         E* out = reinterpret_cast<E*>(a.out) + row * D + 4 * grp;
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
-          *reinterpret_cast<uint2*>(out + 16 * (wave + kWaves * t)) =
-              make_uint2(pack2<QT>(go[t][0] / gl, go[t][1] / gl),
-                         pack2<QT>(go[t][2] / gl, go[t][3] / gl));
+          if (tile_of(t) < NT)
+            *reinterpret_cast<uint2*>(out + 16 * tile_of(t)) =
+                make_uint2(pack2<QT>(go[t][0] / gl, go[t][1] / gl),
+                           pack2<QT>(go[t][2] / gl, go[t][3] / gl));
       }
     } else {
       // slot 1 holds the group whose sequence head starts strictly inside this workgroup's
       // range (it runs past the end); slot 0 the one that started at or before the range start
       const int wslot = gs0 > (int)blockIdx.x * WGB ? 1 : 0;
       const size_t ps = ((size_t)blockIdx.x * 2 + wslot) * G + col;
-      // publish with device-coherent stores, wait for them to complete, then count the part;
-      // the counter's last arrival reads the parts back with device-coherent loads
-      if (col < G) {
+      if (col < G) {                                // device-coherent stores
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
-          store_coherent(a.ws_acc + ps * D + 16 * (wave + kWaves * t) + 4 * grp, go[t]);
+          if (tile_of(t) < NT)
+            store_coherent(a.ws_acc + ps * D + 16 * tile_of(t) + 4 * grp, go[t]);
         if (wave == 0 && grp == 0) {
           store_coherent(a.ws_ml + ps * 2, gm);
           store_coherent(a.ws_ml + ps * 2 + 1, gl);
         }
       }
-      wait_memory_ops();
-      __syncthreads();
       const int c0 = gs0 / WGB, c1 = (gs0 + (gnblk - gskip) - 1) / WGB;
-      if (tid == 0)
-        sm_last = __hip_atomic_fetch_add(a.ws_cnt + c1, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == c1 - c0;
-      __syncthreads();
-      if (sm_last) {
-        merge_published(c0, c1);
-        if (tid == 0)                                 // ready for the next call
-          __hip_atomic_store(a.ws_cnt + c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        if (x == npub) {
+          pb_b[x] = gb;
+          pb_kvh[x] = gkvh;
+          pb_skip[x] = gskip;
+          pb_s0[x] = gs0;
+          pb_c0[x] = c0;
+          pb_c1[x] = c1;
+        }
+      ++npub;
     }
   };
 
@@ -674,7 +748,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       gl = gl * x + pl * y;
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
-        go[t] = go[t] * x + sm_pacc[k >> 1][k & 1][wave + kWaves * t][lane] * y;
+        if (tile_of(t) < NT) go[t] = go[t] * x + sm_pacc[k >> 1][k & 1][tile_of(t)][lane] * y;
       gm = M_;
       gj1 = mt.j1;
     } else {
@@ -689,10 +763,34 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       gm = pm;
       gl = pl;
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) go[t] = sm_pacc[k >> 1][k & 1][wave + kWaves * t][lane];
+      for (int t = 0; t < TPW; ++t)
+        if (tile_of(t) < NT) go[t] = sm_pacc[k >> 1][k & 1][tile_of(t)][lane];
     }
   }
   if (gb >= 0) emit();
+  if (npub == 0) return;
+
+  // Wait for the published parts to complete, then count them: the counter of a sequence head
+  // sits at the last workgroup range it touches, and its last arrival merges.
+  wait_memory_ops();
+  __syncthreads();
+  // both counts in flight at once, from two waves
+  if (tid == 0 || (tid == 64 && npub > 1)) {
+    const int x = tid == 0 ? 0 : 1;
+    const int c0 = x == 0 ? pb_c0[0] : pb_c0[1], c1 = x == 0 ? pb_c1[0] : pb_c1[1];
+    sm_last[x] = __hip_atomic_fetch_add(a.ws_cnt + c1, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == c1 - c0;
+  }
+  __syncthreads();
+  for (int x = 0; x < npub; ++x) {
+    if (!sm_last[x]) continue;
+    const int c1 = x == 0 ? pb_c1[0] : pb_c1[1];
+    merge_published<D, QT>(a, x == 0 ? pb_b[0] : pb_b[1], x == 0 ? pb_kvh[0] : pb_kvh[1],
+                           x == 0 ? pb_skip[0] : pb_skip[1], x == 0 ? pb_s0[0] : pb_s0[1],
+                           x == 0 ? pb_c0[0] : pb_c0[1], c1, WGB, sm_mw, sm_ml, sm_hm, sm_hl);
+    if (tid == 0)                                   // ready for the next call
+      __hip_atomic_store(a.ws_cnt + c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---- Shared prefixes.
@@ -863,17 +961,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
 }
 
 // One workgroup per unit: the shared blocks [16k, min(p, 16k + 16)) of one KV head, read once
-// for all members of a tile (column r*group + g = query head g of member r).  The four waves
+// for all members of a tile (column r*group + g = query head g of member r).  The waves
 // take the unit's 32-token steps in turn and merge in LDS; the unnormalised result and its
 // (max, exp-sum) are left for decode_kernel as part k of each member's query rows.
 template <int D, int QT, int KVT>
-__global__ __launch_bounds__(256, 2) void prefix_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeArgs a) {
   typedef Stepper<D, QT, KVT, false> St;
   typedef typename St::V8 V8;
   typedef typename St::E E;
   constexpr int NC = St::NC;
   constexpr int NT = St::NT;
-  constexpr int TPW = NT / kWaves;
+  constexpr int TPW = (NT + kWaves - 1) / kWaves;   // tiles w, w + kWaves, ... of wave w
   constexpr int kMaxTiles = 2 * kPlanMaxBatch / 3;
 
   __shared__ int sm_ub[kMaxTiles + 1], sm_lead[kMaxTiles], sm_p[kMaxTiles];
@@ -948,6 +1046,7 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(DecodeArgs a) {
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) {
         const int ti = wave + kWaves * tt;
+        if (ti >= NT) break;
         f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) o += sm_acc[w][ti][lane] * wt[w];

@@ -83,6 +83,11 @@ __device__ __forceinline__ void store_coherent(float* p, f32x4 v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ f32x2 load_coherent2(const float* p) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+  return __builtin_bit_cast(f32x2,
+                            __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
 __device__ __forceinline__ f32x4 load_coherent4(const float* p) {
   uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
   const f32x2 a = __builtin_bit_cast(

@@ -9,7 +9,10 @@ namespace pa {
 
 constexpr int kBlock = 16;          // tokens per physical KV block
 constexpr int kStepTokens = 32;     // tokens one wave consumes per step (two blocks)
-constexpr int kWaves = 4;           // waves per decode workgroup
+#ifndef PA_WG_WAVES
+#define PA_WG_WAVES 8
+#endif
+constexpr int kWaves = PA_WG_WAVES;  // waves per decode workgroup (4: two per CU, 8: one per CU)
 constexpr int kMaxPartition = 65536; // largest fixed key partition (tokens)
 
 struct AppendArgs {

@@ -92,9 +92,10 @@ COUNTERS = 65536 * 4
 
 def test_workspace_size_and_check():
     # fixed chunks of 32 tokens (2 blocks): the upper bound of the flattened space is
-    # 4 sequences x 2 kv heads x ceil(100/16)=7 blocks = 56 blocks -> 28 chunks -> 7 workgroups
+    # 4 sequences x 2 kv heads x ceil(100/16)=7 blocks = 56 blocks -> 28 chunks -> 4 workgroups
+    # of 8 waves
     d = _desc(max_context_len=100, partition_tokens=32)
-    wgs = 7
+    wgs = 4
     expect = COUNTERS + _r(wgs * 2 * 4 * 64 * 4) + _r(wgs * 2 * 4 * 2 * 4)
     assert pa.pa_decode_workspace_size(d) == expect
     # balanced chunks: at most one per two-block slice of the space
@@ -105,9 +106,9 @@ def test_workspace_size_and_check():
     # a longer hint never shrinks the workspace; the table row (7 blocks) caps it
     sizes = [pa.pa_decode_workspace_size(_desc(max_context_len=L)) for L in (32, 64, 100, 112, 500)]
     assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]
-    # balanced mode never launches more than 8192 waves = 2048 workgroups
+    # balanced mode never launches more than 8192 waves = 1024 workgroups
     big = _desc(batch=4096, num_blocks=1 << 20, max_blocks_per_seq=4096)
-    cap = COUNTERS + _r(2048 * 2 * 4 * 64 * 4) + _r(2048 * 2 * 4 * 2 * 4)
+    cap = COUNTERS + _r(1024 * 2 * 4 * 64 * 4) + _r(1024 * 2 * 4 * 2 * 4)
     assert pa.pa_decode_workspace_size(big) == cap
     # fixed partitions beyond 65536 workgroups are refused
     huge = _desc(batch=4096, num_blocks=1 << 20, max_blocks_per_seq=4096, partition_tokens=32)
