@@ -136,12 +136,12 @@ pa_status pa_kv_append(const pa_cache_desc* cache, int32_t num_tokens,
  * (F16, FP8_E4M3).  Accumulation is fp32.  Results depend only on logical token positions and
  * on the context lengths of the batch (which set the chunk boundaries), so the same data behind
  * any physical block placement gives bit-identical output (with shared_prefixes 0).  One kernel
- * is enqueued; with shared prefixes taken, a planning and a prefix kernel run before it.
+ * is enqueued; with shared prefixes taken, a prefix kernel runs before it.
  *
- * Shared prefixes: a planning pass groups the sequences whose first block-table entries are
- * equal; the shared length of a group is the number of leading entries every member has in
- * common with the group's first sequence, stops before the block that holds any member's last
- * token and is at most 256 blocks; groups sharing fewer than two blocks are not used.  The shared
+ * Shared prefixes: the sequences whose first block-table entries are equal form a group; the
+ * shared length of a group is the number of leading entries every member has in common with the
+ * group's first sequence, stops before the block that holds any member's last token and is at
+ * most 256 blocks; groups sharing fewer than two blocks are not used.  The shared
  * blocks' partial softmax results are merged into each member's own with the log-sum-exp rule.
  * Results then also depend on the grouping (not on which member gets which MFMA column).
  */
@@ -155,10 +155,9 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
  * 262144 + workgroups * 2 * group * (head_dim + 2) * 4 bytes (each part rounded up to 256),
  * where workgroups = ceil(chunks / 8): at most 1024 when partition_tokens is 0, else the
  * chunks of partition_tokens / 16 blocks that cover batch * num_kv_heads *
- * ceil(max_context_len / 16) blocks.  Shared prefixes, when taken, add a plan
- * of (5 + batch + 19 * T) * 4 bytes with T = max(1, floor(2 * batch / 3)), and
- * batch * num_q_heads * P * (head_dim + 2) * 4 bytes of partial results with
- * P = ceil(min(max_blocks_per_seq, 256) / 16) (each part rounded up to 256). */
+ * ceil(max_context_len / 16) blocks.  Shared prefixes, when taken, add batch * 4 bytes of
+ * per-sequence counts and batch * num_q_heads * P * (head_dim + 2) * 4 bytes of partial results
+ * with P = ceil(min(max_blocks_per_seq, 256) / 32) (each part rounded up to 256). */
 size_t pa_decode_workspace_size(const pa_decode_desc* desc);
 
 /* A static, human-readable name for a status code. */

@@ -33,7 +33,7 @@
 //    results are identical for any block placement.
 //  * Shared prefixes (opt-in).  Sequences whose block tables start with the same physical blocks
 //    (a prefix cache shares blocks this way: youngju.dev guide, PagedAttention "主な特性"; Scaling
-//    Book note, "プレフィックスキャッシュ") are grouped by plan_kernel, and prefix_kernel reads
+//    Book note, "プレフィックスキャッシュ") are grouped by prefix_kernel, which runs first and reads
 //    each shared block once per tile of up to 16/group members (their query heads fill the 16
 //    columns of an MFMA tile) instead of once per sequence.  It leaves every member's partial
 //    results (running max, exp-sum, unnormalised output) over the shared blocks in the
@@ -96,8 +96,8 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // plan never takes the block holding a sequence's last token, so at least one block is left;
 // the clamp only keeps indexing in range.
 __device__ __forceinline__ int skip_of(const DecodeArgs& a, int b, int nblk) {
-  if (!a.ws_plan) return 0;
-  const int s = a.ws_plan[kPlanHeader + b];
+  if (!a.ws_skip) return 0;
+  const int s = a.ws_skip[b];
   return max(0, min(s, nblk - 1));
 }
 
@@ -795,16 +795,21 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
 
 // ---- Shared prefixes.
 //
-// plan_kernel (one workgroup, one thread per sequence) groups the sequences whose block tables
-// start with the same physical block, finds how many leading entries every member shares with
-// the group's first sequence (its leader), and lays the groups out as tiles of up to 16/group
-// members.  The shared length stops before the block that holds a member's last token, so every
-// sequence keeps at least one block of its own, and is capped at kMaxSharedBlocks.  Which tile
-// and column a member gets depends on the order of LDS atomics, but the columns of an MFMA tile
-// never mix, so results do not.
+// prefix_kernel groups the sequences whose block tables start with the same physical block,
+// finds how many leading entries every member shares with the group's first sequence (its
+// leader), and lays each group out as tiles of up to 16/group members in sequence order.  The
+// shared length stops before the block that holds a member's last token, so every sequence
+// keeps at least one block of its own, and is capped at kMaxSharedBlocks.  Every workgroup
+// makes this plan in its own LDS (it depends only on the lengths and tables, so all agree);
+// workgroup 0 also writes each sequence's skipped block count for decode_kernel.  Then the
+// workgroups take the units: the shared blocks [32k, min(p, 32k + 32)) of one KV head for the
+// members of one tile (column r*group + g = query head g of member r), read once.  The waves
+// take the unit's 32-token steps in turn and merge in LDS; the unnormalised result and its
+// (max, exp-sum) are left for decode_kernel as part k of each member's query rows.
 
-// Exclusive prefix sum over the workgroup's kPlanThreads threads; `total` gets the sum.
-__device__ __forceinline__ int plan_scan(int v, int* sm, int& total) {
+// Exclusive prefix sum over the workgroup's threads (in thread order); `total` gets the sum.
+template <int NTH>
+__device__ __forceinline__ int block_scan(int v, int* sm, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -817,7 +822,7 @@ __device__ __forceinline__ int plan_scan(int v, int* sm, int& total) {
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int i = 0; i < kPlanThreads / 64; ++i) {
+  for (int i = 0; i < NTH / 64; ++i) {
     const int x = sm[i];
     before += i < w ? x : 0;
     total += x;
@@ -826,144 +831,6 @@ __device__ __forceinline__ int plan_scan(int v, int* sm, int& total) {
   return before + incl - v;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
-  constexpr int HS = 2048;                          // hash slots: more than twice the batch
-  static_assert(HS == 2 * kPlanThreads && kPlanThreads >= kPlanMaxBatch, "plan sizes");
-  __shared__ int h_key[HS], h_lead[HS], h_cnt[HS], h_p[HS], h_ub[HS];
-  __shared__ int s_full[kPlanThreads], s_rank[kPlanThreads], s_slot[kPlanThreads];
-  __shared__ int s_off[kPlanThreads], s_cmp[kPlanThreads];
-  __shared__ int s_scan[kPlanThreads / 64];
-
-  const int tid = threadIdx.x;
-  const int B = a.batch, MB = a.max_blocks_per_seq, S = 16 / a.group;
-  const PlanLayout pl(B, a.plan_tiles);
-  int* plan = a.ws_plan;
-  for (int i = tid; i < HS; i += kPlanThreads) {
-    h_key[i] = -1;
-    h_lead[i] = INT_MAX;
-    h_cnt[i] = 0;
-    h_p[i] = INT_MAX;
-  }
-  __syncthreads();
-
-  // 1. Candidates (two or more whole blocks before the one with the last token), hashed by
-  // their first physical block; the leader is the smallest sequence index of a group.
-  const int b = tid;
-  int slot = -1, full = 0;
-  if (b < B) {
-    const int L = clamp_len(a.context_lens[b], a.len_cap);
-    const int key = a.block_tables[(size_t)b * MB];
-    full = L > 0 ? min((L - 1) / kBlock, kMaxSharedBlocks) : 0;
-    if (full >= 2 && (unsigned)key < (unsigned)a.num_blocks) {
-      unsigned h = ((unsigned)key * 2654435761u) >> 21;
-      for (;;) {                                    // ends: fewer keys than slots
-        const int prev = atomicCAS(&h_key[h], -1, key);
-        if (prev == -1 || prev == key) break;
-        h = (h + 1) & (HS - 1);
-      }
-      slot = (int)h;
-      atomicMin(&h_lead[slot], b);
-      s_rank[b] = atomicAdd(&h_cnt[slot], 1);
-    }
-  }
-  s_full[tid] = full;
-  s_slot[tid] = slot;
-  __syncthreads();
-
-  // 2. Shared length of a group: the first table entry where a member differs from the leader,
-  // at most the shorter of their whole-block counts.  The comparisons go in runs of 8 entries,
-  // spread over all threads.
-  int nrun = 0, cmp = 0;
-  if (slot >= 0) {
-    const int lead = h_lead[slot];
-    cmp = min(full, s_full[lead]);
-    atomicMin(&h_p[slot], cmp);
-    if (b != lead) nrun = (cmp - 1 + 7) / 8;        // entries 1 .. cmp-1; entry 0 is the key
-  }
-  s_cmp[tid] = cmp;
-  int nruns;
-  s_off[tid] = plan_scan(nrun, s_scan, nruns);
-  __syncthreads();
-  for (int i = tid; i < nruns; i += kPlanThreads) {
-    int lo = 0, hi = kPlanThreads - 1;              // last thread whose runs start at or before i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int m = lo, sl = s_slot[m];
-    const int j0 = 1 + 8 * (i - s_off[m]), j1 = min(j0 + 8, s_cmp[m]);
-    const int32_t* rm = a.block_tables + (size_t)m * MB;
-    const int32_t* rl = a.block_tables + (size_t)h_lead[sl] * MB;
-    int x[8], y[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      x[u] = j0 + u < j1 ? rm[j0 + u] : 0;
-      y[u] = j0 + u < j1 ? rl[j0 + u] : 0;
-    }
-    int first = INT_MAX;
-#pragma unroll
-    for (int u = 7; u >= 0; --u)
-      if (x[u] != y[u]) first = j0 + u;
-    if (first != INT_MAX) atomicMin(&h_p[sl], first);
-  }
-  __syncthreads();
-
-  // 3. Tiles and units of each group (two hash slots per thread), numbered by prefix sums.
-  int nt[2], nu[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int s = 2 * tid + k;
-    const int cnt = h_cnt[s], p = h_p[s];
-    const bool ok = cnt >= 2 && p >= 2;
-    nt[k] = ok ? (cnt + S - 1) / S : 0;
-    nu[k] = ok ? nt[k] * a.num_kv_heads * prefix_parts(p) : 0;
-  }
-  int T, U;
-  const int tb = plan_scan(nt[0] + nt[1], s_scan, T);
-  const int ub = plan_scan(nu[0] + nu[1], s_scan, U);
-  h_key[2 * tid] = tb;                              // h_key now holds each slot's first tile
-  h_key[2 * tid + 1] = tb + nt[0];
-  h_ub[2 * tid] = ub;
-  h_ub[2 * tid + 1] = ub + nu[0];
-  __syncthreads();
-  const bool fits = T <= a.plan_tiles;              // always, by the tile bound; else no sharing
-
-  // 4. Members: column in their tile; shared blocks to skip.
-  if (b < B) {
-    int sk = 0;
-    if (fits && slot >= 0 && h_cnt[slot] >= 2 && h_p[slot] >= 2) {
-      const int r = s_rank[b];
-      plan[pl.mem + (size_t)(h_key[slot] + r / S) * 16 + r % S] = b;
-      sk = h_p[slot];
-    }
-    plan[pl.skip + b] = sk;
-  }
-  // 5. Tiles: table row read, shared length, first unit, unused columns.
-  if (fits) {
-    for (int t = tid; t < T; t += kPlanThreads) {
-      int lo = 0, hi = HS - 1;                      // last slot whose first tile is <= t
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (h_key[mid] <= t) lo = mid; else hi = mid - 1;
-      }
-      const int s = lo, i = t - h_key[s], p = h_p[s];
-      plan[pl.lead + t] = h_lead[s];
-      plan[pl.p + t] = p;
-      plan[pl.ubase + t] = h_ub[s] + i * a.num_kv_heads * prefix_parts(p);
-      for (int r = min(S, h_cnt[s] - i * S); r < 16; ++r) plan[pl.mem + (size_t)t * 16 + r] = -1;
-    }
-  }
-  if (tid == 0) {
-    plan[0] = fits ? T : 0;
-    plan[1] = fits ? U : 0;
-    plan[pl.ubase + (fits ? T : 0)] = fits ? U : 0;
-  }
-}
-
-// One workgroup per unit: the shared blocks [16k, min(p, 16k + 16)) of one KV head, read once
-// for all members of a tile (column r*group + g = query head g of member r).  The waves
-// take the unit's 32-token steps in turn and merge in LDS; the unnormalised result and its
-// (max, exp-sum) are left for decode_kernel as part k of each member's query rows.
 template <int D, int QT, int KVT>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeArgs a) {
   typedef Stepper<D, QT, KVT, false> St;
@@ -972,46 +839,213 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
   constexpr int NC = St::NC;
   constexpr int NT = St::NT;
   constexpr int TPW = (NT + kWaves - 1) / kWaves;   // tiles w, w + kWaves, ... of wave w
-  constexpr int kMaxTiles = 2 * kPlanMaxBatch / 3;
+  constexpr int NTH = 64 * kWaves;
+  constexpr int HS = 2048;                          // hash slots: at least twice the batch
+  constexpr int PER = kPlanMaxBatch / NTH;          // sequences per thread
+  constexpr int SPT = HS / NTH;                     // hash slots per thread
+  static_assert(HS >= 2 * kPlanMaxBatch && kPlanMaxBatch % NTH == 0 && HS % NTH == 0, "plan");
 
-  __shared__ int sm_ub[kMaxTiles + 1], sm_lead[kMaxTiles], sm_p[kMaxTiles];
-  __shared__ int sm_tu[2];
+  __shared__ int h_key[HS], h_lead[HS], h_cnt[HS], h_p[HS];
+  __shared__ int h_mbase[HS];                       // per slot: the group's first member
+  __shared__ int s_full[kPlanMaxBatch], s_slot[kPlanMaxBatch];
+  __shared__ int s_off[kPlanMaxBatch], s_mslot[kPlanMaxBatch], s_mseq[kPlanMaxBatch];
+  __shared__ int s_mlist[kPlanMaxBatch];            // members, group by group, in sequence order
+  __shared__ int s_ubase[kPlanMaxBatch];            // per leader: the group's first unit
+  __shared__ int s_scan[NTH / 64];
   __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
   __shared__ f32x4 sm_acc[kWaves][NT][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int Hq = a.num_q_heads, G = a.group, S = 16 / G;
-  const int* plan = a.ws_plan;
-  const PlanLayout pl(a.batch, a.plan_tiles);
-  // the plan's tile arrays, read whole in one round (entries past the tile count are unused)
-  if (tid < 2) sm_tu[tid] = plan[tid];
-  for (int t = tid; t <= a.plan_tiles; t += blockDim.x) {
-    sm_ub[t] = plan[pl.ubase + t];
-    if (t < a.plan_tiles) {
-      sm_lead[t] = plan[pl.lead + t];
-      sm_p[t] = plan[pl.p + t];
+  const int B = a.batch, MB = a.max_blocks_per_seq, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int G = a.group, S = 16 / G;
+
+  // ---- 1. Candidates: two or more whole blocks before the one with the last token, hashed by
+  // their first physical block.  A group's leader is its smallest sequence index.
+#pragma unroll
+  for (int x = 0; x < SPT; ++x) {
+    h_key[tid * SPT + x] = -1;
+    h_lead[tid * SPT + x] = INT_MAX;
+    h_cnt[tid * SPT + x] = 0;
+    h_p[tid * SPT + x] = INT_MAX;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = tid * PER + q;
+    int slot = -1, full = 0;
+    if (b < B) {
+      const int L = clamp_len(a.context_lens[b], a.len_cap);
+      const int key = a.block_tables[(size_t)b * MB];
+      full = L > 0 ? min((L - 1) / kBlock, kMaxSharedBlocks) : 0;
+      if (full >= 2 && (unsigned)key < (unsigned)a.num_blocks) {
+        unsigned h = ((unsigned)key * 2654435761u) >> 21;
+        for (;;) {                                  // ends: fewer keys than slots
+          const int prev = atomicCAS(&h_key[h], -1, key);
+          if (prev == -1 || prev == key) break;
+          h = (h + 1) & (HS - 1);
+        }
+        slot = (int)h;
+        atomicMin(&h_lead[slot], b);
+        atomicAdd(&h_cnt[slot], 1);
+      }
+    }
+    s_full[b] = full;
+    s_slot[b] = slot;
+  }
+  __syncthreads();
+
+  // ---- 2. Shared length of a group: the first table entry where a member differs from the
+  // leader, at most the shorter of their whole-block counts.  A wave compares 8 members at a
+  // time, 64 consecutive entries of each row per round (one coalesced load per row), and stops
+  // at a member's first difference.
+  int cmpb[PER], csum = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = tid * PER + q, slot = s_slot[b];
+    cmpb[q] = 0;
+    if (slot >= 0 && h_cnt[slot] >= 2) {
+      const int lead = h_lead[slot];
+      const int cmp = min(s_full[b], s_full[lead]);
+      atomicMin(&h_p[slot], cmp);
+      if (b != lead && cmp > 1) cmpb[q] = cmp;
+    }
+    csum += cmpb[q] > 0;
+  }
+  int ncmp;
+  {
+    int pos = block_scan<NTH>(csum, s_scan, ncmp);
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (cmpb[q] > 0) {
+        s_off[pos] = tid * PER + q;                 // members to compare, in sequence order
+        s_mseq[pos] = cmpb[q];                      // and their comparison lengths
+        ++pos;
+      }
+  }
+  __syncthreads();
+  for (int k0 = wave * 8; k0 < ncmp; k0 += kWaves * 8) {
+    int mb[8], len[8], first[8];
+    const int32_t* rm[8];
+    const int32_t* rl[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int k = k0 + v;
+      mb[v] = k < ncmp ? s_off[k] : -1;
+      len[v] = k < ncmp ? s_mseq[k] : 0;
+      first[v] = INT_MAX;
+      const int lead = mb[v] >= 0 ? h_lead[s_slot[mb[v]]] : 0;
+      rm[v] = a.block_tables + (size_t)(mb[v] >= 0 ? mb[v] : 0) * MB;
+      rl[v] = a.block_tables + (size_t)lead * MB;
+    }
+    for (int j0 = 1;; j0 += 64) {
+      const int j = j0 + lane;
+      int x[8], y[8];
+      bool live = false;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const bool act = first[v] == INT_MAX && j0 < len[v];   // wave-uniform
+        x[v] = act && j < len[v] ? rm[v][j] : 0;
+        y[v] = act && j < len[v] ? rl[v][j] : 0;
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const bool act = first[v] == INT_MAX && j0 < len[v];
+        const unsigned long long diff = __ballot(act && x[v] != y[v]);
+        if (diff) first[v] = j0 + __ffsll((long long)diff) - 1;
+        live |= first[v] == INT_MAX && j0 + 64 < len[v];
+      }
+      if (!live) break;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        if (first[v] != INT_MAX) atomicMin(&h_p[s_slot[mb[v]]], first[v]);
     }
   }
   __syncthreads();
-  const int T = sm_tu[0], U = sm_tu[1];
 
+  // ---- 3. Members (of groups of two or more sharing two or more blocks), listed in sequence
+  // order; a member's rank is the number of members of its group before it.
+  int mem[PER], msum = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int slot = s_slot[tid * PER + q];
+    mem[q] = slot >= 0 && h_cnt[slot] >= 2 && h_p[slot] >= 2;
+    msum += mem[q];
+  }
+  int nmem;
+  {
+    int pos = block_scan<NTH>(msum, s_scan, nmem);
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (mem[q]) {
+        s_mslot[pos] = s_slot[tid * PER + q];
+        s_mseq[pos] = tid * PER + q;
+        ++pos;
+      }
+  }
+  // Groups are numbered in the order of their leaders (hash slots may differ between
+  // workgroups; leaders do not): each group's first member and first unit, by prefix sums over
+  // the sequences.
+  int mc[PER], uc[PER], ms = 0, us = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = tid * PER + q, slot = s_slot[b];
+    const bool leader = mem[q] && h_lead[slot] == b;
+    const int cnt = leader ? h_cnt[slot] : 0;
+    mc[q] = cnt;
+    uc[q] = leader ? (cnt + S - 1) / S * Hkv * prefix_parts(h_p[slot]) : 0;
+    ms += mc[q];
+    us += uc[q];
+  }
+  int U;
+  {
+    int mb = block_scan<NTH>(ms, s_scan, nmem);
+    int ub = block_scan<NTH>(us, s_scan, U);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int b = tid * PER + q;
+      if (mc[q] > 0) h_mbase[s_slot[b]] = mb;
+      s_ubase[b] = ub;
+      mb += mc[q];
+      ub += uc[q];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nmem; i += NTH) {
+    const int slot = s_mslot[i];
+    int rank = 0;
+    for (int j = 0; j < i; ++j) rank += s_mslot[j] == slot;
+    s_mlist[h_mbase[slot] + rank] = s_mseq[i];
+  }
+  if (blockIdx.x == 0) {                            // shared blocks each sequence skips
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int b = tid * PER + q, slot = s_slot[b];
+      if (b < B) a.ws_skip[b] = mem[q] ? h_p[slot] : 0;
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. The units.
   const St st(a, lane);
   const int r = col / G, g = col - r * G;
   for (int u = blockIdx.x; u < U; u += gridDim.x) {
-    int lo = 0, hi = T - 1;                         // tile of unit u
+    int lo = 0, hi = kPlanMaxBatch - 1;             // the leader whose group's units contain u
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (sm_ub[mid] <= u) lo = mid; else hi = mid - 1;
+      if (s_ubase[mid] <= u) lo = mid; else hi = mid - 1;
     }
-    const int t = lo;
-    const int lead = sm_lead[t], p = sm_p[t];
+    const int s = s_slot[lo], p = h_p[s], lead = lo, cnt = h_cnt[s];
     const int ks = prefix_parts(p);
-    const int rem = u - sm_ub[t];
+    const int uu = u - s_ubase[lo];
+    const int tile = uu / (Hkv * ks), rem = uu - tile * (Hkv * ks);
     const int kvh = rem / ks, k = rem - kvh * ks;
     const int j0 = k * kUnitBlocks, j1 = min(p, j0 + kUnitBlocks);
-    const int member = r < S ? plan[pl.mem + (size_t)t * 16 + r] : -1;
+    const int mi = tile * S + r;                    // this column's member within the group
+    const int member = r < S && mi < cnt ? s_mlist[h_mbase[s] + mi] : -1;
     const size_t row = (size_t)member * Hq + kvh * G + g;
 
     V8 qB[NC];
@@ -1020,8 +1054,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
     f32x4 acc[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    st.run(qB, a.block_tables + (size_t)lead * a.max_blocks_per_seq, kvh, j0, j1, kBlock * j1,
-           wave, kWaves, m_run, l_run, acc);
+    st.run(qB, a.block_tables + (size_t)lead * MB, kvh, j0, j1, kBlock * j1, wave, kWaves, m_run,
+           l_run, acc);
     l_run = sum_across_rows(l_run);
 
     if (grp == 0) {
@@ -1063,13 +1097,10 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
 
 template <int D, int QT, int KVT>
 static hipError_t launch_t(const DecodeArgs& a, int prefix_wgs, hipStream_t stream) {
-  if (a.ws_plan) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (a.ws_skip) {
     hipLaunchKernelGGL((prefix_kernel<D, QT, KVT>), dim3(prefix_wgs), dim3(64 * kWaves), 0,
                        stream, a);
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((decode_kernel<D, QT, KVT>), dim3(a.total_waves / kWaves), dim3(64 * kWaves),

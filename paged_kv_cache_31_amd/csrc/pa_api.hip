@@ -221,10 +221,9 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   a.ws_cnt = reinterpret_cast<int*>(ws);
   a.ws_acc = reinterpret_cast<float*>(ws + lay.acc);
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
-  a.ws_plan = share ? reinterpret_cast<int*>(ws + lay.plan) : nullptr;
+  a.ws_skip = share ? reinterpret_cast<int*>(ws + lay.plan) : nullptr;
   a.gp_acc = share ? reinterpret_cast<float*>(ws + lay.gp_acc) : nullptr;
   a.gp_ml = share ? reinterpret_cast<float*>(ws + lay.gp_ml) : nullptr;
-  a.plan_tiles = pa::plan_tiles_of(desc->batch);
   a.prefix_parts = share ? pa::prefix_parts_of(desc->max_blocks_per_seq) : 0;
   a.batch = desc->batch;
   a.num_q_heads = desc->num_q_heads;
@@ -240,7 +239,8 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   // prefix workgroups: one per resident slot, never more than the plan can have units
   int64_t prefix_wgs = 0;
   if (share) {
-    const int64_t units = (int64_t)a.plan_tiles * a.num_kv_heads * a.prefix_parts;
+    const int64_t units =
+        (int64_t)pa::plan_tiles_of(desc->batch) * a.num_kv_heads * a.prefix_parts;
     prefix_wgs = resident_waves(desc) / pa::kWaves;
     if (prefix_wgs < 1) prefix_wgs = 1;
     if (prefix_wgs > units) prefix_wgs = units;

@@ -39,10 +39,9 @@ struct DecodeArgs {
   float* ws_acc;        // [workgroups][2][group][head_dim]: unnormalised output of a cut group
   float* ws_ml;         // [workgroups][2][group][2]: running max (log2 units), exp-sum
   // Shared-prefix plan and prefix partial results (all null when shared prefixes are off).
-  int* ws_plan;         // PlanLayout(batch, plan_tiles): see below
+  int* ws_skip;         // [batch]: leading blocks of each sequence the prefix kernel covers
   float* gp_acc;        // [batch * num_q_heads][prefix_parts][head_dim]: unnormalised output
   float* gp_ml;         // [batch * num_q_heads][prefix_parts][2]: running max (log2), exp-sum
-  int plan_tiles;       // tile capacity of the plan
   int prefix_parts;     // partial results per query row: ceil(min(table width, 256) / 16)
   int batch;
   int num_q_heads;
@@ -56,30 +55,14 @@ struct DecodeArgs {
   float qk_scale_log2;  // scale * log2(e)
 };
 
-// Shared prefixes.  A plan groups sequences whose block tables start with the same physical
-// blocks; each group is cut into tiles of up to 16/group members (one MFMA column per query head
-// of a member), and a tile's shared blocks are read in units of kUnitBlocks blocks per KV head.
-constexpr int kPlanMaxBatch = 1024;   // plans are made for batches up to this size
-constexpr int kUnitBlocks = 16;       // shared blocks one prefix workgroup reads per unit
+// Shared prefixes.  Sequences whose block tables start with the same physical blocks are
+// grouped; each group is cut into tiles of up to 16/group members (one MFMA column per query
+// head of a member), and a tile's shared blocks are read in units of kUnitBlocks blocks per KV
+// head.
+constexpr int kPlanMaxBatch = 1024;   // groups are formed for batches up to this size
+constexpr int kUnitBlocks = 32;       // shared blocks one prefix workgroup reads per unit
 constexpr int kMaxSharedBlocks = 256; // longest shared prefix taken (blocks)
-constexpr int kPlanThreads = 1024;
 
-// Integer plan, offsets in ints: header [tiles, units, 0, 0], then skip[batch] (shared blocks
-// of each sequence, 0 if none), tile_lead[T] (table row read for the tile), tile_p[T] (shared
-// blocks), unit_base[T + 1] (first unit of each tile; the last entry is the unit count) and
-// tile_mem[T][16] (member sequences, -1 padded).
-constexpr int kPlanHeader = 4;
-struct PlanLayout {
-  long skip, lead, p, ubase, mem, total;
-  __host__ __device__ PlanLayout(long batch, long tiles) {
-    skip = kPlanHeader;
-    lead = skip + batch;
-    p = lead + tiles;
-    ubase = p + tiles;
-    mem = ubase + tiles + 1;
-    total = mem + 16 * tiles;
-  }
-};
 // Groups have at least two members and tiles at least two columns of members, so a batch of n
 // sequences makes at most floor(2n/3) tiles (groups of three, two tiles each, are the worst case).
 inline int plan_tiles_of(int batch) { return 2 * batch / 3 > 0 ? 2 * batch / 3 : 1; }
@@ -90,8 +73,8 @@ inline int prefix_parts_of(int max_blocks_per_seq) {
 
 // Workspace: a fixed region of arrival counters (so that their place never depends on the
 // descriptor and a workspace zero-filled once stays valid for every call), then two published
-// partial results per workgroup; with shared prefixes, the plan and the prefix partial results
-// follow.  Each part is 256-byte aligned.
+// partial results per workgroup; with shared prefixes, each sequence's skipped block count and
+// the prefix partial results follow.  Each part is 256-byte aligned.
 constexpr long kMaxWorkgroups = 65536;
 struct WorkspaceLayout {
   size_t acc, ml, plan, gp_acc, gp_ml, total;
@@ -106,7 +89,7 @@ inline WorkspaceLayout workspace_layout(int group, int head_dim, long workgroups
   w.gp_acc = w.gp_ml = w.total = w.plan;
   if (prefix_parts > 0) {
     const size_t rows = (size_t)batch * num_q_heads * prefix_parts;
-    w.gp_acc = w.plan + align256(PlanLayout(batch, plan_tiles_of(batch)).total * sizeof(int));
+    w.gp_acc = w.plan + align256((size_t)batch * sizeof(int));
     w.gp_ml = w.gp_acc + align256(rows * head_dim * sizeof(float));
     w.total = w.gp_ml + align256(rows * 2 * sizeof(float));
   }
@@ -117,8 +100,7 @@ inline WorkspaceLayout workspace_layout(int group, int head_dim, long workgroups
 constexpr long kMaxWaves = 8192;
 
 hipError_t launch_append(const AppendArgs& a, int num_tokens, int elem_bytes, hipStream_t stream);
-// Enqueues the decode; with a.ws_plan set, the plan and prefix kernels run first (prefix_wgs
-// workgroups for the latter).
+// Enqueues the decode; with a.ws_skip set, the prefix kernel runs first (prefix_wgs workgroups).
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
                          int prefix_wgs, hipStream_t stream);
 // Resident decode workgroups per CU for this kernel instance (0 if the query fails).

@@ -132,15 +132,14 @@ def test_append_rejects():
 
 
 def test_workspace_with_shared_prefixes():
-    """Shared prefixes add the plan and the prefix partial results when they are taken (group
-    <= 8, batch <= 1024) and nothing otherwise."""
+    """Shared prefixes add per-sequence skip counts and the prefix partial results when they are
+    taken (group <= 8, batch <= 1024) and nothing otherwise."""
     d = _desc(max_context_len=100)
     base = pa.pa_decode_workspace_size(d)
     s = _desc(max_context_len=100, shared_prefixes=1)
     B, Hq, D, MB = 4, 8, 64, 7
-    T = max(1, 2 * B // 3)
-    P = -(-min(MB, 256) // 16)
-    plan = _r((5 + B + 19 * T) * 4)
+    P = -(-min(MB, 256) // 32)
+    plan = _r(B * 4)
     parts = _r(B * Hq * P * D * 4) + _r(B * Hq * P * 2 * 4)
     assert pa.pa_decode_workspace_size(s) == base + plan + parts
     # group 16 and batches over 1024 run without a plan
