@@ -67,24 +67,23 @@ def cpu_baseline(wl, decode_bytes_fn, append_bytes, min_s: float = 10.0,
 
 
 def traffic_record(workload: str):
-    """HBM bytes per decode launch measured with rocprofv3 PMC counters (profiles/), reported
+    """HBM bytes per decode call measured with rocprofv3 PMC counters (profiles/), reported
     only while the kernel sources still hash to what they were when the counters were taken."""
+    import glob
     import hashlib
     import re
 
-    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}.md")
-    if not os.path.exists(path):
-        return None
-    m = re.search(r"<!-- traffic-record (\{.*?\}) -->", open(path).read())
-    if not m:
-        return None
-    rec = json.loads(m.group(1))
     h = hashlib.sha256()
     for f in ("decode.hip", "device_common.hpp", "pa_internal.hpp"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_31_amd", "csrc", f), "rb").read())
-    if h.hexdigest() != rec.get("kernel_source_sha256"):
-        return None
-    return rec.get("traffic_bytes_per_launch")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
+        m = re.search(r"<!-- traffic-record (\{.*?\}) -->", open(path).read())
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("workload") == workload and h.hexdigest() == rec.get("kernel_source_sha256"):
+            return rec.get("traffic_bytes_per_launch")
+    return None
 
 
 def copy_probe(dev) -> int:
@@ -223,8 +222,8 @@ def main() -> int:
 
     achieved = bytes_decode / launch_s / 1e9
     value = (bytes_decode + bytes_append) / (ms_per_step / 1e3) / 1e9
-    # the decode call is one kernel, or the plan, prefix and decode kernels with shared prefixes
-    kernel = "plan_kernel+prefix_kernel+decode_kernel" if share else "decode_kernel"
+    # the decode call is one kernel, or the prefix and decode kernels with shared prefixes
+    kernel = "prefix_kernel+decode_kernel" if share else "decode_kernel"
     lens_np = wl.context_lens
     result = {
         "metric": METRIC,
