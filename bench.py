@@ -110,6 +110,8 @@ def main() -> int:
     ap.add_argument("--partition", type=int, default=None,
                     help="key-partition tokens (default: the workload's, else the library's)")
     ap.add_argument("--rotations", type=int, default=0, help="pool copies cycled (0: auto)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="time a step as pa_kv_append + pa_decode instead of pa_decode_append")
     ap.add_argument("--no-shared-prefixes", action="store_true",
                     help="decode a workload with a shared prefix without the prefix plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,15 +186,26 @@ def main() -> int:
     scale = float(wl.scale)
     mcl = wl.max_context_len
 
-    appends = [pa.AppendCall(x["k_new"], x["v_new"], slots, x["k"], x["v"]) for x in rots]
     decodes = [pa.DecodeCall(x["q"], x["k"], x["v"], tables, lens, scale, x["out"],
                              k_scale=k_scale, v_scale=v_scale, max_context_len=mcl,
                              partition_tokens=P, workspace=workspace, shared_prefixes=share)
                for x in rots]
+    if args.separate_append:
+        appends = [pa.AppendCall(x["k_new"], x["v_new"], slots, x["k"], x["v"]) for x in rots]
 
-    def step(r):
-        appends[r]()
-        decodes[r]()
+        def step(r):
+            appends[r]()
+            decodes[r]()
+    else:
+        # the whole step in one launch: the append of token L-1 fused into the decode
+        fused = [pa.DecodeCall(x["q"], x["k"], x["v"], tables, lens, scale, x["out"],
+                               k_scale=k_scale, v_scale=v_scale, max_context_len=mcl,
+                               partition_tokens=P, workspace=workspace, shared_prefixes=share,
+                               k_new=x["k_new"], v_new=x["v_new"])
+                 for x in rots]
+
+        def step(r):
+            fused[r]()
 
     for i in range(args.warmup):
         step(i % R)
@@ -245,7 +258,8 @@ def main() -> int:
             "context_tokens": int(lens_np.sum()), "unique_tokens": int(wl.unique_tokens),
             "num_blocks": wl.num_blocks, "partition_tokens": P or "balanced", "rotations": R,
             "shared_prefixes": share,
-            "step": "pa_kv_append (1 token per sequence) + pa_decode",
+            "step": ("pa_kv_append (1 token per sequence) + pa_decode" if args.separate_append
+                     else "pa_decode_append (append of 1 token per sequence fused into the decode)"),
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "decode_tokens_per_s": round(B / launch_s, 1),

@@ -150,6 +150,31 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
                     const int32_t* block_tables, const int32_t* context_lens, float scale,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_append -- one whole decode step in one launch: for every sequence b with
+ * L_b = context_lens[b] > 0 (clamped as in pa_decode), store the new token's K/V row into
+ * token L_b - 1 of the sequence (offset (L_b-1) % 16 of physical block
+ * block_tables[b][(L_b-1) / 16], for every KV head), then compute pa_decode over the L_b tokens.
+ * It is pa_kv_append with that slot for each sequence followed by pa_decode (each generation
+ * step appends the new token's K/V before attending: Scaling Book note, "Transformer 推論の基礎:
+ * Prefill と Generation"; youngju.dev guide, KV-cache module), without the second launch and its
+ * gap (design.babushkai.com "GPU推論の内部構造": the per-launch cost of decode steps).
+ *
+ *   k_new, v_new  [batch][num_kv_heads][head_dim] of kv_dtype, 16-byte aligned (fp8: codes
+ *                 already quantised with the scale of their block; copied unchanged)
+ *   other arguments as pa_decode; k_cache and v_cache are updated in place.
+ *
+ * The block that receives a sequence's new token must not be read by another sequence of the
+ * same call (a block that is appended to is owned by one sequence; shared blocks are copied
+ * before they are written).  A block id outside the pool skips that store.  Output equals
+ * pa_kv_append + pa_decode bit for bit.
+ */
+pa_status pa_decode_append(const pa_decode_desc* desc, const void* q, const void* k_new,
+                           const void* v_new, void* k_cache, void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace pa_decode needs for this descriptor, or 0 if the descriptor is invalid
  * (pa_decode reports why).  It depends only on the descriptor, not on the GPU:
  * 262144 + workgroups * 2 * group * (head_dim + 2) * 4 bytes (each part rounded up to 256),

@@ -52,8 +52,8 @@ class PaError(RuntimeError):
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ("pa_kv_append", "pa_decode", "pa_decode_workspace_size", "pa_status_string",
-           "pa_last_hip_error")
+EXPORTS = ("pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_workspace_size",
+           "pa_status_string", "pa_last_hip_error")
 
 
 def lib() -> ctypes.CDLL:
@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
             L.pa_decode.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp, sz, vp]
             L.pa_decode.restype = i32
+            L.pa_decode_append.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
+            L.pa_decode_append.restype = i32
             L.pa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc)]
             L.pa_decode_workspace_size.restype = sz
             L.pa_status_string.argtypes = [i32]
@@ -172,11 +175,12 @@ def _workspace(nbytes: int, device, stream_handle: int):
 
 
 class DecodeCall:
-    """pa_decode with its arguments marshalled once; calling it only enqueues the kernel."""
+    """pa_decode (or, with k_new/v_new, pa_decode_append) with its arguments marshalled once;
+    calling it only enqueues the kernels."""
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
                  v_scale=None, max_context_len=0, partition_tokens=0, workspace=None,
-                 stream=None, shared_prefixes=False):
+                 stream=None, shared_prefixes=False, k_new=None, v_new=None):
         for t in (q, k_cache, v_cache, block_tables, context_lens, out):
             assert t.is_cuda and t.is_contiguous()
         assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
@@ -184,6 +188,12 @@ class DecodeCall:
         NB, Hkv, bs, D = k_cache.shape
         assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
         assert q.shape[2] == D and context_lens.shape[0] == q.shape[0] == block_tables.shape[0]
+        fused = k_new is not None
+        if fused:
+            B = q.shape[0]
+            for t in (k_new, v_new):
+                assert t.is_contiguous() and tuple(t.shape) == (B, Hkv, D)
+                assert t.element_size() == k_cache.element_size()
         self._desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens,
                                  shared_prefixes)
         need = pa_decode_workspace_size(self._desc)
@@ -192,16 +202,21 @@ class DecodeCall:
             workspace = _workspace(need, q.device, st.value or 0)
         wbytes = workspace.numel() * workspace.element_size()
         self._keep = (q, k_cache, v_cache, block_tables, context_lens, out, k_scale, v_scale,
-                      workspace)
-        self._fn = lib().pa_decode
-        self._args = (ctypes.byref(self._desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                      _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
-                      ctypes.c_float(scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(wbytes), st)
+                      workspace, k_new, v_new)
+        tail = (_ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+                ctypes.c_float(scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(wbytes), st)
+        if fused:
+            self._name, self._fn = "pa_decode_append", lib().pa_decode_append
+            self._args = (ctypes.byref(self._desc), _ptr(q), _ptr(k_new), _ptr(v_new),
+                          _ptr(k_cache), _ptr(v_cache)) + tail
+        else:
+            self._name, self._fn = "pa_decode", lib().pa_decode
+            self._args = (ctypes.byref(self._desc), _ptr(q), _ptr(k_cache), _ptr(v_cache)) + tail
 
     def __call__(self) -> None:
         st = self._fn(*self._args)
         if st != PA_OK:
-            _check("pa_decode", st)
+            _check(self._name, st)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
@@ -213,4 +228,15 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_sca
     sequences (see pa_decode_desc.shared_prefixes)."""
     DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                max_context_len, partition_tokens, workspace, stream, shared_prefixes)()
+    return out
+
+
+def pa_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                     k_scale=None, v_scale=None, max_context_len=0, partition_tokens=0,
+                     workspace=None, stream=None, shared_prefixes=False) -> torch.Tensor:
+    """Store k_new/v_new [B][Hkv][D] as token context_lens[b]-1 of every sequence, then decode
+    (pa_kv_append + pa_decode in one launch); returns out."""
+    DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
+               max_context_len, partition_tokens, workspace, stream, shared_prefixes, k_new,
+               v_new)()
     return out

@@ -176,9 +176,14 @@ struct Stepper {
   // Online-softmax attention over logical blocks [j0, j1) of table row trow for KV head kvh
   // (tokens at or past end_tok are masked), taking the steps s_first, s_first + stride, ... of
   // the range, into the running (m_run, l_run, acc).
+  // wait_stores: this wave's earlier stores write a block the run reads in its last step.  The
+  // loads of a run's third and later steps are issued after the first step's wait on the memory
+  // counter, which in-order completion makes cover those older stores; a run of one or two
+  // steps waits for them explicitly before its first load.
   __device__ __forceinline__ void run(const V8 (&qB)[NC], const int32_t* trow, int kvh, int j0,
                                       int j1, int end_tok, int s_first, int stride,
-                                      float& m_run, float& l_run, f32x4 (&acc)[NT]) const {
+                                      float& m_run, float& l_run, f32x4 (&acc)[NT],
+                                      bool wait_stores = false) const {
     const int nsteps = (j1 - j0 + 1) >> 1;
     if (s_first >= nsteps) return;
 
@@ -195,6 +200,7 @@ struct Stepper {
     };
     int nid0, nid1;
     ids_of(s_first, nid0, nid1);
+    if (wait_stores && nsteps - s_first <= 2 * stride) wait_memory_ops();
 
     auto issue = [&](StepRegs<D, FP8>& r, int s) {
       const int pb0 = nid0, pb1 = nid1;
@@ -365,6 +371,30 @@ __device__ __forceinline__ void fold_prefix(const DecodeArgs& a, size_t row, int
           *reinterpret_cast<const f32x4*>(a.gp_acc + part * D + 16 * (t0 + tstride * t) + 4 * grp);
       acc[t] = p * x + acc[t] * y;
     }
+  }
+}
+
+// Stores the new token of sequence b, KV head kvh (k_new/v_new [B][Hkv][D]) into offset off of
+// physical block blk, one wave: the K row is contiguous, the V elements are strided (dim-major
+// tile).  A block id outside the pool skips the store, as pa_kv_append skips such a slot.
+template <int D, int KVT>
+__device__ __forceinline__ void append_token(const DecodeArgs& a, int b, int kvh, int blk, int off,
+                                             int lane) {
+  constexpr int EB = KVT == DT_FP8 ? 1 : 2;
+  if ((unsigned)blk >= (unsigned)a.num_blocks) return;
+  const size_t row = ((size_t)b * a.num_kv_heads + kvh) * D * EB;
+  const size_t tile = ((size_t)blk * a.num_kv_heads + kvh) * kBlock * D * EB;
+  uint8_t* kc = reinterpret_cast<uint8_t*>(const_cast<void*>(a.k_cache));
+  uint8_t* vc = reinterpret_cast<uint8_t*>(const_cast<void*>(a.v_cache));
+  if (lane < D * EB / 16)
+    *reinterpret_cast<uint4*>(kc + tile + (size_t)off * D * EB + 16 * lane) =
+        *reinterpret_cast<const uint4*>(a.k_new + row + 16 * lane);
+  for (int d = lane; d < D; d += 64) {
+    if constexpr (EB == 2)
+      *reinterpret_cast<uint16_t*>(vc + tile + ((size_t)d * kBlock + off) * 2) =
+          *reinterpret_cast<const uint16_t*>(a.v_new + row + 2 * d);
+    else
+      vc[tile + (size_t)d * kBlock + off] = a.v_new[row + d];
   }
 }
 
@@ -626,6 +656,13 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
     const int end_tok = j1 == nblk ? L : kBlock * j1;   // tokens at or past end_tok are masked
     const int h0 = kvh * G;
 
+    const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+
+    // Fused append: the piece that holds the sequence head's last block (no other wave reads
+    // it in this launch) first stores the new token L-1 of this KV head into its slot.
+    const bool append = a.k_new != nullptr && j1 == nblk;
+    if (append) append_token<D, KVT>(a, b, kvh, trow[(L - 1) / kBlock], (L - 1) % kBlock, lane);
+
     V8 qB[NC];
     st.load_q(qB, col < G ? reinterpret_cast<const E*>(a.q) + ((size_t)b * Hq + h0 + col) * D
                           : nullptr);
@@ -633,8 +670,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
     f32x4 acc[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    st.run(qB, a.block_tables + (size_t)b * a.max_blocks_per_seq, kvh, j0, j1, end_tok, 0, 1,
-           m_run, l_run, acc);
+    st.run(qB, trow, kvh, j0, j1, end_tok, 0, 1, m_run, l_run, acc, append);
 
     // ---- finish the piece: whole sequence head -> output; cut piece -> LDS slot
     l_run = sum_across_rows(l_run);

@@ -178,11 +178,14 @@ PA_EXPORT size_t pa_decode_workspace_size(const pa_decode_desc* desc) {
   return workspace_bytes_of(desc);
 }
 
-PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cache,
-                              const void* v_cache, const float* k_scale, const float* v_scale,
-                              const int32_t* block_tables, const int32_t* context_lens,
-                              float scale, void* out, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+namespace {
+
+// pa_decode, and with k_new/v_new set, pa_decode_append.
+pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_new,
+                      const void* v_new, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   pa_status s = check_decode_desc(desc);
   if (s != PA_OK) return s;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
@@ -217,6 +220,8 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
   a.v_scale = v_scale;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
   a.out = out;
   a.ws_cnt = reinterpret_cast<int*>(ws);
   a.ws_acc = reinterpret_cast<float*>(ws + lay.acc);
@@ -252,4 +257,26 @@ PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const v
     return PA_ERR_HIP;
   }
   return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cache,
+                              const void* v_cache, const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return decode_impl(desc, q, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
+                     block_tables, context_lens, scale, out, workspace, workspace_bytes, stream);
+}
+
+PA_EXPORT pa_status pa_decode_append(const pa_decode_desc* desc, const void* q,
+                                     const void* k_new, const void* v_new, void* k_cache,
+                                     void* v_cache, const float* k_scale, const float* v_scale,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     float scale, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return PA_ERR_INVALID_ARG;
+  return decode_impl(desc, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     context_lens, scale, out, workspace, workspace_bytes, stream);
 }

@@ -34,6 +34,8 @@ struct DecodeArgs {
   const float* v_scale;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const uint8_t* k_new;   // fused append: [batch][num_kv_heads][head_dim] (null: decode only)
+  const uint8_t* v_new;
   void* out;
   int* ws_cnt;          // [kMaxWorkgroups] arrival counters, zero between calls
   float* ws_acc;        // [workgroups][2][group][head_dim]: unnormalised output of a cut group

@@ -149,3 +149,15 @@ def test_workspace_with_shared_prefixes():
     big = dict(batch=1025, num_blocks=1 << 16)
     assert (pa.pa_decode_workspace_size(_desc(shared_prefixes=1, **big))
             == pa.pa_decode_workspace_size(_desc(**big)))
+
+
+def test_decode_append_rejects_missing_rows():
+    d = _desc()
+    lib = pa.lib()
+    args = lambda kn, vn: (ctypes.byref(d), FAKE, kn, vn, FAKE, FAKE, None, None, FAKE, FAKE,
+                           0.125, FAKE, None, 0, None)
+    assert lib.pa_decode_append(*args(None, FAKE)) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_append(*args(FAKE, None)) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_append(*args(ctypes.c_void_p(0x10008), FAKE)) == pa.PA_ERR_INVALID_ARG
+    # otherwise validated as pa_decode: no workspace
+    assert lib.pa_decode_append(*args(FAKE, FAKE)) == pa.PA_ERR_WORKSPACE
