@@ -45,6 +45,30 @@ def e4m3fn_to_f64(bits: np.ndarray) -> np.ndarray:
     return E4M3FN_TABLE[np.asarray(bits, dtype=np.uint8)]
 
 
+_E4M3FN_CODE_OF = {float(E4M3FN_TABLE[c]): c for c in range(0x7F)}   # finite, non-negative
+
+
+def e4m3fn_encode(y: np.ndarray) -> np.ndarray:
+    """Round values to OCP e4m3fn codes: saturate to +-448 (the largest finite magnitude; the
+    format has no infinities), then round to the nearest representable value, ties to the even
+    mantissa.  NaN gives 0x7F.  The sign of a value that rounds to zero is kept (0x80 = -0).
+
+    The grid spacing in the binade [2**e, 2**(e+1)) is 2**(e-3) (3 mantissa bits); below 2**-6
+    (the smallest normal) the subnormal spacing 2**-9 continues down to zero.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    nan = np.isnan(y)
+    neg = np.signbit(y)
+    a = np.minimum(np.abs(np.where(nan, 0.0, y)), 448.0)
+    _, ex = np.frexp(a)                          # a = f * 2**ex with f in [0.5, 1)
+    e = np.maximum(ex.astype(np.float64) - 1.0, -6.0)
+    q = np.exp2(e - 3.0)
+    r = np.round(a / q) * q                      # numpy rounds halves to even; a / q is exact
+    codes = np.vectorize(lambda v: _E4M3FN_CODE_OF[float(v)], otypes=[np.uint8])(r)
+    codes = np.where(neg, codes | 0x80, codes).astype(np.uint8)
+    return np.where(nan, np.uint8(0x7F), codes).astype(np.uint8)
+
+
 def to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_to_f64(bits)

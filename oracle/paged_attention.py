@@ -37,7 +37,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import to_f64
+from .formats import e4m3fn_encode, to_f64
 
 BLOCK = 16
 
@@ -58,6 +58,53 @@ def kv_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new
         k[blk, :, off, :] = k_new[i]
         v[blk, :, :, off] = v_new[i]
     return k, v
+
+
+SCALE_KEEP = 0          # quantise with the block's stored scale
+SCALE_FIRST_TOKEN = 1   # a token written at offset 0 of its block first sets that block's scale
+
+
+def kv_append_quant(k_cache, v_cache, k_scale, v_scale, k_new, v_new, src_dtype, slot_mapping,
+                    policy):
+    """Append 16-bit K/V rows into an fp8 e4m3fn cache with per-(block, KV head) scales.
+
+    The fp8 KV cache stores value = code * scale (babushkai.com "GPU推論の内部構造", KV-cache and
+    quantisation sections).  The pages do not say how a block's scale is chosen or what happens
+    when later tokens outgrow it; the reading taken here:
+      * policy SCALE_FIRST_TOKEN: every token of this call written at offset 0 of its block
+        first sets that block's scale, per KV head and separately for K and V, to
+        fp32(max |x|) / fp32(448) in fp32 (1 if the maximum is 0; NaN elements are ignored);
+      * then every token is encoded as e4m3fn(clamp(fp32(x) / fp32(scale), +-448)), the division
+        in fp32 and the rounding to nearest even (a token later in a block uses the block's
+        scale as it stands, saturating if it is larger).
+    Tokens are applied in order (a duplicated slot: the last one wins).  Returns new arrays.
+    """
+    k, v = k_cache.copy(), v_cache.copy()
+    ks, vs = k_scale.copy(), v_scale.copy()
+    xk = to_f64(k_new, src_dtype).astype(np.float32)   # exact: 16-bit values fit in fp32
+    xv = to_f64(v_new, src_dtype).astype(np.float32)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+
+    def first_scale(row):
+        with np.errstate(invalid="ignore"):
+            m = np.float32(np.nanmax(np.abs(row))) if not np.all(np.isnan(row)) else np.float32(0)
+        return np.float32(1.0) if m == 0 else np.float32(m / np.float32(448.0))
+
+    if policy == SCALE_FIRST_TOKEN:
+        for i, s in enumerate(slots):
+            if s >= 0 and s % BLOCK == 0:
+                blk = int(s) // BLOCK
+                for h in range(k.shape[1]):
+                    ks[blk, h] = first_scale(xk[i, h])
+                    vs[blk, h] = first_scale(xv[i, h])
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        blk, off = divmod(int(s), BLOCK)
+        for h in range(k.shape[1]):
+            k[blk, h, off, :] = e4m3fn_encode(xk[i, h] / ks[blk, h])
+            v[blk, h, :, off] = e4m3fn_encode(xv[i, h] / vs[blk, h])
+    return k, v, ks, vs
 
 
 def gather(k_cache, v_cache, kv_dtype, table_row, length, kvh, k_scale=None, v_scale=None):

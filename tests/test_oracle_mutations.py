@@ -103,3 +103,79 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
 def test_unmutated_pins_pass():
     for pin in PINS:
         pin()
+
+
+# ---- fp8 quantisation: planted mistakes in the encoder and in the quantising append.
+
+import oracle as O  # noqa: E402
+import oracle.formats as F  # noqa: E402
+import test_oracle_quant as Q  # noqa: E402
+
+_orig_encode, _orig_quant = F.e4m3fn_encode, pa.kv_append_quant
+
+
+def _encode_with(rounder):
+    def enc(y):
+        y = np.asarray(y, dtype=np.float64)
+        nan, neg = np.isnan(y), np.signbit(y)
+        a = np.minimum(np.abs(np.where(nan, 0.0, y)), 448.0)
+        _, ex = np.frexp(a)
+        q = np.exp2(np.maximum(ex - 1.0, -6.0) - 3.0)
+        r = rounder(a / q) * q
+        codes = np.vectorize(lambda v: F._E4M3FN_CODE_OF[float(v)], otypes=[np.uint8])(r)
+        codes = np.where(neg, codes | 0x80, codes).astype(np.uint8)
+        return np.where(nan, np.uint8(0x7F), codes).astype(np.uint8)
+    return enc
+
+
+def quant_scale_without_448(k_cache, v_cache, k_scale, v_scale, k_new, v_new, src_dtype, slots,
+                            policy):
+    k, v, ks, vs = _orig_quant(k_cache, v_cache, k_scale, v_scale, k_new, v_new, src_dtype, slots,
+                               policy)
+    if policy == O.SCALE_FIRST_TOKEN:             # mistake: scale = amax (codes then tiny)
+        x = O.to_f64(k_new, src_dtype)
+        for i, s in enumerate(slots):
+            if s >= 0 and s % BLOCK == 0:
+                for h in range(k.shape[1]):
+                    ks[s // BLOCK, h] = np.float32(np.abs(x[i, h]).max() or 1.0)
+                    k[s // BLOCK, h, s % BLOCK] = F.e4m3fn_encode(x[i, h] / ks[s // BLOCK, h])
+    return k, v, ks, vs
+
+
+def quant_v_scale_from_k(k_cache, v_cache, k_scale, v_scale, k_new, v_new, src_dtype, slots,
+                         policy):
+    return _orig_quant(k_cache, v_cache, k_scale, v_scale, k_new, k_new, src_dtype, slots, policy)
+
+
+QUANT_MUTATIONS = {
+    "encode: rounds toward zero": ("encode", _encode_with(np.trunc)),
+    "encode: ties away from zero": ("encode", _encode_with(lambda m: np.floor(m + 0.5))),
+    "quant append: scale is amax, not amax / 448": ("quant", quant_scale_without_448),
+    "quant append: V quantised from K": ("quant", quant_v_scale_from_k),
+}
+
+QUANT_PINS = [
+    Q.test_encode_matches_torch_on_every_bf16_value_in_range,
+    Q.test_encode_matches_torch_on_random_fp32_and_midpoints,
+    Q.test_ties_saturation_and_special_values,
+    Q.test_first_token_sets_the_scale_and_its_largest_element_encodes_to_448,
+    Q.test_keep_policy_uses_the_stored_scale_and_saturates,
+]
+
+
+@pytest.mark.parametrize("name", list(QUANT_MUTATIONS))
+def test_quant_pins_catch_planted_mistake(name, monkeypatch):
+    kind, fn = QUANT_MUTATIONS[name]
+    if kind == "encode":
+        for mod in (F, pa, O):
+            monkeypatch.setattr(mod, "e4m3fn_encode", fn)
+    else:
+        for mod in (pa, O):
+            monkeypatch.setattr(mod, "kv_append_quant", fn)
+    caught = 0
+    for pin in QUANT_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"no pin caught: {name}"
