@@ -111,6 +111,40 @@ pa_status pa_kv_append(const pa_cache_desc* cache, int32_t num_tokens,
                        const void* k_new, const void* v_new, const int64_t* slot_mapping,
                        void* k_cache, void* v_cache, void* stream);
 
+/* Scale policies of pa_kv_append_quant. */
+typedef enum pa_scale_policy {
+  PA_SCALE_KEEP = 0,        /* quantise with the block's stored scale */
+  PA_SCALE_FIRST_TOKEN = 1  /* a token written at offset 0 of its block first sets its scale */
+} pa_scale_policy;
+
+/*
+ * pa_kv_append_quant -- write num_tokens new K/V rows given in 16 bits into an fp8 (e4m3fn)
+ * cache, quantising them with the per-(block, KV head) scales (value = code * scale: the FP8 KV
+ * cache of design.babushkai.com "GPU推論の内部構造", KV-cache and quantisation sections).
+ *
+ *   src_dtype     PA_F16 or PA_BF16: the dtype of k_new, v_new [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping  as pa_kv_append (negative or outside the pool: skipped)
+ *   k_cache, v_cache  fp8 pools (cache->kv_dtype must be PA_FP8_E4M3), updated in place
+ *   k_scale, v_scale  [num_blocks][num_kv_heads] fp32, read, and written under
+ *                 PA_SCALE_FIRST_TOKEN
+ *   scale_policy  PA_SCALE_KEEP: every row uses its block's stored scale.
+ *                 PA_SCALE_FIRST_TOKEN: first, each token of this call at offset 0 of its block
+ *                 sets that block's scale, per KV head and separately for K and V, to
+ *                 fp32(max |x|) / 448 (1 if the maximum is 0; NaN elements are ignored);
+ *                 then all rows are quantised (a token later in a block uses the block's scale
+ *                 as it stands and saturates if it is larger).
+ *
+ * Each element becomes e4m3fn(clamp(fp32(x) / fp32(scale), +-448)): IEEE fp32 division, round to
+ * nearest even, sign kept (0x80 for values that round to zero from below), NaN -> 0x7F.  The
+ * pages leave the scale policy open; this is one plain reading.  Two tokens with the same slot,
+ * or two offset-0 tokens of one block, in one call race (caller error).  Two kernels are
+ * enqueued under PA_SCALE_FIRST_TOKEN, one under PA_SCALE_KEEP.
+ */
+pa_status pa_kv_append_quant(const pa_cache_desc* cache, int32_t num_tokens, int32_t src_dtype,
+                             const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                             int32_t scale_policy, void* stream);
+
 /*
  * pa_decode -- out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b for every sequence b and query
  * head h, where K_b, V_b are the first context_lens[b] tokens of sequence b gathered through

@@ -81,8 +81,9 @@ def kv_append_quant(k_cache, v_cache, k_scale, v_scale, k_new, v_new, src_dtype,
     """
     k, v = k_cache.copy(), v_cache.copy()
     ks, vs = k_scale.copy(), v_scale.copy()
-    xk = to_f64(k_new, src_dtype).astype(np.float32)   # exact: 16-bit values fit in fp32
-    xv = to_f64(v_new, src_dtype).astype(np.float32)
+    with np.errstate(invalid="ignore"):                  # NaN payloads stay NaN
+        xk = to_f64(k_new, src_dtype).astype(np.float32)   # exact: 16-bit values fit in fp32
+        xv = to_f64(v_new, src_dtype).astype(np.float32)
     slots = np.asarray(slot_mapping, dtype=np.int64)
 
     def first_scale(row):
@@ -102,8 +103,9 @@ def kv_append_quant(k_cache, v_cache, k_scale, v_scale, k_new, v_new, src_dtype,
             continue
         blk, off = divmod(int(s), BLOCK)
         for h in range(k.shape[1]):
-            k[blk, h, off, :] = e4m3fn_encode(xk[i, h] / ks[blk, h])
-            v[blk, h, :, off] = e4m3fn_encode(xv[i, h] / vs[blk, h])
+            with np.errstate(over="ignore", invalid="ignore"):   # inf and NaN are encoded too
+                k[blk, h, off, :] = e4m3fn_encode(xk[i, h] / ks[blk, h])
+                v[blk, h, :, off] = e4m3fn_encode(xv[i, h] / vs[blk, h])
     return k, v, ks, vs
 
 

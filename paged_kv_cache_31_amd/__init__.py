@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_SCALE_KEEP, PA_SCALE_FIRST_TOKEN = 0, 1
 BLOCK_SIZE = 16
 
 
@@ -52,8 +53,8 @@ class PaError(RuntimeError):
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ("pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_workspace_size",
-           "pa_status_string", "pa_last_hip_error")
+EXPORTS = ("pa_kv_append", "pa_kv_append_quant", "pa_decode", "pa_decode_append",
+           "pa_decode_workspace_size", "pa_status_string", "pa_last_hip_error")
 
 
 def lib() -> ctypes.CDLL:
@@ -67,6 +68,9 @@ def lib() -> ctypes.CDLL:
             vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
             L.pa_kv_append.argtypes = [ctypes.POINTER(CacheDesc), i32, vp, vp, vp, vp, vp, vp]
             L.pa_kv_append.restype = i32
+            L.pa_kv_append_quant.argtypes = [ctypes.POINTER(CacheDesc), i32, i32, vp, vp, vp, vp,
+                                             vp, vp, vp, i32, vp]
+            L.pa_kv_append_quant.restype = i32
             L.pa_decode.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp, sz, vp]
             L.pa_decode.restype = i32
@@ -144,6 +148,26 @@ class AppendCall:
 def pa_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """Scatter k_new/v_new [T][Hkv][D] into their slots (int64 [T], <0 skips)."""
     AppendCall(k_new, v_new, slot_mapping, k_cache, v_cache, stream)()
+
+
+def pa_kv_append_quant(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                       first_token_scale=False, stream=None) -> None:
+    """Quantise 16-bit k_new/v_new [T][Hkv][D] into the fp8 pools at their slots with the
+    per-(block, KV head) scales; first_token_scale: a token at offset 0 of its block first sets
+    that block's scales (amax / 448)."""
+    for t in (k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale):
+        assert t.is_cuda and t.is_contiguous()
+    assert slot_mapping.dtype == torch.int64 and k_scale.dtype == torch.float32
+    NB, Hkv, bs, D = k_cache.shape
+    assert tuple(v_cache.shape) == (NB, Hkv, D, bs) and tuple(k_scale.shape) == (NB, Hkv)
+    T = slot_mapping.shape[0]
+    assert tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D)
+    st = lib().pa_kv_append_quant(ctypes.byref(cache_desc(k_cache)), T, _dtype_code(k_new, False),
+                                  _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                  PA_SCALE_FIRST_TOKEN if first_token_scale else PA_SCALE_KEEP,
+                                  _stream(stream))
+    _check("pa_kv_append_quant", st)
 
 
 def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_tokens=0,

@@ -39,6 +39,92 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   reinterpret_cast<E*>(a.v_cache)[(tile * D + t) * kBlock + off] = v;
 }
 
+// ---- Quantising append into an fp8 (OCP e4m3fn) cache with per-(block, KV head) scales.
+//
+// The fp8 KV cache stores value = code * scale (design.babushkai.com "GPU推論の内部構造", KV-cache
+// and quantisation sections).  How a block's scale is chosen is not given there; this follows
+// one reading: with the first-token policy, a token written at offset 0 of its block first sets
+// that block's scale to fp32(max |x|) / 448 (1 if the maximum is 0), per KV head and separately
+// for K and V (quant_scale_kernel); then every token is encoded as
+// e4m3fn(clamp(fp32(x) / scale, +-448)) with round-to-nearest-even (quant_append_kernel).  A
+// token later in a block uses the block's scale as it stands and saturates if it is larger.
+
+template <typename S>
+__device__ __forceinline__ float widen(S x) {
+  return (float)x;                                  // exact: 16-bit values fit in fp32
+}
+
+template <typename S>
+__global__ __launch_bounds__(64) void quant_scale_kernel(QuantAppendArgs a) {
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int64_t s = a.slots[i];
+  if (s < 0 || s >= a.num_slots || (s & 15) != 0) return;   // only a block's first token
+  const int H = a.num_kv_heads, D = a.head_dim;
+  const S* kn = reinterpret_cast<const S*>(a.k_new) + ((size_t)i * H + h) * D;
+  const S* vn = reinterpret_cast<const S*>(a.v_new) + ((size_t)i * H + h) * D;
+  // A compare-and-select skips NaN elements of either kind (fmaxf would let a signalling NaN
+  // through as a quiet one), so the running maxima stay numbers.
+  float km = 0.0f, vm = 0.0f;
+  for (int d = lane; d < D; d += 64) {
+    const float xk = fabsf(widen(kn[d])), xv = fabsf(widen(vn[d]));
+    km = xk > km ? xk : km;
+    vm = xv > vm ? xv : vm;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    km = fmaxf(km, __shfl_xor(km, o));
+    vm = fmaxf(vm, __shfl_xor(vm, o));
+  }
+  if (lane == 0) {
+    const size_t at = (size_t)(s >> 4) * H + h;
+    a.k_scale[at] = km == 0.0f ? 1.0f : km / 448.0f;
+    a.v_scale[at] = vm == 0.0f ? 1.0f : vm / 448.0f;
+  }
+}
+
+// e4m3fn code of y: saturate at 448, round to nearest even (the hardware conversion on the
+// magnitude), keep the sign (so -0 and values that round to zero from below give 0x80), NaN 0x7F.
+__device__ __forceinline__ uint8_t e4m3fn_code(float y) {
+  if (y != y) return 0x7F;
+  const float m = fminf(fabsf(y), 448.0f);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(m, m, 0, false) & 0x7Fu;
+  return (uint8_t)(c | (__builtin_signbitf(y) ? 0x80u : 0u));
+}
+
+template <typename S>
+__global__ __launch_bounds__(128) void quant_append_kernel(QuantAppendArgs a) {
+  const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x;   // t < head_dim
+  const int H = a.num_kv_heads, D = a.head_dim;
+  const size_t row = ((size_t)i * H + h) * D;
+  const float xk = widen(reinterpret_cast<const S*>(a.k_new)[row + t]);
+  const float xv = widen(reinterpret_cast<const S*>(a.v_new)[row + t]);
+  const int64_t s = a.slots[i];
+  if (s < 0 || s >= a.num_slots) return;
+  const int off = (int)(s & 15);
+  const size_t tile = (size_t)(s >> 4) * H + h;
+  const uint8_t ck = e4m3fn_code(xk / a.k_scale[tile]);   // IEEE fp32 division
+  const uint8_t cv = e4m3fn_code(xv / a.v_scale[tile]);
+  a.k_cache[(tile * kBlock + off) * D + t] = ck;
+  a.v_cache[(tile * D + t) * kBlock + off] = cv;
+}
+
+hipError_t launch_append_quant(const QuantAppendArgs& a, int num_tokens, bool bf16_src,
+                               bool first_token_scale, hipStream_t stream) {
+  const dim3 grid(num_tokens, a.num_kv_heads);
+  if (first_token_scale) {
+    if (bf16_src)
+      hipLaunchKernelGGL(quant_scale_kernel<__bf16>, grid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(quant_scale_kernel<_Float16>, grid, dim3(64), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (bf16_src)
+    hipLaunchKernelGGL(quant_append_kernel<__bf16>, grid, dim3(a.head_dim), 0, stream, a);
+  else
+    hipLaunchKernelGGL(quant_append_kernel<_Float16>, grid, dim3(a.head_dim), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendArgs& a, int num_tokens, int elem_bytes, hipStream_t stream) {
   const dim3 grid(num_tokens, a.num_kv_heads), block(a.head_dim);
   if (elem_bytes == 2)

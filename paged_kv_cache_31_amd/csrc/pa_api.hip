@@ -173,6 +173,46 @@ PA_EXPORT pa_status pa_kv_append(const pa_cache_desc* cache, int32_t num_tokens,
   return PA_OK;
 }
 
+PA_EXPORT pa_status pa_kv_append_quant(const pa_cache_desc* cache, int32_t num_tokens,
+                                       int32_t src_dtype, const void* k_new, const void* v_new,
+                                       const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                       float* k_scale, float* v_scale, int32_t scale_policy,
+                                       void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (scale_policy != PA_SCALE_KEEP && scale_policy != PA_SCALE_FIRST_TOKEN)
+    return PA_ERR_INVALID_ARG;
+  if (src_dtype != PA_F16 && src_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (cache->kv_dtype != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4))
+    return PA_ERR_INVALID_ARG;
+  pa::QuantAppendArgs a;
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
+  a.slots = slot_mapping;
+  a.k_cache = static_cast<uint8_t*>(k_cache);
+  a.v_cache = static_cast<uint8_t*>(v_cache);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.num_slots = (int64_t)cache->num_blocks * pa::kBlock;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  hipError_t e = pa::launch_append_quant(a, num_tokens, src_dtype == PA_BF16,
+                                         scale_policy == PA_SCALE_FIRST_TOKEN,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
 PA_EXPORT size_t pa_decode_workspace_size(const pa_decode_desc* desc) {
   if (check_decode_desc(desc) != PA_OK) return 0;
   return workspace_bytes_of(desc);

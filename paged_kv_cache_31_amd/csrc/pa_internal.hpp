@@ -26,6 +26,19 @@ struct AppendArgs {
   int head_dim;
 };
 
+struct QuantAppendArgs {
+  const uint8_t* k_new;  // [T][num_kv_heads][head_dim] 16-bit
+  const uint8_t* v_new;
+  const int64_t* slots;
+  uint8_t* k_cache;      // fp8 pools
+  uint8_t* v_cache;
+  float* k_scale;        // [num_blocks][num_kv_heads]
+  float* v_scale;
+  int64_t num_slots;
+  int num_kv_heads;
+  int head_dim;
+};
+
 struct DecodeArgs {
   const void* q;
   const void* k_cache;
@@ -102,6 +115,8 @@ inline WorkspaceLayout workspace_layout(int group, int head_dim, long workgroups
 constexpr long kMaxWaves = 8192;
 
 hipError_t launch_append(const AppendArgs& a, int num_tokens, int elem_bytes, hipStream_t stream);
+hipError_t launch_append_quant(const QuantAppendArgs& a, int num_tokens, bool bf16_src,
+                               bool first_token_scale, hipStream_t stream);
 // Enqueues the decode; with a.ws_skip set, the prefix kernel runs first (prefix_wgs workgroups).
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
                          int prefix_wgs, hipStream_t stream);

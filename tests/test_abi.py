@@ -161,3 +161,28 @@ def test_decode_append_rejects_missing_rows():
     assert lib.pa_decode_append(*args(ctypes.c_void_p(0x10008), FAKE)) == pa.PA_ERR_INVALID_ARG
     # otherwise validated as pa_decode: no workspace
     assert lib.pa_decode_append(*args(FAKE, FAKE)) == pa.PA_ERR_WORKSPACE
+
+
+def test_append_quant_rejects():
+    lib = pa.lib()
+    c = pa.CacheDesc(64, 2, 64, 16, pa.PA_FP8_E4M3)
+    ptrs = [FAKE] * 7
+
+    def call(desc=ctypes.byref(c), n=1, src=pa.PA_BF16, p=ptrs, policy=pa.PA_SCALE_KEEP):
+        return lib.pa_kv_append_quant(desc, n, src, *p, policy, None)
+
+    assert call(n=0) == pa.PA_OK                                   # no tokens: no-op
+    assert call(n=-1) == pa.PA_ERR_INVALID_ARG
+    assert call(desc=None) == pa.PA_ERR_INVALID_ARG
+    assert call(policy=2) == pa.PA_ERR_INVALID_ARG
+    assert call(src=pa.PA_FP8_E4M3) == pa.PA_ERR_UNSUPPORTED      # 16-bit sources only
+    c16 = pa.CacheDesc(64, 2, 64, 16, pa.PA_BF16)
+    assert call(desc=ctypes.byref(c16)) == pa.PA_ERR_UNSUPPORTED  # fp8 caches only
+    for i in range(7):
+        p = list(ptrs)
+        p[i] = None
+        assert call(p=p) == pa.PA_ERR_INVALID_ARG, i
+    for i, bad in enumerate((0x10008, 0x10008, 0x10004, 0x10008, 0x10008, 0x10002, 0x10002)):
+        p = list(ptrs)
+        p[i] = ctypes.c_void_p(bad)
+        assert call(p=p) == pa.PA_ERR_INVALID_ARG, i
