@@ -9,4 +9,4 @@ decoded inputs, and shares no code with the HIP library.
 from .formats import (E4M3FN_TABLE, bf16_to_f64, e4m3fn_encode, e4m3fn_to_f64,  # noqa: F401
                       f16_to_f64, to_f64)
 from .paged_attention import (SCALE_FIRST_TOKEN, SCALE_KEEP, attend, decode,  # noqa: F401
-                              decode_split, gather, kv_append, kv_append_quant)
+                              decode_multi, decode_split, gather, kv_append, kv_append_quant)

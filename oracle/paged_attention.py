@@ -18,6 +18,12 @@ What is computed, and where the pages state it:
   KV-cache attention module; scale is passed in, the configs use 1/sqrt(head_dim)).
   GQA: query head h reads KV head h // (Hq / Hkv) (Scaling Book note, "生成スループット/レイテンシ
   改善のテクニック": groups of query heads share one KV head).
+* decode_multi -- several new query tokens per sequence in one pass, each attending causally
+  to every cached token up to and including its own position: the target model's verification
+  of K draft tokens in one forward pass (youngju.dev guide, speculative-decoding figure; magi
+  page, "投機的デコードとの相互作用") and a chunk of a long prompt processed against the cache
+  built so far (magi page, "Prefill-Decode 分離 — chunked prefill と disaggregation").  The T
+  new tokens are the last T of the sequence's context_lens tokens (already in the cache).
 * decode_split -- the same attention evaluated over fixed key partitions and merged by
   log-sum-exp; used only to pin the merge algebra the GPU's split-KV path relies on.  The pages
   give online softmax without spelling out a split (babushkai.com "GPU推論の内部構造",
@@ -161,6 +167,36 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_dtype, kv_d
             if return_weights:
                 weights[(b, kvh)] = w
     return (out, weights) if return_weights else out
+
+
+def decode_multi(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, q_dtype,
+                 kv_dtype, k_scale=None, v_scale=None):
+    """Causal attention of several query tokens per sequence over its paged cache.
+
+    q holds [N][Hq][D] query rows; sequence b owns rows query_start[b] .. query_start[b+1]-1,
+    T_b of them, and context_lens[b] = L_b counts every cached token including those T_b.
+    Row i of sequence b sits at logical position p = L_b - T_b + i and attends to the tokens
+    0 .. p, i.e. the first min(max(p + 1, 0), L_b) of the sequence (none when p < 0: zeros, as for
+    an empty context).  Returns [N][Hq][D] float64.
+    """
+    qf = _q_f64(q, q_dtype)
+    N, Hq, D = qf.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    sc = float(np.float32(scale))
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = np.zeros((N, Hq, D))
+    for b in range(len(qs) - 1):
+        T = int(qs[b + 1] - qs[b])
+        L = int(context_lens[b])
+        for kvh in range(Hkv):
+            k, v = gather(k_cache, v_cache, kv_dtype, block_tables[b], L, kvh, k_scale, v_scale)
+            for i in range(T):
+                n = min(max(L - T + i + 1, 0), L)
+                row = int(qs[b]) + i
+                o, _ = attend(qf[row, kvh * G:(kvh + 1) * G], k[:n], v[:n], sc)
+                out[row, kvh * G:(kvh + 1) * G] = o
+    return out
 
 
 def decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, q_dtype, kv_dtype,

@@ -179,3 +179,68 @@ def test_quant_pins_catch_planted_mistake(name, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught >= 1, f"no pin caught: {name}"
+
+
+# ---- several query tokens per sequence: planted mistakes in the causal window and row mapping.
+import test_oracle_multi as M  # noqa: E402
+
+_orig_multi = pa.decode_multi
+
+
+def _multi_with(n_of=lambda L, T, i: min(max(L - T + i + 1, 0), L),
+                row_of=lambda qs, b, i: int(qs[b]) + i):
+    def multi(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, q_dtype,
+              kv_dtype, k_scale=None, v_scale=None):
+        qf = pa._q_f64(q, q_dtype)
+        N, Hq, D = qf.shape
+        Hkv = k_cache.shape[1]
+        G = Hq // Hkv
+        qs = np.asarray(query_start, dtype=np.int64)
+        out = np.zeros((N, Hq, D))
+        for b in range(len(qs) - 1):
+            T, L = int(qs[b + 1] - qs[b]), int(context_lens[b])
+            for kvh in range(Hkv):
+                k, v = pa.gather(k_cache, v_cache, kv_dtype, block_tables[b], L, kvh, k_scale,
+                                 v_scale)
+                for i in range(T):
+                    n = n_of(L, T, i)
+                    o, _ = pa.attend(qf[row_of(qs, b, i), kvh * G:(kvh + 1) * G], k[:n], v[:n],
+                                     float(np.float32(scale)))
+                    out[int(qs[b]) + i, kvh * G:(kvh + 1) * G] = o
+        return out
+    return multi
+
+
+MULTI_MUTATIONS = {
+    "multi: a row misses its own token": _multi_with(n_of=lambda L, T, i: max(L - T + i, 0)),
+    "multi: mask aligned to the first key": _multi_with(n_of=lambda L, T, i: min(i + 1, L)),
+    "multi: no causal mask": _multi_with(n_of=lambda L, T, i: L),
+    "multi: rows of a sequence reversed":
+        _multi_with(row_of=lambda qs, b, i: int(qs[b + 1]) - 1 - i),
+}
+
+MULTI_PINS = [
+    lambda: M.test_multi_matches_masked_sdpa("bf16", "bf16", 3),
+    M.test_each_row_is_the_single_query_decode_at_its_position,
+    M.test_a_row_ignores_every_later_token,
+    M.test_rows_before_the_context_are_zero_and_empty_sequences_have_no_rows,
+]
+
+
+@pytest.mark.parametrize("name", list(MULTI_MUTATIONS))
+def test_multi_pins_catch_planted_mistake(name, monkeypatch):
+    monkeypatch.setattr(pa, "decode_multi", MULTI_MUTATIONS[name])
+    monkeypatch.setattr(M.oracle, "decode_multi", MULTI_MUTATIONS[name])
+    caught = 0
+    for pin in MULTI_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"no pin caught: {name}"
+
+
+def test_multi_unmutated_copy_passes(monkeypatch):
+    monkeypatch.setattr(M.oracle, "decode_multi", _multi_with())
+    for pin in MULTI_PINS:
+        pin()
