@@ -94,6 +94,20 @@ typedef struct pa_decode_desc {
                                  The result is the same attention up to rounding order. */
 } pa_decode_desc;
 
+typedef struct pa_multi_desc {
+  pa_cache_desc cache;
+  int32_t batch;              /* sequences, > 0 */
+  int32_t num_q_heads;        /* a multiple of num_kv_heads (any group size) */
+  int32_t max_blocks_per_seq; /* row length (stride) of block_tables, > 0 */
+  int32_t max_context_len;    /* host-side bound on context_lens, as in pa_decode_desc (0: table) */
+  int32_t total_queries;      /* rows of q and out, >= 0 */
+  int32_t max_query_len;      /* host-side bound on query_start[b+1] - query_start[b], > 0 */
+  int32_t partition_tokens;   /* key partition per row tile, a multiple of 32 in [32, 65536];
+                                 0 = chosen from the shape (one partition when there are rows
+                                 enough to fill the GPU) */
+  int32_t q_dtype;            /* PA_F16 or PA_BF16; the output has the same dtype */
+} pa_multi_desc;
+
 /*
  * pa_kv_append -- write num_tokens new K/V rows into their cache slots.
  *
@@ -183,6 +197,38 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
                     const void* v_cache, const float* k_scale, const float* v_scale,
                     const int32_t* block_tables, const int32_t* context_lens, float scale,
                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_multi -- causal attention of several new query tokens per sequence over the paged
+ * cache: the target model's one-pass check of draft tokens in speculative decoding (youngju.dev
+ * guide, speculative-decoding figure; magi-web "Inference Batching", "投機的デコードとの相互作用")
+ * and a chunk of a long prompt against the cache built so far (magi-web, "Prefill-Decode 分離 —
+ * chunked prefill と disaggregation").
+ *
+ *   q             [total_queries][num_q_heads][head_dim] of q_dtype, 16-byte aligned
+ *   query_start   [batch + 1] int32 (device): sequence b owns rows query_start[b] ..
+ *                 query_start[b+1] - 1, T_b of them (clamped to [0, max_query_len]); rows no
+ *                 sequence owns are left untouched in out
+ *   context_lens  [batch] int32 (device): L_b counts every cached token including the T_b new
+ *                 ones, which must already be in the cache (pa_kv_append with their slots)
+ *   out           [total_queries][num_q_heads][head_dim] of q_dtype
+ *   other arguments as pa_decode
+ *
+ * Row i of sequence b sits at position p = L_b - T_b + i and gets
+ * softmax(scale * q . K[0..p]^T) . V[0..p] with query head h reading KV head h / group; a row
+ * with p < 0 sees no token and is zero.  fp32 accumulation; within 2e-3 absolute + 2e-3 relative
+ * of the exact result.  The workspace (pa_decode_multi_workspace_size bytes, 16-byte aligned) is
+ * needed only when a row tile's keys are cut into several partitions; its contents need no
+ * initialisation.  Calls sharing a workspace must be ordered on one stream.
+ */
+pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q, const int32_t* query_start,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* block_tables,
+                          const int32_t* context_lens, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_decode_multi needs for desc (0 if none or if desc is invalid). */
+size_t pa_decode_multi_workspace_size(const pa_multi_desc* desc);
 
 /*
  * pa_decode_append -- one whole decode step in one launch: for every sequence b with

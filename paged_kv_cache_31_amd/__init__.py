@@ -40,6 +40,14 @@ class DecodeDesc(ctypes.Structure):
                 ("q_dtype", ctypes.c_int32), ("shared_prefixes", ctypes.c_int32)]
 
 
+class MultiDesc(ctypes.Structure):
+    _fields_ = [("cache", CacheDesc), ("batch", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("max_context_len", ctypes.c_int32), ("total_queries", ctypes.c_int32),
+                ("max_query_len", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32)]
+
+
 class PaError(RuntimeError):
     def __init__(self, fn: str, status: int, hip_error: int = 0):
         self.status = status
@@ -54,7 +62,8 @@ _lib = None
 _lock = threading.Lock()
 
 EXPORTS = ("pa_kv_append", "pa_kv_append_quant", "pa_decode", "pa_decode_append",
-           "pa_decode_workspace_size", "pa_status_string", "pa_last_hip_error")
+           "pa_decode_workspace_size", "pa_decode_multi", "pa_decode_multi_workspace_size",
+           "pa_status_string", "pa_last_hip_error")
 
 
 def lib() -> ctypes.CDLL:
@@ -79,6 +88,11 @@ def lib() -> ctypes.CDLL:
             L.pa_decode_append.restype = i32
             L.pa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc)]
             L.pa_decode_workspace_size.restype = sz
+            L.pa_decode_multi.argtypes = [ctypes.POINTER(MultiDesc), vp, vp, vp, vp, vp, vp, vp,
+                                          vp, ctypes.c_float, vp, vp, sz, vp]
+            L.pa_decode_multi.restype = i32
+            L.pa_decode_multi_workspace_size.argtypes = [ctypes.POINTER(MultiDesc)]
+            L.pa_decode_multi_workspace_size.restype = sz
             L.pa_status_string.argtypes = [i32]
             L.pa_status_string.restype = ctypes.c_char_p
             L.pa_last_hip_error.argtypes = []
@@ -263,4 +277,66 @@ def pa_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_le
     DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                max_context_len, partition_tokens, workspace, stream, shared_prefixes, k_new,
                v_new)()
+    return out
+
+
+def multi_desc(q, k_cache, block_tables, max_query_len, max_context_len=0,
+               partition_tokens=0) -> MultiDesc:
+    N, Hq, D = q.shape
+    return MultiDesc(cache_desc(k_cache), block_tables.shape[0], Hq, block_tables.shape[1],
+                     int(max_context_len), N, int(max_query_len), int(partition_tokens),
+                     _dtype_code(q, False))
+
+
+def pa_decode_multi_workspace_size(desc: MultiDesc) -> int:
+    return int(lib().pa_decode_multi_workspace_size(ctypes.byref(desc)))
+
+
+class MultiCall:
+    """pa_decode_multi with its arguments marshalled once; calling it only enqueues the kernels.
+
+    q, out [N][Hq][D]; query_start int32 [B + 1] (rows of sequence b: query_start[b] ..
+    query_start[b+1]-1, the last tokens of its context_lens[b] cached tokens)."""
+
+    def __init__(self, q, query_start, k_cache, v_cache, block_tables, context_lens, scale, out,
+                 max_query_len, k_scale=None, v_scale=None, max_context_len=0,
+                 partition_tokens=0, workspace=None, stream=None):
+        for t in (q, query_start, k_cache, v_cache, block_tables, context_lens, out):
+            assert t.is_cuda and t.is_contiguous()
+        assert query_start.dtype == torch.int32 and block_tables.dtype == torch.int32
+        assert context_lens.dtype == torch.int32
+        assert out.shape == q.shape and out.dtype == q.dtype
+        NB, Hkv, bs, D = k_cache.shape
+        assert tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB][Hkv][D][16]"
+        B = block_tables.shape[0]
+        assert q.shape[2] == D and context_lens.shape[0] == B and query_start.shape[0] == B + 1
+        self._desc = multi_desc(q, k_cache, block_tables, max_query_len, max_context_len,
+                                partition_tokens)
+        need = pa_decode_multi_workspace_size(self._desc)
+        st = _stream(stream)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._keep = (q, query_start, k_cache, v_cache, block_tables, context_lens, out, k_scale,
+                      v_scale, workspace)
+        self._fn = lib().pa_decode_multi
+        self._args = (ctypes.byref(self._desc), _ptr(q), _ptr(query_start), _ptr(k_cache),
+                      _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                      _ptr(context_lens), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+                      ctypes.c_size_t(wbytes), st)
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check("pa_decode_multi", st)
+
+
+def pa_decode_multi(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, out,
+                    max_query_len, k_scale=None, v_scale=None, max_context_len=0,
+                    partition_tokens=0, workspace=None, stream=None) -> torch.Tensor:
+    """Causal attention of several query tokens per sequence (speculative verification, prefill
+    chunks) over the paged cache; returns out."""
+    MultiCall(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, out,
+              max_query_len, k_scale, v_scale, max_context_len, partition_tokens, workspace,
+              stream)()
     return out

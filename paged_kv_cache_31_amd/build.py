@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_api.hip", "append.hip", "decode.hip"]
+SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "multi.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -59,38 +59,9 @@
 
 #include "device_common.hpp"
 #include "pa_internal.hpp"
+#include "stepper.hpp"
 
 namespace pa {
-
-template <int D, bool FP8> struct StepRegs;
-template <int D> struct StepRegs<D, false> {
-  uint4 k[2][D / 32];   // per 16-token row set m: one 16-byte load per 32-dim chunk
-  uint4 v[D / 16];      // per 16-dim tile: 8 tokens x 16-bit
-};
-template <int D> struct StepRegs<D, true> {
-  uint4 k[2][D / 64];   // one 16-byte load covers two 32-dim chunks of 8 codes
-  uint2 v[D / 16];      // 8 tokens x 1 byte
-  float ks, vs;         // block scales of this lane's block
-};
-
-template <typename V8>
-__device__ __forceinline__ V8 zero_vec8() {
-  return __builtin_bit_cast(V8, make_uint4(0u, 0u, 0u, 0u));
-}
-
-template <int QT>
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  typedef typename Mfma<QT>::elem E;
-  E a = (E)x, b = (E)y;
-  uint16_t ua, ub;
-  __builtin_memcpy(&ua, &a, 2);
-  __builtin_memcpy(&ub, &b, 2);
-  return (uint32_t)ua | ((uint32_t)ub << 16);
-}
-
-__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
-__device__ __forceinline__ int blocks_of(int L) { return (L + kBlock - 1) / kBlock; }
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Leading blocks of sequence b that prefix_kernel covers (0 when shared prefixes are off).  The
 // plan never takes the block holding a sequence's last token, so at least one block is left;
@@ -109,245 +80,6 @@ struct PieceMeta {
 
 // Published parts a merging workgroup stages in LDS at once (more are folded in batches).
 constexpr int kMergeStage = 64;
-
-// The streaming core shared by decode_kernel and prefix_kernel: one wave, one query column per
-// lane column (lane%16), online softmax over a range of logical blocks of one table row.  K/V
-// loads are non-temporal (STREAM) where each byte is read once per launch, and cached where
-// several workgroups read the same blocks.
-template <int D, int QT, int KVT, bool STREAM = true>
-struct Stepper {
-  typedef Mfma<QT> M;
-  typedef typename M::vec8 V8;
-  typedef typename M::elem E;
-  static constexpr bool FP8 = KVT == DT_FP8;
-  static constexpr bool SPLIT_P = QT == DT_BF16;
-  static constexpr int EB = FP8 ? 1 : 2;          // bytes per cache element
-  static constexpr int NC = D / 32;               // 32-dim chunks (QK)
-  static constexpr int NT = D / 16;               // 16-dim tiles (PV)
-  static constexpr int KL = FP8 ? NC / 2 : NC;    // K loads per row set
-  static constexpr int TILE = kBlock * D * EB;    // bytes of one (block, kv head) tile
-
-  const uint8_t* kc;
-  const uint8_t* vc;
-  const float* ksc;
-  const float* vsc;
-  int Hkv, num_blocks;
-  float qk_scale_log2;
-  int col, grp, k_lane_off, v_lane_off, tb_lane;
-  bool k_hi, v_hi;
-
-  __device__ __forceinline__ Stepper(const DecodeArgs& a, int lane)
-      : kc(reinterpret_cast<const uint8_t*>(a.k_cache)),
-        vc(reinterpret_cast<const uint8_t*>(a.v_cache)),
-        ksc(a.k_scale), vsc(a.v_scale), Hkv(a.num_kv_heads), num_blocks(a.num_blocks),
-        qk_scale_log2(a.qk_scale_log2) {
-    col = lane & 15;
-    grp = lane >> 4;
-    // K row r = col of MFMA m holds token 16*(r/8) + 8*((r/4)%2) + 4*m + r%4 of the step; its
-    // block is r/8.  Result row 4*grp+i of MFMA m is then token tb + 4*m + i with
-    // tb = 16*(grp/2) + 8*(grp%2), which is exactly the token order the PV operands use.
-    k_lane_off = (8 * ((col >> 2) & 1) + (col & 3)) * D * EB + 16 * grp;
-    v_lane_off = (col * kBlock + 8 * (grp & 1)) * EB;
-    k_hi = col >= 8;
-    v_hi = grp >= 2;
-    tb_lane = 16 * (grp >> 1) + 8 * (grp & 1);
-  }
-
-  static __device__ __forceinline__ uint4 load16(const uint8_t* p) {
-    if constexpr (STREAM) return load_stream16(p);
-    else return *reinterpret_cast<const uint4*>(p);
-  }
-  static __device__ __forceinline__ uint2 load8(const uint8_t* p) {
-    if constexpr (STREAM) return load_stream8(p);
-    else return *reinterpret_cast<const uint2*>(p);
-  }
-
-  // Q^T as the B operand of the QK product for this lane's query row (nullptr: zeros).  Lane
-  // (column col, group grp) holds 8 dims per chunk; fp8 tiles pair chunks (2c, 2c+1) in one
-  // 16-byte load, which permutes which dims a lane holds for each chunk, and Q follows suit.
-  __device__ __forceinline__ void load_q(V8 (&qB)[NC], const E* qrow) const {
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const int d0 = FP8 ? 64 * (cc >> 1) + 16 * grp + 8 * (cc & 1) : 32 * cc + 8 * grp;
-      qB[cc] = qrow ? as_vec8<V8>(*reinterpret_cast<const uint4*>(qrow + d0)) : zero_vec8<V8>();
-    }
-  }
-
-  // Online-softmax attention over logical blocks [j0, j1) of table row trow for KV head kvh
-  // (tokens at or past end_tok are masked), taking the steps s_first, s_first + stride, ... of
-  // the range, into the running (m_run, l_run, acc).
-  // wait_stores: this wave's earlier stores write a block the run reads in its last step.  The
-  // loads of a run's third and later steps are issued after the first step's wait on the memory
-  // counter, which in-order completion makes cover those older stores; a run of one or two
-  // steps waits for them explicitly before its first load.
-  __device__ __forceinline__ void run(const V8 (&qB)[NC], const int32_t* trow, int kvh, int j0,
-                                      int j1, int end_tok, int s_first, int stride,
-                                      float& m_run, float& l_run, f32x4 (&acc)[NT],
-                                      bool wait_stores = false) const {
-    const int nsteps = (j1 - j0 + 1) >> 1;
-    if (s_first >= nsteps) return;
-
-    // Block ids of a step: logical blocks j0+2s and j0+2s+1 (the second one repeats the first
-    // when the range ends after one block; its tokens are masked).  Ids outside the pool read
-    // block 0.
-    auto ids_of = [&](int s, int& p0, int& p1) {
-      s = min(s, nsteps - 1);
-      const int jb = j0 + 2 * s;
-      const int jb1 = jb + 1 < j1 ? jb + 1 : jb;
-      const int i0 = trow[jb], i1 = trow[jb1];
-      p0 = (unsigned)i0 < (unsigned)num_blocks ? i0 : 0;
-      p1 = (unsigned)i1 < (unsigned)num_blocks ? i1 : 0;
-    };
-    int nid0, nid1;
-    ids_of(s_first, nid0, nid1);
-    if (wait_stores && nsteps - s_first <= 2 * stride) wait_memory_ops();
-
-    auto issue = [&](StepRegs<D, FP8>& r, int s) {
-      const int pb0 = nid0, pb1 = nid1;
-      ids_of(s + stride, nid0, nid1);              // prefetch the next step's block ids
-      const int kb = k_hi ? pb1 : pb0;
-      const int vb = v_hi ? pb1 : pb0;
-      const uint8_t* kp = kc + ((size_t)kb * Hkv + kvh) * TILE + k_lane_off;
-      const uint8_t* vp = vc + ((size_t)vb * Hkv + kvh) * TILE + v_lane_off;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int cc = 0; cc < KL; ++cc) r.k[m][cc] = load16(kp + m * 4 * D * EB + cc * 64);
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        if constexpr (FP8)
-          r.v[i] = load8(vp + i * 16 * kBlock * EB);
-        else
-          r.v[i] = load16(vp + i * 16 * kBlock * EB);
-      }
-      if constexpr (FP8) {
-        r.ks = ksc[(size_t)vb * Hkv + kvh];
-        r.vs = vsc[(size_t)vb * Hkv + kvh];
-      }
-    };
-
-    auto compute = [&](StepRegs<D, FP8>& r, int s) {
-      const int t0 = kBlock * (j0 + 2 * s);
-      const int tb = t0 + tb_lane;
-      const bool partial = t0 + kStepTokens > end_tok;     // wave-uniform
-
-      // scores of 8 tokens (tb + jj) for head col
-      f32x4 S[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        S[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          V8 kA;
-          if constexpr (FP8) {
-            const uint4 w = r.k[m][cc >> 1];
-            kA = (cc & 1) ? fp8x8_to_vec8<QT>(w.z, w.w) : fp8x8_to_vec8<QT>(w.x, w.y);
-          } else {
-            kA = as_vec8<V8>(r.k[m][cc]);
-          }
-          S[m] = M::mma(kA, qB[cc], S[m]);
-        }
-      }
-      float qs = qk_scale_log2;
-      if constexpr (FP8) qs *= r.ks;
-      float sc[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sc[jj] = S[jj >> 2][jj & 3] * qs;
-      int nval = 8;
-      if (partial) {
-        nval = min(max(end_tok - tb, 0), 8);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (jj >= nval) sc[jj] = -INFINITY;
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
-      mx = max_across_rows(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      float pr[8], psum = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        pr[jj] = fast_exp2(sc[jj] - m_new);
-        psum += pr[jj];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < NT; ++i) acc[i] *= alpha;
-      if constexpr (FP8) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pr[jj] *= r.vs;
-      }
-
-      // P^T as the B operand: this lane's 8 weights, in token order.
-      uint4 hi_bits, lo_bits;
-      {
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          h[w] = pack2<QT>(pr[2 * w], pr[2 * w + 1]);
-          if constexpr (SPLIT_P) {
-            const V8 hv = as_vec8<V8>(make_uint4(h[w], 0u, 0u, 0u));
-            l[w] = pack2<QT>(pr[2 * w] - (float)hv[0], pr[2 * w + 1] - (float)hv[1]);
-          }
-        }
-        hi_bits = make_uint4(h[0], h[1], h[2], h[3]);
-        if constexpr (SPLIT_P) lo_bits = make_uint4(l[0], l[1], l[2], l[3]);
-      }
-      const V8 pHi = as_vec8<V8>(hi_bits);
-      V8 pLo;
-      if constexpr (SPLIT_P) pLo = as_vec8<V8>(lo_bits);
-
-      // Masked tokens get weight 0, but their cache slots may hold anything (NaN included), so
-      // their V elements are zeroed before the product.
-      uint32_t vm[4] = {~0u, ~0u, ~0u, ~0u};
-      if (partial) {
-        if constexpr (FP8) {
-          vm[0] = nval >= 4 ? ~0u : (nval <= 0 ? 0u : (1u << (8 * nval)) - 1u);
-          vm[1] = nval >= 8 ? ~0u : (nval <= 4 ? 0u : (1u << (8 * (nval - 4))) - 1u);
-        } else {
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            vm[w] = (2 * w < nval ? 0x0000FFFFu : 0u) | (2 * w + 1 < nval ? 0xFFFF0000u : 0u);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        V8 vA;
-        if constexpr (FP8) {
-          vA = fp8x8_to_vec8<QT>(r.v[i].x & vm[0], r.v[i].y & vm[1]);
-        } else {
-          const uint4 u = r.v[i];
-          vA = as_vec8<V8>(make_uint4(u.x & vm[0], u.y & vm[1], u.z & vm[2], u.w & vm[3]));
-        }
-        acc[i] = M::mma(vA, pHi, acc[i]);
-        if constexpr (SPLIT_P) acc[i] = M::mma(vA, pLo, acc[i]);
-      }
-    };
-
-
-    // The steady-state loop issues the next step's loads unconditionally (the tail is peeled),
-    // so the loads of one step stay in flight while the previous step is computed.
-    StepRegs<D, FP8> r0, r1;
-    int s = s_first, rest = (nsteps - 1 - s_first) / stride;
-    issue(r0, s);
-    for (; rest >= 2; rest -= 2, s += 2 * stride) {
-      issue(r1, s + stride);
-      compute(r0, s);
-      issue(r0, s + 2 * stride);
-      compute(r1, s + stride);
-    }
-    if (rest == 1) {
-      issue(r1, s + stride);
-      compute(r0, s);
-      compute(r1, s + stride);
-    } else {
-      compute(r0, s);
-    }
-  }
-};
 
 // Parts (partial results over kUnitBlocks shared blocks each) that cover `skip` shared blocks.
 __device__ __forceinline__ int prefix_parts(int skip) { return (skip + kUnitBlocks - 1) / kUnitBlocks; }

@@ -69,6 +69,20 @@ int len_cap(const pa_decode_desc* d) {
   return (int)cap;
 }
 
+// Longest context a multi-query launch covers (same rule as len_cap).
+int multi_len_cap(const pa_multi_desc* d) {
+  const int64_t table_cap = (int64_t)d->max_blocks_per_seq * pa::kBlock;
+  int64_t cap = d->max_context_len > 0 ? d->max_context_len : table_cap;
+  if (cap > table_cap) cap = table_cap;
+  if (cap > INT32_MAX) cap = INT32_MAX;
+  return (int)cap;
+}
+
+pa::MultiPlan multi_plan_of(const pa_multi_desc* d) {
+  return pa::multi_plan(d->batch, d->cache.num_kv_heads, d->num_q_heads / d->cache.num_kv_heads,
+                        d->max_query_len, multi_len_cap(d), d->partition_tokens);
+}
+
 // Upper bound of the flattened (sequence, KV head, block) space.
 int64_t blocks_upper(const pa_decode_desc* d) {
   return (int64_t)d->batch * d->cache.num_kv_heads * ((len_cap(d) + pa::kBlock - 1) / pa::kBlock);
@@ -206,6 +220,102 @@ PA_EXPORT pa_status pa_kv_append_quant(const pa_cache_desc* cache, int32_t num_t
   hipError_t e = pa::launch_append_quant(a, num_tokens, src_dtype == PA_BF16,
                                          scale_policy == PA_SCALE_FIRST_TOKEN,
                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+namespace {
+
+pa_status check_multi_desc(const pa_multi_desc* d) {
+  if (!d) return PA_ERR_INVALID_ARG;
+  pa_status s = check_cache(&d->cache);
+  if (s != PA_OK) return s;
+  if (d->batch <= 0 || d->num_q_heads <= 0 || d->max_blocks_per_seq <= 0 ||
+      d->max_context_len < 0 || d->partition_tokens < 0 || d->total_queries < 0 ||
+      d->max_query_len <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->cache.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (d->partition_tokens != 0 &&
+      (d->partition_tokens % pa::kStepTokens != 0 || d->partition_tokens > pa::kMaxPartition))
+    return PA_ERR_INVALID_ARG;
+  if (d->q_dtype != PA_F16 && d->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  const int kv = d->cache.kv_dtype;
+  if (kv != PA_FP8_E4M3 && kv != d->q_dtype) return PA_ERR_UNSUPPORTED;
+  // grid sizes: items of the attention kernel and rows of the merge, 4 waves per workgroup
+  const pa::MultiPlan p = multi_plan_of(d);
+  if (p.items > (1LL << 32) || (long long)d->batch * d->max_query_len * d->num_q_heads > (1LL << 32))
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT size_t pa_decode_multi_workspace_size(const pa_multi_desc* desc) {
+  if (check_multi_desc(desc) != PA_OK) return 0;
+  return pa::multi_workspace_bytes(multi_plan_of(desc), desc->total_queries, desc->num_q_heads,
+                                   desc->cache.head_dim);
+}
+
+PA_EXPORT pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q,
+                                    const int32_t* query_start, const void* k_cache,
+                                    const void* v_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_tables,
+                                    const int32_t* context_lens, float scale, void* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status s = check_multi_desc(desc);
+  if (s != PA_OK) return s;
+  if (!query_start || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (desc->total_queries > 0 && (!q || !out || !aligned(q, 16) || !aligned(out, 16)))
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_INVALID_ARG;
+  const bool fp8 = desc->cache.kv_dtype == PA_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return PA_ERR_INVALID_ARG;
+  if (!fp8 && (k_scale || v_scale)) return PA_ERR_INVALID_ARG;
+  const pa::MultiPlan p = multi_plan_of(desc);
+  const size_t need = pa::multi_workspace_bytes(p, desc->total_queries, desc->num_q_heads,
+                                                desc->cache.head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return PA_ERR_WORKSPACE;
+  if (desc->total_queries == 0) return PA_OK;
+
+  pa::MultiArgs a;
+  a.q = q;
+  a.query_start = query_start;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  const size_t rows = (size_t)desc->total_queries * desc->num_q_heads * p.num_parts;
+  a.ws_acc = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                pa::align256(rows * desc->cache.head_dim * 4))
+                     : nullptr;
+  a.batch = desc->batch;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->cache.num_kv_heads;
+  a.group = desc->num_q_heads / desc->cache.num_kv_heads;
+  a.num_blocks = desc->cache.num_blocks;
+  a.max_blocks_per_seq = desc->max_blocks_per_seq;
+  a.len_cap = multi_len_cap(desc);
+  a.total_queries = desc->total_queries;
+  a.max_query_len = desc->max_query_len;
+  a.tiles_per_head = p.tiles_per_head;
+  a.num_parts = p.num_parts;
+  a.part_blocks = p.part_blocks;
+  a.total_items = p.items;
+  a.qk_scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pa::launch_multi(a, desc->cache.head_dim, desc->q_dtype, desc->cache.kv_dtype,
+                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_hip_error = (int32_t)e;
     return PA_ERR_HIP;

@@ -114,12 +114,88 @@ inline WorkspaceLayout workspace_layout(int group, int head_dim, long workgroups
 // Waves launched by the balanced mode never exceed this (a workspace bound known without a GPU).
 constexpr long kMaxWaves = 8192;
 
+// Several query tokens per sequence (pa_decode_multi).  The query rows of one (sequence, KV
+// head) are (token i, group member g) pairs in the order i * group + g, cut into tiles of 16
+// (one MFMA column each); each tile's keys are cut into partitions of part_blocks blocks.  An
+// item is one (sequence, KV head, partition, tile), handled by one wave.
+struct MultiArgs {
+  const void* q;               // [total_queries][num_q_heads][head_dim]
+  const int32_t* query_start;  // [batch + 1]: rows of sequence b are query_start[b] ..
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;                   // [total_queries][num_q_heads][head_dim]
+  float* ws_acc;               // [total_queries * num_q_heads][num_parts][head_dim] (num_parts > 1)
+  float* ws_ml;                // [total_queries * num_q_heads][num_parts][2]: max (log2), exp-sum
+  int batch;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int num_blocks;
+  int max_blocks_per_seq;
+  int len_cap;                 // context lengths are clamped to [0, len_cap]
+  int total_queries;
+  int max_query_len;           // query counts are clamped to [0, max_query_len]
+  int tiles_per_head;          // ceil(max_query_len * group / 16)
+  int num_parts;
+  int part_blocks;             // even
+  long long total_items;
+  float qk_scale_log2;
+};
+
+constexpr int kMultiWaves = 4;             // waves per multi_kernel workgroup
+constexpr long kMultiTargetWaves = 4096;   // items the automatic partition aims for
+constexpr int kMultiMinPartBlocks = 16;    // automatic partitions are at least 256 tokens
+
+struct MultiPlan {
+  int tiles_per_head, num_parts, part_blocks;
+  long long items;
+};
+// A pure function of the descriptor, so the workspace size is known without a GPU.
+inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_query_len,
+                            int len_cap, int partition_tokens) {
+  MultiPlan p;
+  p.tiles_per_head = (int)(((long long)max_query_len * group + 15) / 16);
+  const long long maxblk = ((long long)len_cap + kBlock - 1) / kBlock;
+  long long pb;
+  if (partition_tokens > 0) {
+    pb = partition_tokens / kBlock;
+  } else {
+    const long long base = (long long)batch * num_kv_heads * (p.tiles_per_head > 0 ? p.tiles_per_head : 1);
+    long long np = (kMultiTargetWaves + base - 1) / base;
+    const long long np_max = (maxblk + kMultiMinPartBlocks - 1) / kMultiMinPartBlocks;
+    if (np > np_max) np = np_max;
+    if (np < 1) np = 1;
+    pb = (maxblk + np - 1) / np;
+    pb += pb & 1;
+    if (pb < 2) pb = 2;
+  }
+  long long np = (maxblk + pb - 1) / pb;
+  if (np < 1) np = 1;
+  p.part_blocks = (int)pb;
+  p.num_parts = (int)np;
+  p.items = (long long)batch * num_kv_heads * np * p.tiles_per_head;
+  return p;
+}
+inline size_t multi_workspace_bytes(const MultiPlan& p, int total_queries, int num_q_heads,
+                                    int head_dim) {
+  if (p.num_parts <= 1) return 0;
+  const size_t rows = (size_t)total_queries * num_q_heads * p.num_parts;
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
 hipError_t launch_append(const AppendArgs& a, int num_tokens, int elem_bytes, hipStream_t stream);
 hipError_t launch_append_quant(const QuantAppendArgs& a, int num_tokens, bool bf16_src,
                                bool first_token_scale, hipStream_t stream);
 // Enqueues the decode; with a.ws_skip set, the prefix kernel runs first (prefix_wgs workgroups).
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_dtype,
                          int prefix_wgs, hipStream_t stream);
+// Enqueues multi_kernel and, with more than one partition, the merge.
+hipError_t launch_multi(const MultiArgs& a, int head_dim, int q_dtype, int kv_dtype,
+                        hipStream_t stream);
 // Resident decode workgroups per CU for this kernel instance (0 if the query fails).
 int decode_workgroups_per_cu(int head_dim, int q_dtype, int kv_dtype);
 

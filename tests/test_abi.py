@@ -186,3 +186,72 @@ def test_append_quant_rejects():
         p = list(ptrs)
         p[i] = ctypes.c_void_p(bad)
         assert call(p=p) == pa.PA_ERR_INVALID_ARG, i
+
+
+def _mdesc(**kw):
+    base = dict(num_blocks=64, num_kv_heads=2, head_dim=64, block_size=16, kv_dtype=pa.PA_BF16)
+    cache = {k: kw.pop(k) for k in list(kw) if k in base}
+    base.update(cache)
+    d = dict(batch=4, num_q_heads=8, max_blocks_per_seq=8, max_context_len=0, total_queries=16,
+             max_query_len=4, partition_tokens=0, q_dtype=pa.PA_BF16)
+    d.update(kw)
+    return pa.MultiDesc(pa.CacheDesc(**base), **d)
+
+
+def test_multi_workspace_size():
+    """No workspace with one partition per row tile; with several, per (row, head, partition) an
+    fp32 output row plus max and exp-sum, each array 256-byte aligned."""
+    # 4 x 2 x ceil(4*4/16) = 8 row tiles; 4096 / 8 -> 512 partitions wanted, at most
+    # ceil(8 blocks / 16) = 1 allowed
+    assert pa.pa_decode_multi_workspace_size(_mdesc()) == 0
+    d = _mdesc(partition_tokens=32, max_blocks_per_seq=10)          # 10 blocks -> 5 partitions
+    rows = 16 * 8 * 5
+    assert pa.pa_decode_multi_workspace_size(d) == _r(rows * 64 * 4) + _r(rows * 2 * 4)
+    # automatic: one sequence, one tile, 4096-token table -> partitions of 16 blocks
+    d = _mdesc(batch=1, num_q_heads=2, total_queries=1, max_query_len=1,
+               max_blocks_per_seq=256)
+    rows = 1 * 2 * 16
+    assert pa.pa_decode_multi_workspace_size(d) == _r(rows * 64 * 4) + _r(rows * 2 * 4)
+    assert pa.pa_decode_multi_workspace_size(_mdesc(max_query_len=0)) == 0   # invalid
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(max_query_len=0), pa.PA_ERR_INVALID_ARG),
+    (dict(total_queries=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(batch=0), pa.PA_ERR_INVALID_ARG),
+    (dict(num_q_heads=7), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=48), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=65536 + 32), pa.PA_ERR_INVALID_ARG),
+    (dict(q_dtype=pa.PA_FP8_E4M3), pa.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=80), pa.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=pa.PA_F16), pa.PA_ERR_UNSUPPORTED),
+])
+def test_multi_rejects_descriptor(kw, status):
+    d = _mdesc(**kw)
+    assert pa.lib().pa_decode_multi(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                                    FAKE, 0.125, FAKE, None, 0, None) == status
+
+
+def test_multi_rejects_pointers_and_workspace():
+    lib = pa.lib()
+
+    def call(d, q=FAKE, qs=FAKE, out=FAKE, ks=None, ws=None, nbytes=0):
+        return lib.pa_decode_multi(ctypes.byref(d), q, qs, FAKE, FAKE, ks, ks, FAKE, FAKE, 0.125,
+                                   out, ws, nbytes, None)
+
+    d = _mdesc()
+    assert call(d, qs=None) == pa.PA_ERR_INVALID_ARG
+    assert call(d, q=None) == pa.PA_ERR_INVALID_ARG
+    assert call(d, out=ctypes.c_void_p(0x10008)) == pa.PA_ERR_INVALID_ARG
+    assert call(d, qs=ctypes.c_void_p(0x10002)) == pa.PA_ERR_INVALID_ARG
+    assert call(d, ks=FAKE) == pa.PA_ERR_INVALID_ARG              # scales only for fp8
+    fp8 = _mdesc(kv_dtype=pa.PA_FP8_E4M3)
+    assert call(fp8) == pa.PA_ERR_INVALID_ARG                     # fp8 needs its scales
+    # no rows: nothing to do, q and out may be absent
+    assert call(_mdesc(total_queries=0), q=None, out=None) == pa.PA_OK
+    split = _mdesc(partition_tokens=32, max_blocks_per_seq=10)
+    need = pa.pa_decode_multi_workspace_size(split)
+    assert need > 0
+    assert call(split) == pa.PA_ERR_WORKSPACE
+    assert call(split, ws=FAKE, nbytes=need - 1) == pa.PA_ERR_WORKSPACE
+    assert call(split, ws=ctypes.c_void_p(0x10008), nbytes=need) == pa.PA_ERR_WORKSPACE

@@ -1,0 +1,149 @@
+"""pa_decode_multi against the oracle: several query tokens per sequence, causal over the paged
+cache (speculative verification: youngju.dev guide, speculative-decoding figure; chunked
+prefill: magi page, "Prefill-Decode 分離").
+
+The cases cover draft lengths 1..8 with every group size the row tiling distinguishes (tiles
+holding several tokens, one token, part of a token), prefill chunks of 512, sequences without
+queries or with more queries than cached tokens (rows before the context are zero), fixed key
+partitions from 32 tokens (many partitions merged) to the whole context, fp16, bf16 and fp8
+caches, head_dim 64 and 128; rows that no sequence owns must be left as they were."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_31_amd as pa
+import workloads
+from gpu_util import assert_close, dev_bits, host_bits
+from workloads.generate import Spec
+
+pytestmark = pytest.mark.gpu
+SENTINEL = {"bf16": 0x7FA5, "f16": 0x7E5A}   # NaN payloads no kernel writes
+
+
+class Multi:
+    """A multi-query problem: a seeded paged cache (every context token stored) plus query rows."""
+
+    def __init__(self, q_dtype, kv_dtype, hkv, g, d, lens, T, seed, spare_rows=0):
+        spec = Spec("multi", len(lens), hkv * g, hkv, d, q_dtype, kv_dtype, ("list", tuple(lens)),
+                    pool=("times", 2), seed=seed)
+        self.wl = wl = workloads.make(spec)
+        self.spec = spec
+        self.k, self.v = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new,
+                                          wl.slot_mapping)
+        self.T = np.asarray(T, dtype=np.int64)
+        self.qs = np.concatenate([[0], np.cumsum(self.T)]).astype(np.int32)
+        self.N = int(self.qs[-1]) + spare_rows
+        rng = np.random.default_rng(seed + 1000)
+        self.q = workloads.storage_bits(rng.standard_normal((self.N, hkv * g, d)), q_dtype)
+        self.max_q = max(1, int(self.T.max(initial=0)))
+
+    def run(self, partition_tokens=0, max_query_len=None, max_context_len=0):
+        s, wl = self.spec, self.wl
+        q = dev_bits(self.q, s.q_dtype)
+        out = torch.full_like(q, 0).view(torch.int16).fill_(SENTINEL[s.q_dtype]).view(q.dtype)
+        pa.pa_decode_multi(q, torch.from_numpy(self.qs).cuda(), dev_bits(self.k, s.kv_dtype),
+                           dev_bits(self.v, s.kv_dtype), torch.from_numpy(wl.block_tables).cuda(),
+                           torch.from_numpy(wl.context_lens).cuda(), float(wl.scale), out,
+                           self.max_q if max_query_len is None else max_query_len,
+                           k_scale=None if wl.k_scale is None else torch.from_numpy(wl.k_scale).cuda(),
+                           v_scale=None if wl.v_scale is None else torch.from_numpy(wl.v_scale).cuda(),
+                           max_context_len=max_context_len, partition_tokens=partition_tokens)
+        torch.cuda.synchronize()
+        return host_bits(out)
+
+    def reference(self):
+        s, wl = self.spec, self.wl
+        return oracle.decode_multi(self.q[:self.qs[-1]], self.qs, self.k, self.v, wl.block_tables,
+                                   wl.context_lens, wl.scale, s.q_dtype, s.kv_dtype, wl.k_scale,
+                                   wl.v_scale)
+
+    def check(self, got, label, ref=None):
+        n = int(self.qs[-1])
+        ref = self.reference() if ref is None else ref
+        assert_close(got[:n], ref, self.spec.q_dtype, label)
+        assert np.all(got[n:] == SENTINEL[self.spec.q_dtype]), f"{label}: unowned rows written"
+
+
+LENS = (1, 2, 5, 16, 17, 33, 64, 100, 257, 700, 1023, 2049)
+DRAFT = (1, 2, 5, 4, 8, 3, 0, 8, 7, 4, 6, 5)       # 2 queries with a 1-token context; one empty
+
+VERIFY = [
+    # (q dtype, kv dtype, kv heads, group, head_dim)
+    ("bf16", "bf16", 2, 8, 128),
+    ("bf16", "bf16", 4, 1, 128),
+    ("bf16", "bf16", 2, 4, 64),
+    ("bf16", "bf16", 2, 3, 128),
+    ("bf16", "bf16", 1, 16, 128),
+    ("bf16", "bf16", 1, 32, 64),
+    ("f16", "f16", 2, 8, 128),
+    ("bf16", "fp8_e4m3", 2, 8, 128),
+    ("f16", "fp8_e4m3", 2, 4, 64),
+]
+
+
+@pytest.mark.parametrize("case", VERIFY, ids=lambda c: f"{c[0]}-{c[1]}-kv{c[2]}g{c[3]}d{c[4]}")
+@pytest.mark.parametrize("P", [0, 32, 256])
+def test_speculative_verification(case, P):
+    qd, kvd, hkv, g, d = case
+    m = Multi(qd, kvd, hkv, g, d, LENS, DRAFT, seed=90 + VERIFY.index(case), spare_rows=3)
+    m.check(m.run(partition_tokens=P), f"verify {case} P{P}")
+
+
+@pytest.mark.parametrize("qd,kvd,g,P", [("bf16", "bf16", 4, 0), ("bf16", "bf16", 4, 512),
+                                        ("f16", "f16", 1, 0), ("bf16", "fp8_e4m3", 8, 0)])
+def test_prefill_chunks_of_512(qd, kvd, g, P):
+    """Chunks of 512 tokens: the first chunk of a prompt (the chunk is the whole context), later
+    chunks of long prompts, and a short last chunk."""
+    lens, T = (512, 1100, 2048, 1700), (512, 512, 512, 188)
+    m = Multi(qd, kvd, 2, g, 128, lens, T, seed=100)
+    m.check(m.run(partition_tokens=P), f"prefill g{g} P{P}")
+
+
+def test_more_queries_than_context_and_loose_bounds():
+    """Rows before the context are zero; host bounds larger than needed change nothing."""
+    m = Multi("bf16", "bf16", 2, 4, 128, (3, 1, 40), (6, 4, 2), seed=101, spare_rows=2)
+    ref = m.reference()
+    assert np.all(ref[0:3] == 0) and np.all(ref[6:9] == 0)
+    m.check(m.run(), "tight", ref)
+    m.check(m.run(max_query_len=64, max_context_len=4096), "loose", ref)
+
+
+def test_repeat_runs_bitwise_identical():
+    m = Multi("bf16", "bf16", 2, 8, 128, LENS, DRAFT, seed=102)
+    first = m.run(partition_tokens=64)
+    for _ in range(2):
+        assert np.array_equal(m.run(partition_tokens=64), first)
+
+
+def _sampled(m, rows_per_seq, rng):
+    """Sampled rows against the single-query oracle decode at each row's position (the pinned
+    equivalence of the two), for sizes where the full oracle would be slow."""
+    wl, s = m.wl, m.spec
+    got = m.run()
+    for b in range(s.batch):
+        T, L = int(m.T[b]), int(wl.context_lens[b])
+        if T == 0:
+            continue
+        for i in sorted(set(rng.integers(0, T, size=rows_per_seq).tolist()) | {0, T - 1}):
+            n = int(m.qs[b]) + i
+            ctx = np.array([min(max(L - T + i + 1, 0), L)], dtype=np.int32)
+            ref = oracle.decode(m.q[n][None], m.k, m.v, wl.block_tables[b:b + 1], ctx, wl.scale,
+                                s.q_dtype, s.kv_dtype, wl.k_scale, wl.v_scale)
+            assert_close(got[n][None], ref, s.q_dtype, f"seq {b} row {i}")
+
+
+def test_full_size_verification_batch():
+    """64 sequences of 128..8192 tokens, GQA 64/8, 4 draft tokens each (sampled rows)."""
+    rng = np.random.default_rng(103)
+    lens = rng.integers(128, 8192, size=64, endpoint=True)
+    m = Multi("bf16", "bf16", 8, 8, 128, lens, [4] * 64, seed=103)
+    _sampled(m, 2, rng)
+
+
+def test_full_size_prefill_chunk():
+    """4 prompts whose last 512-token chunk runs against 4096 cached tokens (sampled rows)."""
+    rng = np.random.default_rng(104)
+    m = Multi("bf16", "bf16", 8, 4, 128, [4608] * 4, [512] * 4, seed=104)
+    _sampled(m, 6, rng)
