@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s"
 PEAK_GBS = 8000.0           # MI355X HBM3E
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA
 DEFAULT_WORKLOAD = "mha_b16_h32_d128_f16_l2048"
 
 
@@ -66,15 +67,19 @@ def cpu_baseline(wl, decode_bytes_fn, append_bytes, min_s: float = 10.0,
                       f"float64 on 1 thread; same byte model as the GPU figure"}
 
 
-def traffic_record(workload: str):
-    """HBM bytes per decode call measured with rocprofv3 PMC counters (profiles/), reported
-    only while the kernel sources still hash to what they were when the counters were taken."""
+DECODE_SOURCES = ("decode.hip", "stepper.hpp", "device_common.hpp", "pa_internal.hpp")
+MULTI_SOURCES = ("multi.hip", "stepper.hpp", "device_common.hpp", "pa_internal.hpp")
+
+
+def traffic_record(workload: str, sources=DECODE_SOURCES):
+    """HBM bytes per call measured with rocprofv3 PMC counters (profiles/), reported only while
+    the kernel sources still hash to what they were when the counters were taken."""
     import glob
     import hashlib
     import re
 
     h = hashlib.sha256()
-    for f in ("decode.hip", "device_common.hpp", "pa_internal.hpp"):
+    for f in sources:
         h.update(open(os.path.join(ROOT, "paged_kv_cache_31_amd", "csrc", f), "rb").read())
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
         m = re.search(r"<!-- traffic-record (\{.*?\}) -->", open(path).read())
@@ -101,12 +106,189 @@ def copy_probe(dev) -> int:
     return 0
 
 
+def multi_cpu_baseline(mw, unit_of, min_s: float = 10.0, max_s: float = 25.0) -> dict:
+    """The fp64 oracle, as it stands, on one thread: oracle.decode_multi one sequence at a time
+    over the workload until about min_s seconds have run."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    wl, s = mw.wl, mw.wl.spec
+    amount, seqs = 0.0, 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while True:
+            for b in range(wl.batch):
+                qs = mw.query_start
+                sub = np.array([0, qs[b + 1] - qs[b]], dtype=np.int32)
+                oracle.decode_multi(mw.q[qs[b]:qs[b + 1]], sub, wl.k_cache, wl.v_cache,
+                                    wl.block_tables[b:b + 1], wl.context_lens[b:b + 1], wl.scale,
+                                    s.q_dtype, s.kv_dtype, wl.k_scale, wl.v_scale)
+                amount += unit_of(b)
+                seqs += 1
+                if time.perf_counter() - t0 > max_s:
+                    break
+            secs = time.perf_counter() - t0
+            if secs >= min_s:
+                break
+    return {"value": amount / secs, "cores": 1, "kind": "oracle",
+            "sample": f"{seqs} sequences' multi-query attention ({seqs / wl.batch:.2f} passes "
+                      f"over the batch) in {secs:.1f} s, numpy float64 on 1 thread; same "
+                      f"byte/flop model as the GPU figure"}
+
+
+def bench_multi(args, dev) -> int:
+    """Several query tokens per sequence: one step = pa_kv_append of the new tokens +
+    pa_decode_multi.  HBM-bound shapes report GB/s, MFMA-bound ones TFLOP/s."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_31_amd as pa
+    import workloads
+
+    t0 = time.perf_counter()
+    mw = workloads.make_multi(args.workload)
+    wl, s = mw.wl, mw.wl.spec
+    B, Hq, Hkv, D = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim
+    N, maxT = int(mw.query_start[-1]), int(mw.query_lens.max())
+    log(f"workload {args.workload}: generated in {time.perf_counter() - t0:.1f} s")
+    nbytes = workloads.multi_bytes(wl.context_lens, mw.query_lens, Hq, Hkv, D, s.q_dtype,
+                                   s.kv_dtype)
+    flops = workloads.multi_flops(wl.context_lens, mw.query_lens, Hq, D)
+    bytes_append = workloads.append_bytes(N, Hkv, D, s.kv_dtype)
+    mfma = flops / nbytes > PEAK_TFLOPS[s.q_dtype] * 1e12 / (PEAK_GBS * 1e9)
+    pool_bytes = wl.k_cache.nbytes + wl.v_cache.nbytes
+    R = args.rotations or max(2, math.ceil(2 * 2**30 / nbytes))
+    R = max(1, min(R, 64, int(48 * 2**30 // pool_bytes)))
+
+    def to_dev(bits, dtype):
+        a = np.ascontiguousarray(bits)
+        if dtype == "fp8_e4m3":
+            return torch.from_numpy(a).to(dev)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+        return torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
+
+    base = {"q": to_dev(mw.q, s.q_dtype), "k": to_dev(wl.k_cache, s.kv_dtype),
+            "v": to_dev(wl.v_cache, s.kv_dtype), "k_new": to_dev(mw.k_new, s.kv_dtype),
+            "v_new": to_dev(mw.v_new, s.kv_dtype)}
+    qs = torch.from_numpy(mw.query_start).to(dev)
+    slots = torch.from_numpy(mw.slot_mapping).to(dev)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    lens = torch.from_numpy(wl.context_lens).to(dev)
+    k_scale = None if wl.k_scale is None else torch.from_numpy(wl.k_scale).to(dev)
+    v_scale = None if wl.v_scale is None else torch.from_numpy(wl.v_scale).to(dev)
+    rots = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(R - 1)]
+    for r in rots:
+        r["out"] = torch.empty_like(r["q"])
+    P = args.partition or 0
+    desc = pa.multi_desc(base["q"], base["k"], tables, maxT, wl.max_context_len, P)
+    ws_bytes = pa.pa_decode_multi_workspace_size(desc)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"uploaded: {R} pool copies of {pool_bytes / 2**30:.2f} GiB; workspace {ws_bytes} B")
+
+    appends = [pa.AppendCall(x["k_new"], x["v_new"], slots, x["k"], x["v"]) for x in rots]
+    calls = [pa.MultiCall(x["q"], qs, x["k"], x["v"], tables, lens, float(wl.scale), x["out"],
+                          maxT, k_scale=k_scale, v_scale=v_scale,
+                          max_context_len=wl.max_context_len, partition_tokens=P,
+                          workspace=workspace)
+             for x in rots]
+
+    def step(r):
+        appends[r]()
+        calls[r]()
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % R)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        calls[i % R]()
+    e1.record()
+    torch.cuda.synchronize()
+    launch_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    log(f"{args.steps} back-to-back pa_decode_multi calls: {launch_s * 1e6:.1f} us each")
+
+    kernel = "multi_kernel+multi_merge_kernel" if ws_bytes > 0 else "multi_kernel"
+    step_s = ms_per_step / 1e3
+    if mfma:
+        peak, unit = PEAK_TFLOPS[s.q_dtype], "TFLOP/s"
+        metric = "paged multi-query attention (chunked prefill): achieved TFLOP/s"
+        value = flops / step_s / 1e12
+        achieved = flops / launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic_record(args.workload,
+                                                                              MULTI_SOURCES),
+                "kernel": kernel, "flops_per_launch": flops,
+                "duration_us": round(launch_s * 1e6, 2)}
+    else:
+        unit = "GB/s"
+        metric = "paged multi-query attention (speculative verification): achieved HBM GB/s"
+        value = (nbytes + bytes_append) / step_s / 1e9
+        achieved = nbytes / launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS, "unit": unit,
+                "frac": round(achieved / PEAK_GBS, 4),
+                "traffic": traffic_record(args.workload, MULTI_SOURCES), "kernel": kernel,
+                "bytes_per_launch": nbytes, "duration_us": round(launch_s * 1e6, 2)}
+    result = {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": s.kv_dtype if s.kv_dtype == s.q_dtype else f"{s.q_dtype}+{s.kv_dtype}",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_dim": D, "block_size": 16, "q_dtype": s.q_dtype, "kv_dtype": s.kv_dtype,
+            "query_tokens": N, "max_query_len": maxT,
+            "context_len_min": int(wl.context_lens.min()),
+            "context_len_max": int(wl.context_lens.max()),
+            "partition_tokens": P or "auto", "rotations": R,
+            "step": "pa_kv_append (the new tokens) + pa_decode_multi",
+        },
+        "query_tokens_per_s": round(N / launch_s, 1),
+        "us_per_call": round(launch_s * 1e6, 2),
+        "bytes_per_call": nbytes, "flops_per_call": flops,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu_baseline)")
+        if mfma:
+            def unit_of(b):
+                return workloads.multi_flops(wl.context_lens[b:b + 1], mw.query_lens[b:b + 1],
+                                             Hq, D) / 1e12
+        else:
+            def unit_of(b):
+                return workloads.multi_bytes(wl.context_lens[b:b + 1], mw.query_lens[b:b + 1],
+                                             Hq, Hkv, D, s.q_dtype, s.kv_dtype) / 1e9
+        cb = multi_cpu_baseline(mw, unit_of)
+        cb["value"] = round(cb["value"], 6)
+        cb["unit"] = unit
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="a single-query workload (default) or a multi-query one: "
+                         "verify_b64_h64kv8_d128_bf16_l128to8192_t4, "
+                         "prefill_b4_h32kv8_d128_bf16_l4608_chunk512")
     ap.add_argument("--partition", type=int, default=None,
                     help="key-partition tokens (default: the workload's, else the library's)")
     ap.add_argument("--rotations", type=int, default=0, help="pool copies cycled (0: auto)")
@@ -137,6 +319,8 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(dev)
     pa.lib()
+    if args.workload in workloads.MULTI_SPECS:
+        return bench_multi(args, dev)
 
     t0 = time.perf_counter()
     wl = workloads.make(args.workload, poison=False)

@@ -44,3 +44,20 @@ def test_decode_bytes_counts_each_part():
     expect8 = 33 * 2 * 8 * 1 * 2 + 3 * 2 * 4 * 2 + 2 * 2 * 4 * 8 * 2 + 3 * 4 + 8
     assert W.decode_bytes(lens, 4, 2, 8, "bf16", "fp8_e4m3") == expect8
     assert W.append_bytes(2, 2, 8, "bf16") == 2 * (2 * 32 * 2 + 8)
+
+
+def test_multi_query_counts():
+    """Visible keys counted one row at a time, and the multi-query bytes part by part."""
+    lens, T = np.array([16, 17, 3]), np.array([4, 1, 5])
+    brute = 0
+    for L, t in zip(lens, T):
+        for i in range(t):
+            brute += sum(1 for key in range(L) if key <= L - t + i)
+    assert W.visible_keys(lens, T) == brute == (13 + 14 + 15 + 16) + 17 + (0 + 0 + 1 + 2 + 3)
+    assert W.multi_flops(lens, T, 4, 8) == 4 * 8 * 4 * brute
+    # K+V once per sequence; q+out per row (10 rows); tables; query starts (B + 1)
+    expect = 36 * 2 * 8 * 2 * 2 + 2 * 10 * 4 * 8 * 2 + (1 + 2 + 1) * 4 + 3 * 4 + 4 * 4
+    assert W.multi_bytes(lens, T, 4, 2, 8, "bf16", "bf16") == expect
+    # one query per sequence: the single-query decode's bytes plus the query start offsets
+    assert (W.multi_bytes(lens, [1, 1, 1], 4, 2, 8, "bf16", "fp8_e4m3")
+            == W.decode_bytes(lens, 4, 2, 8, "bf16", "fp8_e4m3") + 16)

@@ -10,7 +10,8 @@ Cache layout used by every producer and consumer (one (block, kv_head) tile each
   V pool  [num_blocks][num_kv_heads][head_dim][16]   dim-major tile
 """
 
-from .generate import SPECS, Workload, make, spec_names, storage_bits  # noqa: F401
+from .generate import (MULTI_SPECS, SPECS, MultiWorkload, Workload, make,  # noqa: F401
+                       make_multi, spec_names, storage_bits)
 from .sizing import (  # noqa: F401
     BLOCK_SIZE,
     append_bytes,
@@ -19,5 +20,8 @@ from .sizing import (  # noqa: F401
     m_alloc,
     m_block,
     m_waste,
+    multi_bytes,
+    multi_flops,
     n_blocks,
+    visible_keys,
 )

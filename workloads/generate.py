@@ -305,3 +305,51 @@ def make(spec: Spec | str, seed: int | None = None, poison: bool = True,
         scale=np.float32(1.0 / math.sqrt(D)),
         sharing=sharing, prefix_blocks=prefix_blocks, unique_tokens=unique_tokens,
     )
+
+
+# Several query tokens per sequence: (cache workload, new query tokens per sequence).
+MULTI_SPECS: dict[str, tuple[Spec, int]] = {
+    # Speculative verification: the GQA serving batch checks 4 draft tokens per sequence.
+    "verify_b64_h64kv8_d128_bf16_l128to8192_t4": (
+        Spec("verify_b64_h64kv8_d128_bf16_l128to8192_t4", 64, 64, 8, 128, "bf16", "bf16",
+             ("uniform", 128, 8192), seed=2), 4),
+    # Chunked prefill: 4 prompts whose next 512-token chunk runs against 4096 cached tokens.
+    "prefill_b4_h32kv8_d128_bf16_l4608_chunk512": (
+        Spec("prefill_b4_h32kv8_d128_bf16_l4608_chunk512", 4, 32, 8, 128, "bf16", "bf16",
+             ("fixed", 4608), seed=6), 512),
+}
+
+
+@dataclasses.dataclass
+class MultiWorkload:
+    wl: Workload                # the cache: context_lens count the new tokens too
+    query_lens: np.ndarray      # [B] int32
+    query_start: np.ndarray     # [B + 1] int32
+    q: np.ndarray               # [N][Hq][D] raw bits of q_dtype
+    slot_mapping: np.ndarray    # [N] int64: cache slot of each new token
+    k_new: np.ndarray           # [N][Hkv][D] raw bits: the new tokens' K/V as stored
+    v_new: np.ndarray
+
+
+def make_multi(name: str, poison: bool = False) -> MultiWorkload:
+    """A multi-query workload: every one of the context_lens tokens already in the cache, the
+    last T of each sequence being the new ones; their rows (for an append) and N(0,1) queries."""
+    spec, T = MULTI_SPECS[name]
+    wl = make(spec, poison=False)
+    B, Hq, D = spec.batch, spec.num_q_heads, spec.head_dim
+    lens = wl.context_lens.astype(np.int64)
+    qlens = np.minimum(lens, T).astype(np.int32)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    N = int(qs[-1])
+    slots = np.empty(N, dtype=np.int64)
+    for b in range(B):
+        pos = lens[b] - qlens[b] + np.arange(qlens[b])
+        slots[qs[b]:qs[b + 1]] = wl.block_tables[b, pos // BLOCK_SIZE].astype(np.int64) * \
+            BLOCK_SIZE + pos % BLOCK_SIZE
+    blk, off = slots // BLOCK_SIZE, slots % BLOCK_SIZE
+    k_new = np.ascontiguousarray(wl.k_cache[blk, :, off, :])
+    v_new = np.ascontiguousarray(wl.v_cache[blk, :, :, off])
+    g = torch.Generator().manual_seed(_derive(wl.seed, 4))
+    q = storage_bits(torch.randn((N, Hq, D), generator=g, dtype=torch.float32), spec.q_dtype)
+    return MultiWorkload(wl=wl, query_lens=qlens, query_start=qs, q=q, slot_mapping=slots,
+                         k_new=k_new, v_new=v_new)

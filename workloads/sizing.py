@@ -68,3 +68,32 @@ def append_bytes(num_tokens: int, num_kv_heads: int, head_dim: int, kv_dtype: st
     """Bytes of one append: read the new K and V rows, write them into the cache, read slots."""
     row = num_kv_heads * head_dim * ELEM_BYTES[kv_dtype]
     return num_tokens * (2 * row * 2 + 8)
+
+
+def visible_keys(context_lens, query_lens) -> int:
+    """Keys seen summed over query rows: row i of a sequence with L cached tokens, the last T of
+    them new, sees min(max(L - T + i + 1, 0), L) of them (causal over the cache)."""
+    total = 0
+    for L, T in zip(np.asarray(context_lens, dtype=np.int64), np.asarray(query_lens, dtype=np.int64)):
+        i = np.arange(int(T))
+        total += int(np.clip(L - T + i + 1, 0, L).sum())
+    return total
+
+
+def multi_bytes(context_lens, query_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                q_dtype: str, kv_dtype: str) -> int:
+    """Algorithmic HBM bytes of one multi-query call: every K/V element of each sequence once
+    (however many rows see it), the fp8 block scales, every query and output row once, the
+    block-table entries and the query start offsets."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    rows = int(np.asarray(query_lens, dtype=np.int64).sum())
+    e_q = ELEM_BYTES[q_dtype]
+    single = decode_bytes(lens, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype)
+    single -= 2 * len(lens) * num_q_heads * head_dim * e_q
+    return single + 2 * rows * num_q_heads * head_dim * e_q + 4 * (len(lens) + 1)
+
+
+def multi_flops(context_lens, query_lens, num_q_heads: int, head_dim: int) -> int:
+    """Algorithmic flops of one multi-query call: per query head and visible key, a head_dim dot
+    product for the score and a head_dim multiply-add into the output (2 * 2 * head_dim)."""
+    return 4 * head_dim * num_q_heads * visible_keys(context_lens, query_lens)
