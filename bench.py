@@ -280,6 +280,61 @@ def bench_multi(args, dev) -> int:
     return 0
 
 
+def graph_timing(args, rots, tables, lens, scale, k_scale, v_scale, mcl, P, share, ws_bytes,
+                 dev) -> dict:
+    """A step of K layers (pa_decode_append on K pool copies, one per layer) timed eagerly and
+    as one HIP graph replay, both on one non-default stream, synchronised around `steps` steps."""
+    import torch
+
+    import paged_kv_cache_31_amd as pa
+
+    K = args.graph_layers
+    stream = torch.cuda.Stream(device=dev)
+    calls = [pa.DecodeCall(x["q"], x["k"], x["v"], tables, lens, scale, x["out"],
+                           k_scale=k_scale, v_scale=v_scale, max_context_len=mcl,
+                           partition_tokens=P, shared_prefixes=share, k_new=x["k_new"],
+                           v_new=x["v_new"], stream=stream,
+                           workspace=pa.new_workspace(ws_bytes, dev))
+             for x in rots[:K]]
+
+    def eager():
+        for c in calls:
+            c()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        stream.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        stream.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / args.steps
+
+    def unprepared():
+        # the convenience function: descriptor, checks and argument marshalling on every call
+        for x in rots[:K]:
+            pa.pa_decode_append(x["q"], x["k_new"], x["v_new"], x["k"], x["v"], tables, lens,
+                                scale, x["out"], k_scale=k_scale, v_scale=v_scale,
+                                max_context_len=mcl, partition_tokens=P, workspace=ws0,
+                                stream=stream, shared_prefixes=share)
+
+    ws0 = pa.new_workspace(ws_bytes, dev)
+    eager()
+    stream.synchronize()
+    graph = pa.StepGraph(calls, stream)
+    t_eager = timed(eager)
+    t_unprep = timed(unprepared)
+    t_graph = timed(graph)
+    launches = K * (2 if share else 1)
+    log(f"{K}-layer step: eager {t_eager:.1f} us, unprepared {t_unprep:.1f} us, "
+        f"graph {t_graph:.1f} us")
+    return {"layers": K, "eager_us_per_step": round(t_eager, 2),
+            "eager_unprepared_us_per_step": round(t_unprep, 2),
+            "graph_us_per_step": round(t_graph, 2), "kernel_launches_per_step": launches,
+            "us_saved_per_launch": round((t_eager - t_graph) / launches, 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +351,9 @@ def main() -> int:
                     help="time a step as pa_kv_append + pa_decode instead of pa_decode_append")
     ap.add_argument("--no-shared-prefixes", action="store_true",
                     help="decode a workload with a shared prefix without the prefix plan")
+    ap.add_argument("--graph-layers", type=int, default=0,
+                    help="also time a step of this many layers (one pool copy each) eagerly "
+                         "and as one HIP graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -337,6 +395,8 @@ def main() -> int:
     pool_bytes = wl.k_cache.nbytes + wl.v_cache.nbytes
     R = args.rotations or max(2, math.ceil(2 * 2**30 / bytes_decode))
     R = max(1, min(R, 64, int(48 * 2**30 // pool_bytes)))
+    if args.graph_layers:
+        R = max(R, args.graph_layers)
 
     def to_dev(bits, dtype):
         a = np.ascontiguousarray(bits)
@@ -457,6 +517,9 @@ def main() -> int:
                      "kernel": kernel, "bytes_per_launch": bytes_decode,
                      "duration_us": round(launch_s * 1e6, 2)},
     }
+    if args.graph_layers:
+        result["graph"] = graph_timing(args, rots, tables, lens, scale, k_scale, v_scale, mcl, P,
+                                       share, ws_bytes, dev)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(wl, dbytes, bytes_append)

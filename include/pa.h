@@ -271,6 +271,31 @@ const char* pa_status_string(pa_status status);
 /* The hipError_t of the last failed launch on the calling thread (0 if none). */
 int32_t pa_last_hip_error(void);
 
+/*
+ * HIP graphs of whole steps: launching one kernel per layer and call costs a few microseconds
+ * each, which a decode step of many layers pays again and again (design.babushkai.com
+ * "GPU推論の内部構造": the per-launch overhead of decode and CUDA graphs as its remedy).  Every
+ * entry point above only enqueues kernels on the given stream (no allocation, no memset, no
+ * synchronisation), so a step made of any sequence of them, for example pa_decode_append for
+ * every layer, can be captured once and replayed with one launch.
+ *
+ * pa_graph_begin  starts capturing the calls made on `stream` (not the null stream) by this
+ *                 thread (hipStreamCaptureModeThreadLocal).  Call each entry point once outside
+ *                 the capture first on this device, so that its one-time device queries are done.
+ * pa_graph_end    ends the capture and instantiates the graph into *graph (NULL on failure).
+ * pa_graph_launch replays the captured step on `stream` with the pointers, sizes and scalars
+ *                 it was captured with; the buffers they point to are read and written afresh
+ *                 each time, so updating the data in place between replays is how a later step
+ *                 runs (new tokens, queries, lengths and tables in the same buffers).
+ * pa_graph_destroy frees the graph (NULL: no-op).
+ * A failure of a HIP call returns PA_ERR_HIP (see pa_last_hip_error).
+ */
+typedef struct pa_graph pa_graph;
+pa_status pa_graph_begin(void* stream);
+pa_status pa_graph_end(void* stream, pa_graph** graph);
+pa_status pa_graph_launch(const pa_graph* graph, void* stream);
+pa_status pa_graph_destroy(pa_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

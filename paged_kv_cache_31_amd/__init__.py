@@ -63,6 +63,7 @@ _lock = threading.Lock()
 
 EXPORTS = ("pa_kv_append", "pa_kv_append_quant", "pa_decode", "pa_decode_append",
            "pa_decode_workspace_size", "pa_decode_multi", "pa_decode_multi_workspace_size",
+           "pa_graph_begin", "pa_graph_end", "pa_graph_launch", "pa_graph_destroy",
            "pa_status_string", "pa_last_hip_error")
 
 
@@ -93,6 +94,14 @@ def lib() -> ctypes.CDLL:
             L.pa_decode_multi.restype = i32
             L.pa_decode_multi_workspace_size.argtypes = [ctypes.POINTER(MultiDesc)]
             L.pa_decode_multi_workspace_size.restype = sz
+            L.pa_graph_begin.argtypes = [vp]
+            L.pa_graph_begin.restype = i32
+            L.pa_graph_end.argtypes = [vp, ctypes.POINTER(vp)]
+            L.pa_graph_end.restype = i32
+            L.pa_graph_launch.argtypes = [vp, vp]
+            L.pa_graph_launch.restype = i32
+            L.pa_graph_destroy.argtypes = [vp]
+            L.pa_graph_destroy.restype = i32
             L.pa_status_string.argtypes = [i32]
             L.pa_status_string.restype = ctypes.c_char_p
             L.pa_last_hip_error.argtypes = []
@@ -340,3 +349,37 @@ def pa_decode_multi(q, query_start, k_cache, v_cache, block_tables, context_lens
               max_query_len, k_scale, v_scale, max_context_len, partition_tokens, workspace,
               stream)()
     return out
+
+
+class StepGraph:
+    """A step made of prepared calls (AppendCall, DecodeCall, MultiCall, ...), captured once into
+    a HIP graph (pa_graph_begin / pa_graph_end) and replayed with one launch per call of the
+    object.  Every call must have been made with `stream` (a non-default torch stream) and run
+    once outside the capture first.  Replays read and write the same buffers: update their data
+    in place between replays."""
+
+    def __init__(self, calls, stream):
+        assert stream is not None and stream.cuda_stream != 0, "capture needs its own stream"
+        L = lib()
+        self._lib, self._calls = L, list(calls)
+        self._stream = ctypes.c_void_p(stream.cuda_stream)
+        _check("pa_graph_begin", L.pa_graph_begin(self._stream))
+        graph = ctypes.c_void_p()
+        try:
+            for c in self._calls:
+                c()
+        finally:
+            st = L.pa_graph_end(self._stream, ctypes.byref(graph))
+        _check("pa_graph_end", st)
+        self._graph = graph
+
+    def __call__(self) -> None:
+        st = self._lib.pa_graph_launch(self._graph, self._stream)
+        if st != PA_OK:
+            _check("pa_graph_launch", st)
+
+    def __del__(self):
+        g = getattr(self, "_graph", None)
+        if g is not None and g.value:
+            self._lib.pa_graph_destroy(g)
+            self._graph = None

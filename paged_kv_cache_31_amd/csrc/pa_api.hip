@@ -430,3 +430,60 @@ PA_EXPORT pa_status pa_decode_append(const pa_decode_desc* desc, const void* q,
   return decode_impl(desc, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
                      context_lens, scale, out, workspace, workspace_bytes, stream);
 }
+
+// ---- HIP graphs of whole steps.  The entry points above enqueue kernels only (no allocation,
+// no memset, no synchronisation), so a step of several of them can be captured once and
+// replayed with a single launch.
+struct pa_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+PA_EXPORT pa_status pa_graph_begin(void* stream) {
+  if (!stream) return PA_ERR_INVALID_ARG;   // the legacy null stream cannot be captured
+  const hipError_t e = hipStreamBeginCapture(static_cast<hipStream_t>(stream),
+                                             hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_graph_end(void* stream, pa_graph** graph) {
+  if (!stream || !graph) return PA_ERR_INVALID_ARG;
+  *graph = nullptr;
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(static_cast<hipStream_t>(stream), &g);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(g);
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  *graph = new pa_graph{g, x};
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_graph_launch(const pa_graph* graph, void* stream) {
+  if (!graph) return PA_ERR_INVALID_ARG;
+  const hipError_t e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_graph_destroy(pa_graph* graph) {
+  if (!graph) return PA_OK;
+  hipGraphExecDestroy(graph->exec);
+  hipGraphDestroy(graph->graph);
+  delete graph;
+  return PA_OK;
+}

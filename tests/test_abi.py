@@ -255,3 +255,13 @@ def test_multi_rejects_pointers_and_workspace():
     assert call(split) == pa.PA_ERR_WORKSPACE
     assert call(split, ws=FAKE, nbytes=need - 1) == pa.PA_ERR_WORKSPACE
     assert call(split, ws=ctypes.c_void_p(0x10008), nbytes=need) == pa.PA_ERR_WORKSPACE
+
+
+def test_graph_rejects():
+    lib = pa.lib()
+    g = ctypes.c_void_p()
+    assert lib.pa_graph_begin(None) == pa.PA_ERR_INVALID_ARG       # the null stream
+    assert lib.pa_graph_end(None, ctypes.byref(g)) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_graph_end(FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_graph_launch(None, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_graph_destroy(None) == pa.PA_OK
