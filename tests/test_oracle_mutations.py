@@ -1,5 +1,7 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that its pins catch each one."""
 
+import os
+
 import numpy as np
 import pytest
 
@@ -243,4 +245,79 @@ def test_multi_pins_catch_planted_mistake(name, monkeypatch):
 def test_multi_unmutated_copy_passes(monkeypatch):
     monkeypatch.setattr(M.oracle, "decode_multi", _multi_with())
     for pin in MULTI_PINS:
+        pin()
+
+
+# ---- block sharing: planted mistakes in the copy and in the reference-count model.
+import oracle.blocks as OB  # noqa: E402
+import test_oracle_blocks as TB  # noqa: E402
+
+_orig_copy = OB.copy_blocks
+
+
+def copy_without_v(k_cache, v_cache, k_scale, v_scale, pairs):
+    k, _, ks, vs = _orig_copy(k_cache, v_cache, k_scale, v_scale, pairs)
+    return k, v_cache.copy(), ks, vs
+
+
+def copy_without_scales(k_cache, v_cache, k_scale, v_scale, pairs):
+    k, v, _, _ = _orig_copy(k_cache, v_cache, k_scale, v_scale, pairs)
+    return k, v, None if k_scale is None else k_scale.copy(), None if v_scale is None else v_scale.copy()
+
+
+def copy_reversed(k_cache, v_cache, k_scale, v_scale, pairs):
+    return _orig_copy(k_cache, v_cache, k_scale, v_scale,
+                      [(d, s) for s, d in np.asarray(pairs).reshape(-1, 2)])
+
+
+class WriteKeepsOldReference(OB.BlockPoolModel):
+    def write(self, block, new_block):
+        if self.ref[block] == 1:
+            assert new_block == block
+            return False
+        self.ref[new_block] = 1                        # mistake: the shared block keeps its count
+        return True
+
+
+class ReleaseIgnoresCounts(OB.BlockPoolModel):
+    def release(self, ids):
+        for i in ids:                                  # mistake: any release frees the block
+            assert self.ref[int(i)] >= 1
+            self.ref[int(i)] = 0
+
+
+BLOCK_MUTATIONS = {
+    "copy: V not copied": ("copy_blocks", copy_without_v),
+    "copy: fp8 scales not copied": ("copy_blocks", copy_without_scales),
+    "copy: source and target swapped": ("copy_blocks", copy_reversed),
+    "model: copy-on-write keeps the old reference": ("BlockPoolModel", WriteKeepsOldReference),
+    "model: release frees a still-shared block": ("BlockPoolModel", ReleaseIgnoresCounts),
+}
+
+BLOCK_PINS = [
+    lambda: TB.test_copy_matches_flat_address_loops(True),
+    lambda: TB.test_decode_through_the_copies_is_unchanged("bf16"),
+    TB.test_parallel_sampling_fork_and_copy_on_write,
+    lambda: TB.test_lifecycle_of_the_100_token_example(
+        os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")),
+    TB.test_model_refuses_what_the_pages_rule_out,
+]
+
+
+@pytest.mark.parametrize("name", list(BLOCK_MUTATIONS))
+def test_block_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = BLOCK_MUTATIONS[name]
+    monkeypatch.setattr(OB, attr, fn)
+    monkeypatch.setattr(TB.oracle, attr, fn)
+    caught = 0
+    for pin in BLOCK_PINS:
+        try:
+            pin()
+        except (AssertionError, pytest.fail.Exception):   # a refusal that did not happen
+            caught += 1
+    assert caught >= 1, f"no pin caught: {name}"
+
+
+def test_block_pins_pass_unmutated():
+    for pin in BLOCK_PINS:
         pin()
