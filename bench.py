@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s"
 PEAK_GBS = 8000.0           # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA
+BLOCK_TOKENS = 16
 DEFAULT_WORKLOAD = "mha_b16_h32_d128_f16_l2048"
 
 
@@ -335,6 +336,103 @@ def graph_timing(args, rots, tables, lens, scale, k_scale, v_scale, mcl, P, shar
             "us_saved_per_launch": round((t_eager - t_graph) / launches, 3)}
 
 
+def bench_copy(args, dev) -> int:
+    """Copy-on-write copies: pa_copy_blocks of N random (source, target) pairs over the
+    workload's pool (targets distinct and never sources), HBM-bound: each pair reads and writes
+    the K and V tiles of every KV head.  Also times the host pool's pa_pool_slot_for."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_31_amd as pa
+    import workloads
+
+    wl = workloads.make(args.workload, poison=False)
+    s = wl.spec
+    Hkv, D = s.num_kv_heads, s.head_dim
+    e = 1 if s.kv_dtype == "fp8_e4m3" else 2
+    NB = wl.num_blocks
+    n = min(args.cow_pairs, NB // 2)
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(NB)
+    pairs_np = np.stack([perm[:n], perm[n:2 * n]], axis=1).astype(np.int32)
+    tile = BLOCK_TOKENS * D * e
+    nbytes = n * Hkv * (2 * 2 * tile + (16 if e == 1 else 0)) + n * 8
+
+    def to_dev(bits, dtype):
+        a = np.ascontiguousarray(bits)
+        if dtype == "fp8_e4m3":
+            return torch.from_numpy(a).to(dev)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+        return torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
+
+    k, v = to_dev(wl.k_cache, s.kv_dtype), to_dev(wl.v_cache, s.kv_dtype)
+    ks = None if wl.k_scale is None else torch.from_numpy(wl.k_scale).to(dev)
+    vs = None if wl.v_scale is None else torch.from_numpy(wl.v_scale).to(dev)
+    pairs = torch.from_numpy(pairs_np).to(dev)
+    for _ in range(args.warmup):
+        pa.pa_copy_blocks(pairs, k, v, ks, vs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        pa.pa_copy_blocks(pairs, k, v, ks, vs)
+    e1.record()
+    torch.cuda.synchronize()
+    launch_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    achieved = nbytes / launch_s / 1e9
+    log(f"pa_copy_blocks of {n} pairs: {launch_s * 1e6:.1f} us, {achieved:.0f} GB/s")
+
+    # host bookkeeping: a decode step of 256 sequences, each forked once, every sequence asks
+    # for the slot of its next token (a copy for the first writer of each shared block)
+    pool = pa.BlockPool(1 << 16)
+    tables, lens = [], []
+    for i in range(128):
+        t = pool.alloc(8)
+        tables += [t, list(t)]
+        pool.share(t)
+        lens += [8 * 16 - 5, 8 * 16 - 5]
+    t0 = time.perf_counter()
+    calls = 0
+    while time.perf_counter() - t0 < 0.5:
+        for b in range(len(tables)):
+            pool.slot_for(tables[b], lens[b], 64)
+            lens[b] += 1
+            calls += 1
+    host_rate = calls / (time.perf_counter() - t0)
+
+    result = {
+        "metric": "copy-on-write block copy: achieved HBM GB/s", "value": round(achieved, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(launch_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8" if e == 1 else "u16", "data": "synthetic",
+        "config": {"workload": f"copy_blocks_{n}pairs_{args.workload}", "pairs": n,
+                   "num_kv_heads": Hkv, "head_dim": D, "kv_dtype": s.kv_dtype,
+                   "num_blocks": NB},
+        "us_per_call": round(launch_s * 1e6, 2),
+        "host_slot_for_calls_per_s": round(host_rate, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "kernel": "copy_blocks_kernel", "bytes_per_launch": nbytes,
+                     "duration_us": round(launch_s * 1e6, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        done = 0
+        sub = max(1, n // 16)
+        while time.perf_counter() - t0 < 10.0:
+            oracle.copy_blocks(wl.k_cache, wl.v_cache, wl.k_scale, wl.v_scale, pairs_np[:sub])
+            done += sub
+        secs = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(done / n * nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle.copy_blocks of {done} pairs in batches of {sub} in {secs:.1f} s "
+                      f"(each call copies the whole pool first, as the oracle returns new arrays)"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,6 +452,9 @@ def main() -> int:
     ap.add_argument("--graph-layers", type=int, default=0,
                     help="also time a step of this many layers (one pool copy each) eagerly "
                          "and as one HIP graph replay")
+    ap.add_argument("--cow-pairs", type=int, default=0,
+                    help="instead: time pa_copy_blocks of this many (source, target) block pairs "
+                         "on the workload's pool, and the host pool's slot bookkeeping")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -379,6 +480,8 @@ def main() -> int:
     pa.lib()
     if args.workload in workloads.MULTI_SPECS:
         return bench_multi(args, dev)
+    if args.cow_pairs:
+        return bench_copy(args, dev)
 
     t0 = time.perf_counter()
     wl = workloads.make(args.workload, poison=False)

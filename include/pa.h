@@ -27,9 +27,11 @@
  *
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  *
- * Ownership and execution: every data pointer is a device pointer owned by the caller.  The
- * library never allocates or frees memory; its only state is a thread-local copy of the last HIP
- * error and a per-device cache of the compute-unit count and kernel occupancy.  Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream)
+ * Ownership and execution: every data pointer of the attention and cache calls is a device
+ * pointer owned by the caller, and the library never allocates or frees device memory.  Its own
+ * state is a thread-local copy of the last HIP error, a per-device cache of the compute-unit
+ * count and kernel occupancy, and the host objects the caller creates and destroys explicitly
+ * (pa_block_pool, pa_graph).  Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream)
  * and return without synchronising; the caller orders and synchronises.
  *
  * Errors: conditions the host can see (null pointers, non-positive sizes, unsupported shapes or
@@ -56,7 +58,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misaligned pointer */
   PA_ERR_UNSUPPORTED = 2,  /* head_dim, block_size, head grouping or dtype pair not implemented */
   PA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than pa_decode_workspace_size() */
-  PA_ERR_HIP = 4           /* a kernel launch failed; pa_last_hip_error() has the hipError_t */
+  PA_ERR_HIP = 4,          /* a kernel launch failed; pa_last_hip_error() has the hipError_t */
+  PA_ERR_OUT_OF_BLOCKS = 5 /* the block pool has too few free blocks (nothing was changed) */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -270,6 +273,62 @@ const char* pa_status_string(pa_status status);
 
 /* The hipError_t of the last failed launch on the calling thread (0 if none). */
 int32_t pa_last_hip_error(void);
+
+/*
+ * Block sharing and copy-on-write (kasblo.com vLLM explainer, "blockはrequestの成長に合わせて
+ * 割り当てる" and "block共有とAutomatic Prefix Caching"): a request takes blocks from a pool of
+ * reusable physical blocks as it grows and gives back, when it ends, the blocks only it uses;
+ * every block has a reference count (the sequences referring to it), so that sequences forked
+ * for parallel sampling or sharing a prefix hold its content once, and a shared block is
+ * duplicated only when one of them writes into it.
+ *
+ * pa_block_pool is a host-side object (one per cache; thread-safe).  A block is free when its
+ * count is 0.  Every call validates all its arguments before changing anything; PA_ERR_INVALID_ARG
+ * (bad id, sharing or writing a free block, releasing a block more often than it is referred to)
+ * and PA_ERR_OUT_OF_BLOCKS (the pool is short: the caller's scheduler preempts) leave the pool
+ * unchanged.  Which free block an allocation returns is unspecified (the most recently freed
+ * first).
+ *
+ * pa_pool_create     a pool of num_blocks free blocks (> 0) in *pool.
+ * pa_pool_destroy    frees the pool (NULL: no-op).
+ * pa_pool_free_blocks, pa_pool_refcount   the free count / a block's count (-1: bad argument).
+ * pa_pool_alloc      n blocks, each now referred to once, into blocks[n]; all or nothing.
+ * pa_pool_share      one more reference to each listed block (all must be in use): a fork, a
+ *                    reused prefix.
+ * pa_pool_release    one reference fewer per listed occurrence; a block reaching 0 is free again.
+ * pa_pool_write      before writing into `block`: if it is referred to once, *target = block and
+ *                    *needs_copy = 0; otherwise the caller's reference moves to a newly allocated
+ *                    block *target (count 1), *needs_copy = 1, and the caller must copy block's
+ *                    content into it (pa_copy_blocks) before writing.
+ * pa_pool_slot_for   the slot of token `pos` of a sequence whose block table (host memory) holds
+ *                    *num_blocks entries of max_blocks: a token at the start of a block after the
+ *                    last opens a new block (appended to the table); a token in a shared block
+ *                    gets a private copy of it (the table entry is replaced and *copy_src,
+ *                    *copy_dst name the copy to make; both are -1 when no copy is needed).
+ *                    Tokens go in order: pos / 16 must be at most *num_blocks.
+ *
+ * pa_copy_blocks     for each of num_pairs (source, target) pairs in `pairs` (device memory,
+ *                    int32 [num_pairs][2]), copies the K and V tiles of every KV head, and for fp8
+ *                    caches the K and V scales, from block source to block target.  Targets must
+ *                    be distinct and must not be sources of other pairs in the same call (copy-on-
+ *                    write targets are fresh blocks, so this holds).  Pairs with a block outside
+ *                    the pool or source == target are skipped.  The copy is exact.
+ */
+typedef struct pa_block_pool pa_block_pool;
+pa_status pa_pool_create(int32_t num_blocks, pa_block_pool** pool);
+pa_status pa_pool_destroy(pa_block_pool* pool);
+int32_t pa_pool_free_blocks(pa_block_pool* pool);
+int32_t pa_pool_refcount(pa_block_pool* pool, int32_t block);
+pa_status pa_pool_alloc(pa_block_pool* pool, int32_t n, int32_t* blocks);
+pa_status pa_pool_share(pa_block_pool* pool, int32_t n, const int32_t* blocks);
+pa_status pa_pool_release(pa_block_pool* pool, int32_t n, const int32_t* blocks);
+pa_status pa_pool_write(pa_block_pool* pool, int32_t block, int32_t* target, int32_t* needs_copy);
+pa_status pa_pool_slot_for(pa_block_pool* pool, int32_t* table, int32_t* num_blocks,
+                           int32_t max_blocks, int32_t pos, int64_t* slot, int32_t* copy_src,
+                           int32_t* copy_dst);
+pa_status pa_copy_blocks(const pa_cache_desc* cache, int32_t num_pairs, const int32_t* pairs,
+                         void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                         void* stream);
 
 /*
  * HIP graphs of whole steps: launching one kernel per layer and call costs a few microseconds

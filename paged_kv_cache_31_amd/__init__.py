@@ -21,7 +21,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_OUT_OF_BLOCKS = range(6)
 PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_SCALE_KEEP, PA_SCALE_FIRST_TOKEN = 0, 1
 BLOCK_SIZE = 16
@@ -64,6 +64,9 @@ _lock = threading.Lock()
 EXPORTS = ("pa_kv_append", "pa_kv_append_quant", "pa_decode", "pa_decode_append",
            "pa_decode_workspace_size", "pa_decode_multi", "pa_decode_multi_workspace_size",
            "pa_graph_begin", "pa_graph_end", "pa_graph_launch", "pa_graph_destroy",
+           "pa_pool_create", "pa_pool_destroy", "pa_pool_free_blocks", "pa_pool_refcount",
+           "pa_pool_alloc", "pa_pool_share", "pa_pool_release", "pa_pool_write",
+           "pa_pool_slot_for", "pa_copy_blocks",
            "pa_status_string", "pa_last_hip_error")
 
 
@@ -102,6 +105,23 @@ def lib() -> ctypes.CDLL:
             L.pa_graph_launch.restype = i32
             L.pa_graph_destroy.argtypes = [vp]
             L.pa_graph_destroy.restype = i32
+            ip = ctypes.POINTER(i32)
+            L.pa_pool_create.argtypes = [i32, ctypes.POINTER(vp)]
+            L.pa_pool_destroy.argtypes = [vp]
+            L.pa_pool_free_blocks.argtypes = [vp]
+            L.pa_pool_refcount.argtypes = [vp, i32]
+            L.pa_pool_alloc.argtypes = [vp, i32, ip]
+            L.pa_pool_share.argtypes = [vp, i32, ip]
+            L.pa_pool_release.argtypes = [vp, i32, ip]
+            L.pa_pool_write.argtypes = [vp, i32, ip, ip]
+            L.pa_pool_slot_for.argtypes = [vp, ip, ip, i32, i32, ctypes.POINTER(ctypes.c_int64),
+                                           ip, ip]
+            for f in ("pa_pool_create", "pa_pool_destroy", "pa_pool_free_blocks",
+                      "pa_pool_refcount", "pa_pool_alloc", "pa_pool_share", "pa_pool_release",
+                      "pa_pool_write", "pa_pool_slot_for"):
+                getattr(L, f).restype = i32
+            L.pa_copy_blocks.argtypes = [ctypes.POINTER(CacheDesc), i32, vp, vp, vp, vp, vp, vp]
+            L.pa_copy_blocks.restype = i32
             L.pa_status_string.argtypes = [i32]
             L.pa_status_string.restype = ctypes.c_char_p
             L.pa_last_hip_error.argtypes = []
@@ -383,3 +403,76 @@ class StepGraph:
         if g is not None and g.value:
             self._lib.pa_graph_destroy(g)
             self._graph = None
+
+
+class BlockPool:
+    """The library's host-side block pool (pa_pool_*): reference counts and copy-on-write for
+    num_blocks physical blocks.  Refusals raise PaError and leave the pool unchanged."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = lib()
+        p = ctypes.c_void_p()
+        _check("pa_pool_create", self._lib.pa_pool_create(int(num_blocks), ctypes.byref(p)))
+        self._p = p
+
+    def __del__(self):
+        p = getattr(self, "_p", None)
+        if p is not None and p.value:
+            self._lib.pa_pool_destroy(p)
+            self._p = None
+
+    @staticmethod
+    def _ids(blocks):
+        arr = (ctypes.c_int32 * max(1, len(blocks)))(*[int(b) for b in blocks])
+        return len(blocks), arr
+
+    def free_blocks(self) -> int:
+        return int(self._lib.pa_pool_free_blocks(self._p))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_pool_refcount(self._p, int(block)))
+
+    def alloc(self, n: int) -> list:
+        arr = (ctypes.c_int32 * max(1, n))()
+        _check("pa_pool_alloc", self._lib.pa_pool_alloc(self._p, int(n), arr))
+        return list(arr[:n])
+
+    def share(self, blocks) -> None:
+        n, arr = self._ids(blocks)
+        _check("pa_pool_share", self._lib.pa_pool_share(self._p, n, arr))
+
+    def release(self, blocks) -> None:
+        n, arr = self._ids(blocks)
+        _check("pa_pool_release", self._lib.pa_pool_release(self._p, n, arr))
+
+    def write(self, block: int):
+        """(target block, whether block's content must first be copied into it)."""
+        t, c = ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_pool_write", self._lib.pa_pool_write(self._p, int(block), ctypes.byref(t),
+                                                        ctypes.byref(c)))
+        return int(t.value), bool(c.value)
+
+    def slot_for(self, table: list, pos: int, max_blocks: int):
+        """Slot of token pos for a sequence with block list `table` (updated in place): returns
+        (slot, (source, target) of the copy to make, or None)."""
+        arr = (ctypes.c_int32 * max(1, max_blocks))(*[int(b) for b in table])
+        nb = ctypes.c_int32(len(table))
+        slot = ctypes.c_int64()
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_pool_slot_for", self._lib.pa_pool_slot_for(
+            self._p, arr, ctypes.byref(nb), int(max_blocks), int(pos), ctypes.byref(slot),
+            ctypes.byref(src), ctypes.byref(dst)))
+        table[:] = list(arr[:nb.value])
+        return int(slot.value), (None if src.value < 0 else (int(src.value), int(dst.value)))
+
+
+def pa_copy_blocks(pairs, k_cache, v_cache, k_scale=None, v_scale=None, stream=None) -> None:
+    """Copy whole blocks (every KV head, K and V, fp8 scales) for int32 pairs [n][2] on the
+    device: (source, target)."""
+    for t in (pairs, k_cache, v_cache):
+        assert t.is_cuda and t.is_contiguous()
+    assert pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2
+    st = lib().pa_copy_blocks(ctypes.byref(cache_desc(k_cache)), pairs.shape[0], _ptr(pairs),
+                              _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                              _stream(stream))
+    _check("pa_copy_blocks", st)

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "multi.hip"]
+SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "multi.hip", "pool.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -45,11 +45,12 @@ def build(verbose: bool = False, save_asm: bool = False) -> str:
     """Compile every HIP source and link libpa.so; always rebuilds.  Returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     cmds = [[cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
     if save_asm:
         cmds += [[cc, *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, s), "-o",
-                  os.path.join(BUILD, s.replace(".hip", f"-{ARCH}.s"))] for s in SOURCES]
+                  os.path.join(BUILD, s.replace(".hip", f"-{ARCH}.s"))] for s in SOURCES
+                 if s.endswith(".hip")]
     with ThreadPoolExecutor(len(cmds)) as ex:
         logs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"

@@ -125,6 +125,38 @@ hipError_t launch_append_quant(const QuantAppendArgs& a, int num_tokens, bool bf
   return hipGetLastError();
 }
 
+// Copy-on-write copies: workgroup (pair i, KV head h) copies the K and V tiles of block
+// pairs[i][0] into block pairs[i][1] with 16-byte loads and stores, and the fp8 scales with
+// them.  Many small workgroups, each thread with one word per pool, keep the reads and writes
+// of the copy interleaved across the chip (measured faster than fewer workgroups moving 16 KiB
+// chunks with all loads issued before the stores).  Pairs whose blocks lie outside the pool,
+// or that copy a block onto itself, are skipped.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int src = a.pairs[2 * i], dst = a.pairs[2 * i + 1];
+  if ((unsigned)src >= (unsigned)a.num_blocks || (unsigned)dst >= (unsigned)a.num_blocks ||
+      src == dst)
+    return;
+  const size_t so = ((size_t)src * a.num_kv_heads + h) * a.tile_bytes;
+  const size_t dof = ((size_t)dst * a.num_kv_heads + h) * a.tile_bytes;
+  const int n16 = a.tile_bytes / 16;
+  for (int e = threadIdx.x; e < n16; e += blockDim.x) {
+    const uint4 kx = *reinterpret_cast<const uint4*>(a.k_cache + so + 16 * (size_t)e);
+    const uint4 vx = *reinterpret_cast<const uint4*>(a.v_cache + so + 16 * (size_t)e);
+    *reinterpret_cast<uint4*>(a.k_cache + dof + 16 * (size_t)e) = kx;
+    *reinterpret_cast<uint4*>(a.v_cache + dof + 16 * (size_t)e) = vx;
+  }
+  if (a.k_scale && threadIdx.x == 0) {
+    a.k_scale[(size_t)dst * a.num_kv_heads + h] = a.k_scale[(size_t)src * a.num_kv_heads + h];
+    a.v_scale[(size_t)dst * a.num_kv_heads + h] = a.v_scale[(size_t)src * a.num_kv_heads + h];
+  }
+}
+
+hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, a.num_kv_heads), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendArgs& a, int num_tokens, int elem_bytes, hipStream_t stream) {
   const dim3 grid(num_tokens, a.num_kv_heads), block(a.head_dim);
   if (elem_bytes == 2)

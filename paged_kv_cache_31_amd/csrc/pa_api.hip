@@ -151,6 +151,7 @@ PA_EXPORT const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch failed";
+    case PA_ERR_OUT_OF_BLOCKS: return "no free block in the pool";
   }
   return "unknown status";
 }
@@ -323,6 +324,38 @@ PA_EXPORT pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q,
   return PA_OK;
 }
 
+PA_EXPORT pa_status pa_copy_blocks(const pa_cache_desc* cache, int32_t num_pairs,
+                                   const int32_t* pairs, void* k_cache, void* v_cache,
+                                   float* k_scale, float* v_scale, void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if (!pairs || !k_cache || !v_cache || !aligned(pairs, 4) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16))
+    return PA_ERR_INVALID_ARG;
+  const bool fp8 = cache->kv_dtype == PA_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return PA_ERR_INVALID_ARG;
+  if (!fp8 && (k_scale || v_scale)) return PA_ERR_INVALID_ARG;
+  pa::CopyArgs a;
+  a.pairs = pairs;
+  a.k_cache = static_cast<uint8_t*>(k_cache);
+  a.v_cache = static_cast<uint8_t*>(v_cache);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.num_blocks = cache->num_blocks;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.tile_bytes = pa::kBlock * cache->head_dim * (fp8 ? 1 : 2);
+  hipError_t e = pa::launch_copy_blocks(a, num_pairs, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
 PA_EXPORT size_t pa_decode_workspace_size(const pa_decode_desc* desc) {
   if (check_decode_desc(desc) != PA_OK) return 0;
   return workspace_bytes_of(desc);
@@ -462,7 +495,7 @@ PA_EXPORT pa_status pa_graph_end(void* stream, pa_graph** graph) {
   hipGraphExec_t x = nullptr;
   e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
   if (e != hipSuccess) {
-    hipGraphDestroy(g);
+    (void)hipGraphDestroy(g);
     g_last_hip_error = (int32_t)e;
     return PA_ERR_HIP;
   }
@@ -482,8 +515,8 @@ PA_EXPORT pa_status pa_graph_launch(const pa_graph* graph, void* stream) {
 
 PA_EXPORT pa_status pa_graph_destroy(pa_graph* graph) {
   if (!graph) return PA_OK;
-  hipGraphExecDestroy(graph->exec);
-  hipGraphDestroy(graph->graph);
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
   delete graph;
   return PA_OK;
 }

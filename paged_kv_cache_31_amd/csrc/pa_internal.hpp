@@ -187,6 +187,18 @@ inline size_t multi_workspace_bytes(const MultiPlan& p, int total_queries, int n
   return align256(rows * head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
+struct CopyArgs {
+  const int32_t* pairs;   // [n][2] (source block, target block), device
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  float* k_scale;         // fp8 caches only (else null)
+  float* v_scale;
+  int num_blocks;
+  int num_kv_heads;
+  int tile_bytes;         // 16 * head_dim * element bytes
+};
+hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t stream);
+
 hipError_t launch_append(const AppendArgs& a, int num_tokens, int elem_bytes, hipStream_t stream);
 hipError_t launch_append_quant(const QuantAppendArgs& a, int num_tokens, bool bf16_src,
                                bool first_token_scale, hipStream_t stream);

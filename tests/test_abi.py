@@ -265,3 +265,21 @@ def test_graph_rejects():
     assert lib.pa_graph_end(FAKE, None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_graph_launch(None, None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_graph_destroy(None) == pa.PA_OK
+
+
+def test_copy_blocks_rejects():
+    lib = pa.lib()
+    c = pa.CacheDesc(64, 2, 64, 16, pa.PA_BF16)
+    c8 = pa.CacheDesc(64, 2, 64, 16, pa.PA_FP8_E4M3)
+
+    def call(desc, n=1, pairs=FAKE, k=FAKE, ks=None):
+        return lib.pa_copy_blocks(ctypes.byref(desc), n, pairs, k, FAKE, ks, ks, None)
+
+    assert call(c, n=0) == pa.PA_OK
+    assert call(c, n=-1) == pa.PA_ERR_INVALID_ARG
+    assert call(c, pairs=None) == pa.PA_ERR_INVALID_ARG
+    assert call(c, pairs=ctypes.c_void_p(0x10002)) == pa.PA_ERR_INVALID_ARG
+    assert call(c, k=ctypes.c_void_p(0x10008)) == pa.PA_ERR_INVALID_ARG
+    assert call(c, ks=FAKE) == pa.PA_ERR_INVALID_ARG       # scales only for fp8
+    assert call(c8) == pa.PA_ERR_INVALID_ARG               # fp8 needs them
+    assert pa.status_string(pa.PA_ERR_OUT_OF_BLOCKS) == "no free block in the pool"
