@@ -112,14 +112,26 @@ __device__ __forceinline__ uint2 load_stream8(const void* p) {
 // Wait until this wave's memory operations have completed (stores acknowledged).
 __device__ __forceinline__ void wait_memory_ops() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Butterfly over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+// Butterfly over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with the gfx950
+// lane-swap instructions, which stay in the vector ALU (a cross-lane shuffle would go through
+// the LDS crossbar).  Swapping a value with itself, v_permlane16_swap returns the even row of
+// each row pair in its first result and the odd row in its second (v_permlane32_swap: the lower
+// and upper halves), so combining the two results gives every lane the same pairwise result.
 __device__ __forceinline__ float max_across_rows(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_across_rows(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 }  // namespace pa

@@ -168,8 +168,296 @@ __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
   }
 }
 
+// ---- Prefill chunks: many query rows per (sequence, KV head).
+//
+// A workgroup of kChunkWaves waves takes kChunkRows consecutive rows of one head, 32 per wave as
+// two 16-column MFMA tiles, and walks the keys its rows see in 32-token steps.  Each step's K
+// and V tiles are loaded from HBM once per workgroup (every thread a few 16-byte words, the next
+// step's loads in flight during the current step's products) and written to one of two LDS
+// buffers; the waves read their MFMA operands from LDS.  Per step a wave issues 16 MFMAs for the
+// scores and 16 (fp16) or 32 (bf16: P as a hi/lo pair) for P.V, against 16 KiB of LDS reads, so
+// the matrix cores rather than memory set the pace.  Operand layouts are those of the streaming
+// core: K token rows in the A operand in the order that makes the score layout the P^T operand,
+// V^T as the A operand of P.V (the LDS V tile is dim-major, 32 tokens per dimension row), rows
+// padded by 16 bytes to spread LDS banks.  V elements of tokens at or past the context end are
+// zeroed when staged, so garbage in the last block's unused slots never reaches the products.
+template <int D>
+struct ChunkLds {
+  // K token rows are unpadded; their 16-byte chunks are permuted per row (kswz) so that the 16
+  // rows one operand read touches (rows 0-3, 8-11, 16-19, 24-27 of the step) fall on distinct
+  // banks.  With 2*D-byte rows, rows r and r + 16 would otherwise share banks.
+  static constexpr int KSTRIDE = 2 * D;                      // bytes per K token row
+  static constexpr int VSTRIDE = 2 * kStepTokens + 16;       // bytes per V dimension row
+  static constexpr int KBYTES = kStepTokens * KSTRIDE;
+  static constexpr int BUF = KBYTES + D * VSTRIDE;
+  static constexpr int WORDS = 2 * kBlock * D * 2 / 16;      // 16-byte words of K (or V) a step
+  static constexpr int PER_THREAD = (WORDS + 64 * kChunkWaves - 1) / (64 * kChunkWaves);
+};
+
+// chunk index of 16-byte chunk c of K token row r in LDS
+template <int D>
+__device__ __forceinline__ int kswz(int r, int c) {
+  if constexpr (D == 128) return c ^ ((r & 3) | (((r >> 3) & 3) << 2));
+  else return c ^ (((r >> 1) & 1) | (((r >> 3) & 3) << 1));   // 8 chunks; rows alternate halves
+}
+
+template <int D, int QT>
+__global__ __launch_bounds__(64 * kChunkWaves, 2) void chunk_kernel(MultiArgs a) {
+  typedef Mfma<QT> M;
+  typedef typename M::vec8 V8;
+  typedef typename M::elem E;
+  typedef ChunkLds<D> Lay;
+  constexpr bool SPLIT_P = QT == DT_BF16;
+  constexpr int NC = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int TB = kBlock * D * 2;                         // bytes of one (block, head) tile
+  constexpr int NTHR = 64 * kChunkWaves;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lay::BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int per_xcd = gridDim.x / 8;
+  const int lwg = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int Hkv = a.num_kv_heads, G = a.group, RBH = a.row_blocks;
+  if ((long long)lwg >= a.total_items) return;               // whole workgroup
+  const int rb = lwg % RBH;
+  const int kvh = (lwg / RBH) % Hkv;
+  const int b = lwg / RBH / Hkv;
+
+  const int q0 = a.query_start[b];
+  const int T = min(max(a.query_start[b + 1] - q0, 0), a.max_query_len);
+  const int L = clamp_len(a.context_lens[b], a.len_cap);
+  const int rows = T * G;
+  const int r0 = rb * kChunkRows;
+  if (r0 >= rows) return;                                    // whole workgroup
+  auto end_of = [&](int ii) { return min(max(L - T + ii + 1, 0), L); };
+  const int r_last = min(r0 + kChunkRows - 1, rows - 1);
+  const int nblk = blocks_of(end_of(r_last / G));
+  const int nsteps = (nblk + 1) >> 1;
+
+  // this wave's rows: tiles u = 0, 1 of 16 columns; columns past the last row repeat it
+  const int rw0 = r0 + 32 * wave;
+  const bool has_rows = rw0 <= r_last;
+  const int rw_last = has_rows ? min(rw0 + 31, r_last) : r_last;
+  const int end_lo = end_of(min(rw0, r_last) / G);
+  const int end_hi = end_of(rw_last / G);
+  int end_lane[2];
+  bool real[2];
+  size_t orow[2];
+  V8 qB[2][NC];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int rr = rw0 + 16 * u + col;
+    real[u] = has_rows && rr <= rw_last;
+    const int r = real[u] ? rr : rw_last;
+    const int i = r / G, g = r - i * G;
+    end_lane[u] = end_of(i);
+    const long long n = (long long)q0 + i;
+    real[u] = real[u] && n >= 0 && n < a.total_queries;
+    orow[u] = (size_t)(real[u] ? n : 0) * a.num_q_heads + kvh * G + g;
+    const E* qrow = reinterpret_cast<const E*>(a.q) + orow[u] * D;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      qB[u][cc] = real[u] ? as_vec8<V8>(*reinterpret_cast<const uint4*>(qrow + 32 * cc + 8 * grp))
+                          : zero_vec8<V8>();
+  }
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+  f32x4 acc[2][NT];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[u][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // ---- staging: this thread's words of a step's K and V tiles
+  const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v_cache);
+  static_assert(Lay::PER_THREAD <= 2, "two staged words per thread at most");
+  // a step's words of K and V held between their load and their LDS store
+  struct Words {
+    uint4 k0, v0, k1, v1;
+  };
+  Words wa, wb;
+  auto fetch_word = [&](int idx, int p0, int p1, uint4& kx, uint4& vx) {
+    const int o = 16 * idx, blk = o / TB, off = o - blk * TB;
+    const size_t tile = ((size_t)(blk ? p1 : p0) * Hkv + kvh) * TB + off;
+    kx = *reinterpret_cast<const uint4*>(kc + tile);
+    vx = *reinterpret_cast<const uint4*>(vc + tile);
+  };
+  auto fetch = [&](int s, Words& w) {
+    const int jb0 = 2 * s, jb1 = 2 * s + 1 < nblk ? 2 * s + 1 : 2 * s;
+    int p0 = trow[jb0], p1 = trow[jb1];
+    p0 = (unsigned)p0 < (unsigned)a.num_blocks ? p0 : 0;
+    p1 = (unsigned)p1 < (unsigned)a.num_blocks ? p1 : 0;
+    if (tid < Lay::WORDS) fetch_word(tid, p0, p1, w.k0, w.v0);
+    if constexpr (Lay::PER_THREAD > 1)
+      if (tid + NTHR < Lay::WORDS) fetch_word(tid + NTHR, p0, p1, w.k1, w.v1);
+  };
+  auto stage_word = [&](int idx, int t0, uint8_t* kb, uint8_t* vb, uint4 kx, uint4 x) {
+    const int o = 16 * idx, blk = o / TB, off = o - blk * TB;
+    // K tile: token rows of 2*D bytes
+    const int tok = off / (2 * D), cb = off - tok * (2 * D);
+    const int row = kBlock * blk + tok;
+    *reinterpret_cast<uint4*>(kb + row * Lay::KSTRIDE + 16 * kswz<D>(row, cb / 16)) = kx;
+    // V tile: dimension rows of 16 tokens (32 bytes); this word holds 8 of them
+    const int d = off / 32, h = (off / 16) & 1;
+    const int tv = kBlock * blk + 8 * h;
+    const int valid = L - (t0 + tv);                         // tokens of the word before the end
+    if (valid < 8) {
+      auto keep = [&](int k) {
+        return (2 * k < valid ? 0x0000FFFFu : 0u) | (2 * k + 1 < valid ? 0xFFFF0000u : 0u);
+      };
+      x.x &= keep(0);
+      x.y &= keep(1);
+      x.z &= keep(2);
+      x.w &= keep(3);
+    }
+    *reinterpret_cast<uint4*>(vb + d * Lay::VSTRIDE + 2 * tv) = x;
+  };
+  auto stage = [&](int s, int buf, const Words& w) {
+    uint8_t* kb = lds + buf * Lay::BUF;
+    uint8_t* vb = kb + Lay::KBYTES;
+    const int t0 = kStepTokens * s;
+    if (tid < Lay::WORDS) stage_word(tid, t0, kb, vb, w.k0, w.v0);
+    if constexpr (Lay::PER_THREAD > 1)
+      if (tid + NTHR < Lay::WORDS) stage_word(tid + NTHR, t0, kb, vb, w.k1, w.v1);
+  };
+
+  // ---- products of one step for this wave's two tiles
+  const int krow0 = 16 * (col >> 3) + 8 * ((col >> 2) & 1) + (col & 3);
+  auto compute = [&](int s, int buf) {
+    const int t0 = kStepTokens * s;
+    if (!has_rows || t0 >= end_hi) return;
+    const uint8_t* kb = lds + buf * Lay::BUF;
+    const uint8_t* vb = kb + Lay::KBYTES;
+    f32x4 S[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) S[u][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const int row = krow0 + 4 * m;
+        const V8 kA = as_vec8<V8>(*reinterpret_cast<const uint4*>(
+            kb + row * Lay::KSTRIDE + 16 * kswz<D>(row, 4 * cc + grp)));
+        S[0][m] = M::mma(kA, qB[0][cc], S[0][m]);
+        S[1][m] = M::mma(kA, qB[1][cc], S[1][m]);
+      }
+    const bool partial = t0 + kStepTokens > end_lo;          // wave-uniform
+    const int tb = t0 + 8 * grp;
+    // Scores stay unscaled until the exponent: the largest scaled score is the scaled largest
+    // (or smallest, for a negative scale) raw one, and exp2(fma(s, scale, -m)) saves a pass.
+    const float qs = a.qk_scale_log2;
+    V8 pHi[2], pLo[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float sc[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) sc[jj] = S[u][jj >> 2][jj & 3];
+      const float masked = qs >= 0.0f ? -INFINITY : INFINITY;
+      if (partial) {
+        const int nval = min(max(end_lane[u] - tb, 0), 8);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (jj >= nval) sc[jj] = masked;
+      }
+      float mx = sc[0];
+      if (qs >= 0.0f) {
+#pragma unroll
+        for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
+        mx = max_across_rows(mx);
+      } else {
+#pragma unroll
+        for (int jj = 1; jj < 8; ++jj) mx = fminf(mx, sc[jj]);
+        mx = -max_across_rows(-mx);
+      }
+      const float m_new = fmaxf(m_run[u], mx * qs);
+      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run[u] - m_ref);
+      float pr[8], psum = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        pr[jj] = fast_exp2(__builtin_fmaf(sc[jj], qs, -m_ref));
+        psum += pr[jj];
+      }
+      l_run[u] = l_run[u] * alpha + psum;
+      m_run[u] = m_new;
+      // once the running maxima settle, most steps leave them unchanged (alpha = 1 exactly)
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[u][t] *= alpha;
+      }
+      uint32_t h[4], lo[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        h[w] = pack2<QT>(pr[2 * w], pr[2 * w + 1]);
+        if constexpr (SPLIT_P) {
+          const V8 hv = as_vec8<V8>(make_uint4(h[w], 0u, 0u, 0u));
+          lo[w] = pack2<QT>(pr[2 * w] - (float)hv[0], pr[2 * w + 1] - (float)hv[1]);
+        }
+      }
+      pHi[u] = as_vec8<V8>(make_uint4(h[0], h[1], h[2], h[3]));
+      if constexpr (SPLIT_P) pLo[u] = as_vec8<V8>(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const V8 vA = as_vec8<V8>(*reinterpret_cast<const uint4*>(
+          vb + (16 * t + col) * Lay::VSTRIDE + 16 * grp));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        acc[u][t] = M::mma(vA, pHi[u], acc[u][t]);
+        if constexpr (SPLIT_P) acc[u][t] = M::mma(vA, pLo[u], acc[u][t]);
+      }
+    }
+  };
+
+  // Two steps ahead: step s is computed from LDS buffer s % 2 while step s + 1 is staged from
+  // registers into the other buffer and step s + 2 is being loaded into the registers step s
+  // has left; the loop is unrolled by two so that each register set keeps its registers.
+  if (nsteps > 0) fetch(0, wa);
+  if (nsteps > 1) fetch(1, wb);
+  if (nsteps > 0) stage(0, 0, wa);
+  __syncthreads();
+  for (int s = 0; s < nsteps;) {
+    if (s + 2 < nsteps) fetch(s + 2, wa);
+    compute(s, 0);
+    if (s + 1 < nsteps) stage(s + 1, 1, wb);
+    __syncthreads();
+    if (++s >= nsteps) break;
+    if (s + 2 < nsteps) fetch(s + 2, wb);
+    compute(s, 1);
+    if (s + 1 < nsteps) stage(s + 1, 0, wa);
+    __syncthreads();
+    ++s;
+  }
+
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const float lsum = sum_across_rows(l_run[u]);
+    if (!real[u]) continue;
+    const float l = lsum > 0.0f ? lsum : 1.0f;
+    E* out = reinterpret_cast<E*>(a.out) + orow[u] * D + 4 * grp;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      *reinterpret_cast<uint2*>(out + 16 * t) =
+          make_uint2(pack2<QT>(acc[u][t][0] / l, acc[u][t][1] / l),
+                     pack2<QT>(acc[u][t][2] / l, acc[u][t][3] / l));
+  }
+}
+
 template <int D, int QT, int KVT>
 static hipError_t launch_multi_t(const MultiArgs& a, hipStream_t stream) {
+  if constexpr (KVT != DT_FP8) {
+    if (a.row_blocks > 0) {
+      long long wgs = (long long)a.batch * a.num_kv_heads * a.row_blocks;
+      wgs = (wgs + 7) / 8 * 8;
+      hipLaunchKernelGGL((chunk_kernel<D, QT>), dim3((unsigned)wgs), dim3(64 * kChunkWaves), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
   long long wgs = (a.total_items + kMultiWaves - 1) / kMultiWaves;
   wgs = (wgs + 7) / 8 * 8;
   if (wgs > 0) {

@@ -80,7 +80,8 @@ int multi_len_cap(const pa_multi_desc* d) {
 
 pa::MultiPlan multi_plan_of(const pa_multi_desc* d) {
   return pa::multi_plan(d->batch, d->cache.num_kv_heads, d->num_q_heads / d->cache.num_kv_heads,
-                        d->max_query_len, multi_len_cap(d), d->partition_tokens);
+                        d->max_query_len, multi_len_cap(d), d->partition_tokens,
+                        d->cache.kv_dtype == PA_FP8_E4M3);
 }
 
 // Upper bound of the flattened (sequence, KV head, block) space.
@@ -249,6 +250,7 @@ pa_status check_multi_desc(const pa_multi_desc* d) {
   const pa::MultiPlan p = multi_plan_of(d);
   if (p.items > (1LL << 32) || (long long)d->batch * d->max_query_len * d->num_q_heads > (1LL << 32))
     return PA_ERR_UNSUPPORTED;
+  if (p.row_blocks > 0 && p.items > (1LL << 31) - 8) return PA_ERR_UNSUPPORTED;  // one per workgroup
   return PA_OK;
 }
 
@@ -314,6 +316,7 @@ PA_EXPORT pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q,
   a.num_parts = p.num_parts;
   a.part_blocks = p.part_blocks;
   a.total_items = p.items;
+  a.row_blocks = p.row_blocks;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = pa::launch_multi(a, desc->cache.head_dim, desc->q_dtype, desc->cache.kv_dtype,
                                   static_cast<hipStream_t>(stream));

@@ -143,6 +143,7 @@ struct MultiArgs {
   int num_parts;
   int part_blocks;             // even
   long long total_items;
+  int row_blocks;              // > 0: chunk_kernel, this many blocks of kChunkRows rows per head
   float qk_scale_log2;
 };
 
@@ -150,14 +151,30 @@ constexpr int kMultiWaves = 4;             // waves per multi_kernel workgroup
 constexpr long kMultiTargetWaves = 4096;   // items the automatic partition aims for
 constexpr int kMultiMinPartBlocks = 16;    // automatic partitions are at least 256 tokens
 
+// Many rows per (sequence, KV head) -- prefill chunks -- go to chunk_kernel: a workgroup takes
+// kChunkRows rows of one head and stages each K/V step once in LDS for all of them.
+constexpr int kChunkWaves = 4;
+constexpr int kChunkRows = 32 * kChunkWaves;
+
 struct MultiPlan {
   int tiles_per_head, num_parts, part_blocks;
   long long items;
+  int row_blocks;              // > 0: chunk_kernel
 };
 // A pure function of the descriptor, so the workspace size is known without a GPU.
 inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_query_len,
-                            int len_cap, int partition_tokens) {
+                            int len_cap, int partition_tokens, bool kv_fp8) {
   MultiPlan p;
+  const long long rows = (long long)max_query_len * group;
+  if (partition_tokens == 0 && !kv_fp8 && rows >= kChunkRows) {
+    p.row_blocks = (int)((rows + kChunkRows - 1) / kChunkRows);
+    p.tiles_per_head = 0;
+    p.num_parts = 1;
+    p.part_blocks = 0;
+    p.items = (long long)batch * num_kv_heads * p.row_blocks;
+    return p;
+  }
+  p.row_blocks = 0;
   p.tiles_per_head = (int)(((long long)max_query_len * group + 15) / 16);
   const long long maxblk = ((long long)len_cap + kBlock - 1) / kBlock;
   long long pb;

@@ -101,6 +101,23 @@ def test_prefill_chunks_of_512(qd, kvd, g, P):
     m.check(m.run(partition_tokens=P), f"prefill g{g} P{P}")
 
 
+CHUNK = [
+    # (q dtype, kv heads, group, head_dim, context lengths, new tokens): 128+ rows per head take
+    # the LDS-staged path; lengths end inside blocks, so the last step holds unused slots
+    ("bf16", 2, 1, 64, (200, 531, 130), (200, 131, 130)),
+    ("f16", 2, 3, 128, (700, 77, 1025), (130, 77, 50)),
+    ("bf16", 1, 8, 128, (40, 1000, 333), (40, 17, 300)),
+    ("bf16", 2, 4, 64, (20, 600, 5), (64, 35, 32)),          # more queries than context
+]
+
+
+@pytest.mark.parametrize("case", CHUNK, ids=lambda c: f"{c[0]}-kv{c[1]}g{c[2]}d{c[3]}")
+def test_prefill_chunk_shapes(case):
+    qd, hkv, g, d, lens, T = case
+    m = Multi(qd, qd, hkv, g, d, lens, T, seed=110 + CHUNK.index(case), spare_rows=2)
+    m.check(m.run(), f"chunk {case}")
+
+
 def test_more_queries_than_context_and_loose_bounds():
     """Rows before the context are zero; host bounds larger than needed change nothing."""
     m = Multi("bf16", "bf16", 2, 4, 128, (3, 1, 40), (6, 4, 2), seed=101, spare_rows=2)
