@@ -222,12 +222,14 @@ def bench_multi(args, dev) -> int:
     launch_s = e0.elapsed_time(e1) / 1e3 / args.steps
     log(f"{args.steps} back-to-back pa_decode_multi calls: {launch_s * 1e6:.1f} us each")
 
-    # the library's choice (pa_internal.hpp multi_plan): 128+ rows per head, 16-bit cache and no
-    # fixed partition take the LDS-staged chunk kernel
-    if P == 0 and s.kv_dtype != "fp8_e4m3" and maxT * (Hq // Hkv) >= 128:
+    # the library's choice (pa_internal.hpp multi_plan): more than 16 rows per head, a 16-bit
+    # cache and no fixed partition take the LDS-staged chunk kernel
+    if P == 0 and s.kv_dtype != "fp8_e4m3" and maxT * (Hq // Hkv) > 16:
         kernel = "chunk_kernel"
     else:
-        kernel = "multi_kernel+multi_merge_kernel" if ws_bytes > 0 else "multi_kernel"
+        kernel = "multi_kernel"
+    if ws_bytes > 0:
+        kernel += "+multi_merge_kernel"
     step_s = ms_per_step / 1e3
     if mfma:
         peak, unit = PEAK_TFLOPS[s.q_dtype], "TFLOP/s"

@@ -168,20 +168,21 @@ __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
   }
 }
 
-// ---- Prefill chunks: many query rows per (sequence, KV head).
+// ---- Many query rows per (sequence, KV head): prefill chunks, verification of several drafts.
 //
-// A workgroup of kChunkWaves waves takes kChunkRows consecutive rows of one head, 32 per wave as
-// two 16-column MFMA tiles, and walks the keys its rows see in 32-token steps.  Each step's K
-// and V tiles are loaded from HBM once per workgroup (every thread a few 16-byte words, the next
-// step's loads in flight during the current step's products) and written to one of two LDS
-// buffers; the waves read their MFMA operands from LDS.  Per step a wave issues 16 MFMAs for the
-// scores and 16 (fp16) or 32 (bf16: P as a hi/lo pair) for P.V, against 16 KiB of LDS reads, so
-// the matrix cores rather than memory set the pace.  Operand layouts are those of the streaming
-// core: K token rows in the A operand in the order that makes the score layout the P^T operand,
-// V^T as the A operand of P.V (the LDS V tile is dim-major, 32 tokens per dimension row), rows
-// padded by 16 bytes to spread LDS banks.  V elements of tokens at or past the context end are
-// zeroed when staged, so garbage in the last block's unused slots never reaches the products.
-template <int D>
+// A workgroup of W waves takes 16 * TPW * W consecutive rows of one head (TPW 16-column MFMA
+// tiles per wave) and walks the keys of one partition of them in 32-token steps.  Each step's K
+// and V tiles are loaded from HBM once per workgroup (every thread a few 16-byte words, two steps
+// ahead of their use) and written to one of two LDS buffers; the waves read their MFMA operands
+// from LDS, so the tiles of a head share every load.  Per step a wave issues 8 MFMAs per tile for
+// the scores and 8 (fp16) or 16 (bf16: P as a hi/lo pair) per tile for P.V.  Operand layouts are
+// those of the streaming core: K token rows in the A operand in the order that makes the score
+// layout the P^T operand, V^T as the A operand of P.V (the LDS V tile is dim-major, 32 tokens
+// per dimension row, rows padded by 16 bytes to spread LDS banks).  V elements of tokens at or
+// past the context end are zeroed when staged, so garbage in the last block's unused slots never
+// reaches the products.  With several key partitions the unnormalised result and its (max,
+// exp-sum) go to the workspace for multi_merge_kernel, as in multi_kernel.
+template <int D, int W>
 struct ChunkLds {
   // K token rows are unpadded; their 16-byte chunks are permuted per row (kswz) so that the 16
   // rows one operand read touches (rows 0-3, 8-11, 16-19, 24-27 of the step) fall on distinct
@@ -191,7 +192,8 @@ struct ChunkLds {
   static constexpr int KBYTES = kStepTokens * KSTRIDE;
   static constexpr int BUF = KBYTES + D * VSTRIDE;
   static constexpr int WORDS = 2 * kBlock * D * 2 / 16;      // 16-byte words of K (or V) a step
-  static constexpr int PER_THREAD = (WORDS + 64 * kChunkWaves - 1) / (64 * kChunkWaves);
+  static constexpr int PER_THREAD = WORDS / (64 * W);
+  static_assert(WORDS % (64 * W) == 0, "whole words per thread");
 };
 
 // chunk index of 16-byte chunk c of K token row r in LDS
@@ -201,52 +203,64 @@ __device__ __forceinline__ int kswz(int r, int c) {
   else return c ^ (((r >> 1) & 1) | (((r >> 3) & 3) << 1));   // 8 chunks; rows alternate halves
 }
 
-template <int D, int QT>
-__global__ __launch_bounds__(64 * kChunkWaves, 2) void chunk_kernel(MultiArgs a) {
+template <int D, int QT, int W, int TPW, int BUFS>
+__global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
   typedef Mfma<QT> M;
   typedef typename M::vec8 V8;
   typedef typename M::elem E;
-  typedef ChunkLds<D> Lay;
+  typedef ChunkLds<D, W> Lay;
+  // bf16 P as a hi/lo pair: rounding it once was measured 20% faster on a 512-token prefill
+  // chunk but misses the 2e-3 tolerance on short contexts
   constexpr bool SPLIT_P = QT == DT_BF16;
   constexpr int NC = D / 32;
   constexpr int NT = D / 16;
   constexpr int TB = kBlock * D * 2;                         // bytes of one (block, head) tile
-  constexpr int NTHR = 64 * kChunkWaves;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lay::BUF];
+  constexpr int NTHR = 64 * W;
+  constexpr int PT = Lay::PER_THREAD;
+  constexpr int ROWS_W = 16 * TPW;                           // rows per wave
+  constexpr int ROWS_G = ROWS_W * W;                         // rows per workgroup
+  static_assert(BUFS == 2 || BUFS == 3, "two or three LDS step buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[BUFS * Lay::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int per_xcd = gridDim.x / 8;
   const int lwg = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int Hkv = a.num_kv_heads, G = a.group, RBH = a.row_blocks;
   if ((long long)lwg >= a.total_items) return;               // whole workgroup
+  const int Hkv = a.num_kv_heads, G = a.group, RBH = a.row_blocks, NP = a.num_parts;
   const int rb = lwg % RBH;
-  const int kvh = (lwg / RBH) % Hkv;
-  const int b = lwg / RBH / Hkv;
+  const int part = (lwg / RBH) % NP;
+  const int kvh = (lwg / RBH / NP) % Hkv;
+  const int b = lwg / RBH / NP / Hkv;
 
   const int q0 = a.query_start[b];
   const int T = min(max(a.query_start[b + 1] - q0, 0), a.max_query_len);
   const int L = clamp_len(a.context_lens[b], a.len_cap);
   const int rows = T * G;
-  const int r0 = rb * kChunkRows;
+  const int r0 = rb * ROWS_G;
   if (r0 >= rows) return;                                    // whole workgroup
-  auto end_of = [&](int ii) { return min(max(L - T + ii + 1, 0), L); };
-  const int r_last = min(r0 + kChunkRows - 1, rows - 1);
-  const int nblk = blocks_of(end_of(r_last / G));
-  const int nsteps = (nblk + 1) >> 1;
+  const int r_last = min(r0 + ROWS_G - 1, rows - 1);
+  auto window = [&](int ii) { return min(max(L - T + ii + 1, 0), L); };
+  const int nblk_all = blocks_of(window(r_last / G));
+  const int j0 = part * a.part_blocks;                       // this partition's blocks [j0, j1)
+  const int j1 = min(j0 + a.part_blocks, nblk_all);
+  const int cap = kBlock * j1;                               // later keys belong to other parts
+  auto end_of = [&](int ii) { return min(window(ii), cap); };
+  const int s0 = j0 >> 1;                                    // j0 is even
+  const int nsteps = j1 > j0 ? ((j1 - j0 + 1) >> 1) : 0;
 
-  // this wave's rows: tiles u = 0, 1 of 16 columns; columns past the last row repeat it
-  const int rw0 = r0 + 32 * wave;
+  // this wave's rows: TPW tiles of 16 columns; columns past the last row repeat it
+  const int rw0 = r0 + ROWS_W * wave;
   const bool has_rows = rw0 <= r_last;
-  const int rw_last = has_rows ? min(rw0 + 31, r_last) : r_last;
+  const int rw_last = has_rows ? min(rw0 + ROWS_W - 1, r_last) : r_last;
   const int end_lo = end_of(min(rw0, r_last) / G);
   const int end_hi = end_of(rw_last / G);
-  int end_lane[2];
-  bool real[2];
-  size_t orow[2];
-  V8 qB[2][NC];
+  int end_lane[TPW];
+  bool real[TPW];
+  size_t orow[TPW];
+  V8 qB[TPW][NC];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < TPW; ++u) {
     const int rr = rw0 + 16 * u + col;
     real[u] = has_rows && rr <= rw_last;
     const int r = real[u] ? rr : rw_last;
@@ -261,21 +275,23 @@ __global__ __launch_bounds__(64 * kChunkWaves, 2) void chunk_kernel(MultiArgs a)
       qB[u][cc] = real[u] ? as_vec8<V8>(*reinterpret_cast<const uint4*>(qrow + 32 * cc + 8 * grp))
                           : zero_vec8<V8>();
   }
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-  f32x4 acc[2][NT];
+  float m_run[TPW], l_run[TPW];
+  f32x4 acc[TPW][NT];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < TPW; ++u) {
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[u][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   // ---- staging: this thread's words of a step's K and V tiles
   const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
   const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v_cache);
-  static_assert(Lay::PER_THREAD <= 2, "two staged words per thread at most");
-  // a step's words of K and V held between their load and their LDS store
-  struct Words {
-    uint4 k0, v0, k1, v1;
+  static_assert(PT >= 1 && PT <= 4, "one to four staged words per thread");
+  struct Words {                                             // a step's words between load and store
+    uint4 k0, v0, k1, v1, k2, v2, k3, v3;
   };
   Words wa, wb;
   auto fetch_word = [&](int idx, int p0, int p1, uint4& kx, uint4& vx) {
@@ -285,15 +301,16 @@ __global__ __launch_bounds__(64 * kChunkWaves, 2) void chunk_kernel(MultiArgs a)
     vx = *reinterpret_cast<const uint4*>(vc + tile);
   };
   auto fetch = [&](int s, Words& w) {
-    const int jb0 = 2 * s, jb1 = 2 * s + 1 < nblk ? 2 * s + 1 : 2 * s;
+    const int jb0 = 2 * s, jb1 = 2 * s + 1 < j1 ? 2 * s + 1 : 2 * s;
     int p0 = trow[jb0], p1 = trow[jb1];
     p0 = (unsigned)p0 < (unsigned)a.num_blocks ? p0 : 0;
     p1 = (unsigned)p1 < (unsigned)a.num_blocks ? p1 : 0;
-    if (tid < Lay::WORDS) fetch_word(tid, p0, p1, w.k0, w.v0);
-    if constexpr (Lay::PER_THREAD > 1)
-      if (tid + NTHR < Lay::WORDS) fetch_word(tid + NTHR, p0, p1, w.k1, w.v1);
+    fetch_word(tid, p0, p1, w.k0, w.v0);
+    if constexpr (PT > 1) fetch_word(tid + NTHR, p0, p1, w.k1, w.v1);
+    if constexpr (PT > 2) fetch_word(tid + 2 * NTHR, p0, p1, w.k2, w.v2);
+    if constexpr (PT > 3) fetch_word(tid + 3 * NTHR, p0, p1, w.k3, w.v3);
   };
-  auto stage_word = [&](int idx, int t0, uint8_t* kb, uint8_t* vb, uint4 kx, uint4 x) {
+  auto stage_word = [&](int idx, int t0, uint8_t* kb, uint8_t* vb, uint4 kx, uint4 vx) {
     const int o = 16 * idx, blk = o / TB, off = o - blk * TB;
     // K tile: token rows of 2*D bytes
     const int tok = off / (2 * D), cb = off - tok * (2 * D);
@@ -307,32 +324,31 @@ __global__ __launch_bounds__(64 * kChunkWaves, 2) void chunk_kernel(MultiArgs a)
       auto keep = [&](int k) {
         return (2 * k < valid ? 0x0000FFFFu : 0u) | (2 * k + 1 < valid ? 0xFFFF0000u : 0u);
       };
-      x.x &= keep(0);
-      x.y &= keep(1);
-      x.z &= keep(2);
-      x.w &= keep(3);
+      vx.x &= keep(0);
+      vx.y &= keep(1);
+      vx.z &= keep(2);
+      vx.w &= keep(3);
     }
-    *reinterpret_cast<uint4*>(vb + d * Lay::VSTRIDE + 2 * tv) = x;
+    *reinterpret_cast<uint4*>(vb + d * Lay::VSTRIDE + 2 * tv) = vx;
   };
   auto stage = [&](int s, int buf, const Words& w) {
     uint8_t* kb = lds + buf * Lay::BUF;
     uint8_t* vb = kb + Lay::KBYTES;
     const int t0 = kStepTokens * s;
-    if (tid < Lay::WORDS) stage_word(tid, t0, kb, vb, w.k0, w.v0);
-    if constexpr (Lay::PER_THREAD > 1)
-      if (tid + NTHR < Lay::WORDS) stage_word(tid + NTHR, t0, kb, vb, w.k1, w.v1);
+    stage_word(tid, t0, kb, vb, w.k0, w.v0);
+    if constexpr (PT > 1) stage_word(tid + NTHR, t0, kb, vb, w.k1, w.v1);
+    if constexpr (PT > 2) stage_word(tid + 2 * NTHR, t0, kb, vb, w.k2, w.v2);
+    if constexpr (PT > 3) stage_word(tid + 3 * NTHR, t0, kb, vb, w.k3, w.v3);
   };
 
-  // ---- products of one step for this wave's two tiles
+  // ---- products of one step for this wave's tiles
   const int krow0 = 16 * (col >> 3) + 8 * ((col >> 2) & 1) + (col & 3);
-  auto compute = [&](int s, int buf) {
-    const int t0 = kStepTokens * s;
-    if (!has_rows || t0 >= end_hi) return;
+  const float qs = a.qk_scale_log2;
+  // scores of step s (unscaled) for this wave's tiles, from LDS buffer buf
+  auto scores = [&](int buf, f32x4 (&S)[TPW][2]) {
     const uint8_t* kb = lds + buf * Lay::BUF;
-    const uint8_t* vb = kb + Lay::KBYTES;
-    f32x4 S[2][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < TPW; ++u)
 #pragma unroll
       for (int m = 0; m < 2; ++m) S[u][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -342,17 +358,21 @@ __global__ __launch_bounds__(64 * kChunkWaves, 2) void chunk_kernel(MultiArgs a)
         const int row = krow0 + 4 * m;
         const V8 kA = as_vec8<V8>(*reinterpret_cast<const uint4*>(
             kb + row * Lay::KSTRIDE + 16 * kswz<D>(row, 4 * cc + grp)));
-        S[0][m] = M::mma(kA, qB[0][cc], S[0][m]);
-        S[1][m] = M::mma(kA, qB[1][cc], S[1][m]);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) S[u][m] = M::mma(kA, qB[u][cc], S[u][m]);
       }
+  };
+  // online softmax of step s's scores and the P.V products, V from LDS buffer buf
+  auto softmax_pv = [&](int s, int buf, const f32x4 (&S)[TPW][2]) {
+    const int t0 = kStepTokens * s;
+    const uint8_t* vb = lds + buf * Lay::BUF + Lay::KBYTES;
     const bool partial = t0 + kStepTokens > end_lo;          // wave-uniform
     const int tb = t0 + 8 * grp;
     // Scores stay unscaled until the exponent: the largest scaled score is the scaled largest
     // (or smallest, for a negative scale) raw one, and exp2(fma(s, scale, -m)) saves a pass.
-    const float qs = a.qk_scale_log2;
-    V8 pHi[2], pLo[2];
+    V8 pHi[TPW], pLo[TPW];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < TPW; ++u) {
       float sc[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) sc[jj] = S[u][jj >> 2][jj & 3];
@@ -406,55 +426,117 @@ __global__ __launch_bounds__(64 * kChunkWaves, 2) void chunk_kernel(MultiArgs a)
       const V8 vA = as_vec8<V8>(*reinterpret_cast<const uint4*>(
           vb + (16 * t + col) * Lay::VSTRIDE + 16 * grp));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < TPW; ++u) {
         acc[u][t] = M::mma(vA, pHi[u], acc[u][t]);
         if constexpr (SPLIT_P) acc[u][t] = M::mma(vA, pLo[u], acc[u][t]);
       }
     }
   };
 
-  // Two steps ahead: step s is computed from LDS buffer s % 2 while step s + 1 is staged from
-  // registers into the other buffer and step s + 2 is being loaded into the registers step s
-  // has left; the loop is unrolled by two so that each register set keeps its registers.
-  if (nsteps > 0) fetch(0, wa);
-  if (nsteps > 1) fetch(1, wb);
-  if (nsteps > 0) stage(0, 0, wa);
-  __syncthreads();
-  for (int s = 0; s < nsteps;) {
-    if (s + 2 < nsteps) fetch(s + 2, wa);
-    compute(s, 0);
-    if (s + 1 < nsteps) stage(s + 1, 1, wb);
+  const int se = s0 + nsteps;
+  auto active = [&](int s) { return has_rows && kStepTokens * s < end_hi; };
+  if constexpr (BUFS == 3) {
+    // Software pipeline (step s in buffer (s - s0) % 3): iteration s issues the score products
+    // of step s + 1 before the softmax and P.V products of step s, so the matrix cores have
+    // independent work while the softmax runs; it then stores step s + 2 into the buffer step
+    // s - 1 has left and loads step s + 4 into the registers step s + 2 has left (two register
+    // sets; the loop is unrolled by two so each keeps its registers).  A wave whose rows see
+    // none of a step's keys skips its products.
+    auto buf_of = [&](int s) { return (s - s0) % 3; };
+    if (s0 < se) fetch(s0, wa);
+    if (s0 + 1 < se) fetch(s0 + 1, wb);
+    if (s0 < se) stage(s0, 0, wa);
+    if (s0 + 2 < se) fetch(s0 + 2, wa);
+    if (s0 + 1 < se) stage(s0 + 1, 1, wb);
+    if (s0 + 3 < se) fetch(s0 + 3, wb);
     __syncthreads();
-    if (++s >= nsteps) break;
-    if (s + 2 < nsteps) fetch(s + 2, wb);
-    compute(s, 1);
-    if (s + 1 < nsteps) stage(s + 1, 0, wa);
+    f32x4 Sa[TPW][2], Sb[TPW][2];
+    if (s0 < se && active(s0)) scores(0, Sa);
+    auto iteration = [&](int s, f32x4 (&Sc)[TPW][2], f32x4 (&Sn)[TPW][2], Words& w) {
+      if (s + 1 < se && active(s + 1)) scores(buf_of(s + 1), Sn);
+      if (active(s)) softmax_pv(s, buf_of(s), Sc);
+      if (s + 2 < se) stage(s + 2, buf_of(s + 2), w);
+      if (s + 4 < se) fetch(s + 4, w);
+      __syncthreads();
+    };
+    for (int s = s0; s < se;) {
+      iteration(s, Sa, Sb, wa);
+      if (++s >= se) break;
+      iteration(s, Sb, Sa, wb);
+      ++s;
+    }
+  } else {
+    // Two buffers (step s in buffer (s - s0) % 2): step s is computed while step s + 1 is
+    // stored from registers into the other buffer and step s + 2 is loaded into the registers
+    // step s has left; unrolled by two for the register sets.
+    if (s0 < se) fetch(s0, wa);
+    if (s0 + 1 < se) fetch(s0 + 1, wb);
+    if (s0 < se) stage(s0, 0, wa);
     __syncthreads();
-    ++s;
+    auto iteration = [&](int s, int buf, Words& wn, Words& wf) {
+      if (s + 2 < se) fetch(s + 2, wf);
+      if (active(s)) {
+        f32x4 S[TPW][2];
+        scores(buf, S);
+        softmax_pv(s, buf, S);
+      }
+      if (s + 1 < se) stage(s + 1, buf ^ 1, wn);
+      __syncthreads();
+    };
+    for (int s = s0; s < se;) {
+      iteration(s, 0, wb, wa);
+      if (++s >= se) break;
+      iteration(s, 1, wa, wb);
+      ++s;
+    }
   }
 
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < TPW; ++u) {
     const float lsum = sum_across_rows(l_run[u]);
     if (!real[u]) continue;
-    const float l = lsum > 0.0f ? lsum : 1.0f;
-    E* out = reinterpret_cast<E*>(a.out) + orow[u] * D + 4 * grp;
+    if (NP == 1) {
+      // a row without keys (before the context) has l = 0 and acc = 0: output zeros
+      const float l = lsum > 0.0f ? lsum : 1.0f;
+      E* out = reinterpret_cast<E*>(a.out) + orow[u] * D + 4 * grp;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      *reinterpret_cast<uint2*>(out + 16 * t) =
-          make_uint2(pack2<QT>(acc[u][t][0] / l, acc[u][t][1] / l),
-                     pack2<QT>(acc[u][t][2] / l, acc[u][t][3] / l));
+      for (int t = 0; t < NT; ++t)
+        *reinterpret_cast<uint2*>(out + 16 * t) =
+            make_uint2(pack2<QT>(acc[u][t][0] / l, acc[u][t][1] / l),
+                       pack2<QT>(acc[u][t][2] / l, acc[u][t][3] / l));
+    } else {
+      const size_t pi = orow[u] * NP + part;
+      if (grp == 0) {
+        a.ws_ml[2 * pi] = m_run[u];
+        a.ws_ml[2 * pi + 1] = lsum;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        *reinterpret_cast<f32x4*>(a.ws_acc + pi * D + 16 * t + 4 * grp) = acc[u][t];
+    }
   }
+}
+
+template <int D, int QT, int W, int TPW, int BUFS>
+static hipError_t launch_chunk(const MultiArgs& a, hipStream_t stream) {
+  const long long wgs = (a.total_items + 7) / 8 * 8;
+  hipLaunchKernelGGL((chunk_kernel<D, QT, W, TPW, BUFS>), dim3((unsigned)wgs), dim3(64 * W), 0,
+                     stream, a);
+  return hipGetLastError();
 }
 
 template <int D, int QT, int KVT>
 static hipError_t launch_multi_t(const MultiArgs& a, hipStream_t stream) {
   if constexpr (KVT != DT_FP8) {
     if (a.row_blocks > 0) {
-      long long wgs = (long long)a.batch * a.num_kv_heads * a.row_blocks;
-      wgs = (wgs + 7) / 8 * 8;
-      hipLaunchKernelGGL((chunk_kernel<D, QT>), dim3((unsigned)wgs), dim3(64 * kChunkWaves), 0,
-                         stream, a);
+      const hipError_t e =
+          a.chunk_wide
+              ? launch_chunk<D, QT, kChunkWide.waves, kChunkWide.tiles, 3>(a, stream)
+              : launch_chunk<D, QT, kChunkNarrow.waves, kChunkNarrow.tiles, 2>(a, stream);
+      if (e != hipSuccess || a.num_parts == 1) return e;
+      const long long waves = (long long)a.batch * a.max_query_len * a.num_q_heads;
+      hipLaunchKernelGGL((multi_merge_kernel<D, QT>), dim3((unsigned)((waves + 3) / 4)),
+                         dim3(256), 0, stream, a);
       return hipGetLastError();
     }
   }

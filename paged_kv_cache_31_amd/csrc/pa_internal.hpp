@@ -143,46 +143,44 @@ struct MultiArgs {
   int num_parts;
   int part_blocks;             // even
   long long total_items;
-  int row_blocks;              // > 0: chunk_kernel, this many blocks of kChunkRows rows per head
+  int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
+  int chunk_wide;              // chunk_kernel shape: 1 kChunkWide, 0 kChunkNarrow
   float qk_scale_log2;
 };
 
 constexpr int kMultiWaves = 4;             // waves per multi_kernel workgroup
-constexpr long kMultiTargetWaves = 4096;   // items the automatic partition aims for
+constexpr long kMultiTargetWaves = 4096;   // waves the automatic partition aims for (multi_kernel)
+// chunk_kernel (narrow): one round of resident workgroups, 4 per CU of 2 waves on 256 CUs; a
+// round and a half (one partition more) was measured 17% slower, two rounds 6%
+constexpr long kChunkTargetWaves = 2048;
 constexpr int kMultiMinPartBlocks = 16;    // automatic partitions are at least 256 tokens
 
-// Many rows per (sequence, KV head) -- prefill chunks -- go to chunk_kernel: a workgroup takes
-// kChunkRows rows of one head and stages each K/V step once in LDS for all of them.
-constexpr int kChunkWaves = 4;
-constexpr int kChunkRows = 32 * kChunkWaves;
+// Heads with more than one MFMA tile of query rows go to chunk_kernel: a workgroup takes a block
+// of rows of one head and stages each K/V step once in LDS for all of them.  Two shapes:
+// kChunkWide (4 waves x 2 tiles = 128 rows, prefill chunks) and kChunkNarrow (2 waves x 1 tile
+// = 32 rows, a few tokens per sequence such as speculative verification).
+struct ChunkShape {
+  int waves, tiles;            // waves per workgroup, 16-column tiles per wave
+};
+constexpr ChunkShape kChunkWide = {4, 2};
+constexpr ChunkShape kChunkNarrow = {2, 1};
 
 struct MultiPlan {
   int tiles_per_head, num_parts, part_blocks;
-  long long items;
-  int row_blocks;              // > 0: chunk_kernel
+  long long items;             // waves (multi_kernel) or workgroups (chunk_kernel)
+  int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
+  int chunk_wide;              // chunk_kernel shape: 1 wide, 0 narrow
 };
-// A pure function of the descriptor, so the workspace size is known without a GPU.
-inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_query_len,
-                            int len_cap, int partition_tokens, bool kv_fp8) {
-  MultiPlan p;
-  const long long rows = (long long)max_query_len * group;
-  if (partition_tokens == 0 && !kv_fp8 && rows >= kChunkRows) {
-    p.row_blocks = (int)((rows + kChunkRows - 1) / kChunkRows);
-    p.tiles_per_head = 0;
-    p.num_parts = 1;
-    p.part_blocks = 0;
-    p.items = (long long)batch * num_kv_heads * p.row_blocks;
-    return p;
-  }
-  p.row_blocks = 0;
-  p.tiles_per_head = (int)(((long long)max_query_len * group + 15) / 16);
-  const long long maxblk = ((long long)len_cap + kBlock - 1) / kBlock;
+
+// Key partitions for `base` independent units so that about `target` units run, each at least
+// kMultiMinPartBlocks blocks long; part_blocks is even.
+inline void multi_parts(MultiPlan& p, long long base, long long target, long long maxblk,
+                        int partition_tokens) {
   long long pb;
   if (partition_tokens > 0) {
     pb = partition_tokens / kBlock;
   } else {
-    const long long base = (long long)batch * num_kv_heads * (p.tiles_per_head > 0 ? p.tiles_per_head : 1);
-    long long np = (kMultiTargetWaves + base - 1) / base;
+    long long np = (target + base - 1) / (base > 0 ? base : 1);
     const long long np_max = (maxblk + kMultiMinPartBlocks - 1) / kMultiMinPartBlocks;
     if (np > np_max) np = np_max;
     if (np < 1) np = 1;
@@ -194,7 +192,35 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
   if (np < 1) np = 1;
   p.part_blocks = (int)pb;
   p.num_parts = (int)np;
-  p.items = (long long)batch * num_kv_heads * np * p.tiles_per_head;
+}
+
+// A pure function of the descriptor, so the workspace size is known without a GPU.
+inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_query_len,
+                            int len_cap, int partition_tokens, bool kv_fp8) {
+  MultiPlan p;
+  const long long rows = (long long)max_query_len * group;
+  const long long maxblk = ((long long)len_cap + kBlock - 1) / kBlock;
+  p.tiles_per_head = (int)((rows + 15) / 16);
+  p.row_blocks = 0;
+  p.chunk_wide = 0;
+  if (partition_tokens == 0 && !kv_fp8 && rows > 16) {
+    const ChunkShape c = rows > 64 ? kChunkWide : kChunkNarrow;
+    const int block_rows = 16 * c.waves * c.tiles;
+    p.chunk_wide = rows > 64 ? 1 : 0;
+    p.row_blocks = (int)((rows + block_rows - 1) / block_rows);
+    const long long base = (long long)batch * num_kv_heads * p.row_blocks;
+    if (p.chunk_wide) {
+      p.num_parts = 1;
+      p.part_blocks = (int)(maxblk + (maxblk & 1));
+    } else {
+      multi_parts(p, base, kChunkTargetWaves / c.waves, maxblk, 0);
+    }
+    p.items = base * p.num_parts;
+    return p;
+  }
+  multi_parts(p, (long long)batch * num_kv_heads * (p.tiles_per_head > 0 ? p.tiles_per_head : 1),
+              kMultiTargetWaves, maxblk, partition_tokens);
+  p.items = (long long)batch * num_kv_heads * p.num_parts * p.tiles_per_head;
   return p;
 }
 inline size_t multi_workspace_bytes(const MultiPlan& p, int total_queries, int num_q_heads,
