@@ -1,0 +1,152 @@
+"""A serving loop over the whole library, step by step against the oracle.
+
+Requests arrive and finish while others decode (continuous batching: kasblo.com vLLM explainer,
+"continuous batchingは別の問題を解く"); each takes its prompt's blocks from the pool, grows one
+block at a time and returns them when it ends ("blockはrequestの成長に合わせて割り当てる"); some are
+forked into two samples that share their blocks until one writes ("block共有とAutomatic Prefix
+Caching").  Every step runs the copies the pool asked for (pa_copy_blocks) and the fused append +
+decode of every live sequence (pa_decode_append); the last step verifies three draft tokens per
+sequence (pa_kv_append + pa_decode_multi).  After every step the caches must equal the oracle's
+bit for bit, the outputs must be within tolerance, and the pool's counts must match the model's."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_31_amd as pa
+import workloads
+from gpu_util import assert_close, dev_bits, host_bits
+
+pytestmark = pytest.mark.gpu
+BLOCK = 16
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_continuous_batching_with_forks(dt):
+    rng = np.random.default_rng(400)
+    NB, Hkv, G, D, MB = 400, 2, 4, 128, 40
+    Hq = Hkv * G
+    scale = np.float32(1 / np.sqrt(D))
+    # (arrival step, prompt length, tokens to generate, fork into two samples)
+    requests = [(0, 37, 9, False), (0, 16, 12, True), (0, 130, 20, False), (1, 1, 10, False),
+                (2, 64, 7, True), (3, 250, 8, False), (5, 15, 10, True), (6, 90, 12, False)]
+    pool, model = pa.BlockPool(NB), oracle.BlockPoolModel(NB)
+    k = workloads.storage_bits(rng.standard_normal((NB, Hkv, BLOCK, D)), dt)
+    v = workloads.storage_bits(rng.standard_normal((NB, Hkv, D, BLOCK)), dt)
+    kd, vd = dev_bits(k, dt), dev_bits(v, dt)
+    live = []                                     # [table, length, tokens left]
+
+    def counts_agree():
+        assert np.array_equal(np.array([pool.refcount(b) for b in range(NB)]), model.ref)
+
+    for step in range(12):
+        # admissions: prefill the prompt's K/V through the pool's slots
+        slots = []
+        for arr, plen, gen, fork in requests:
+            if arr != step:
+                continue
+            t = []
+            for pos in range(plen):
+                slots.append(pool.slot_for(t, pos, MB)[0])
+            model.take(t)
+            live.append([t, plen, gen])
+            if fork:
+                child = list(t)
+                pool.share(child)
+                model.share(child)
+                live.append([child, plen, gen])
+        if slots:
+            kn = workloads.storage_bits(rng.standard_normal((len(slots), Hkv, D)), dt)
+            vn = workloads.storage_bits(rng.standard_normal((len(slots), Hkv, D)), dt)
+            pa.pa_kv_append(dev_bits(kn, dt), dev_bits(vn, dt), torch.tensor(slots).cuda(), kd, vd)
+            k, v = oracle.kv_append(k, v, kn, vn, np.array(slots))
+        counts_agree()
+
+        # one decode step of every live sequence: slots, copies, fused append + attention
+        pairs, slots = [], []
+        for seq in live:
+            t, L = seq[0], seq[1]
+            slot, copy = pool.slot_for(t, L, MB)
+            if copy is not None:
+                assert model.write(*copy)
+                pairs.append(copy)
+            elif L % BLOCK == 0:
+                model.take([t[-1]])
+            else:
+                assert not model.write(t[L // BLOCK], t[L // BLOCK])
+            slots.append(slot)
+            seq[1] += 1
+        counts_agree()
+        if pairs:
+            pa.pa_copy_blocks(torch.tensor(pairs, dtype=torch.int32).cuda(), kd, vd)
+            k, v, _, _ = oracle.copy_blocks(k, v, None, None, pairs)
+        B = len(live)
+        kn = workloads.storage_bits(rng.standard_normal((B, Hkv, D)), dt)
+        vn = workloads.storage_bits(rng.standard_normal((B, Hkv, D)), dt)
+        qb = workloads.storage_bits(rng.standard_normal((B, Hq, D)), dt)
+        tab = np.zeros((B, MB), dtype=np.int32)
+        for i, seq in enumerate(live):
+            tab[i, :len(seq[0])] = seq[0]
+        lens = np.array([seq[1] for seq in live], dtype=np.int32)
+        out = torch.empty_like(dev_bits(qb, dt))
+        pa.pa_decode_append(dev_bits(qb, dt), dev_bits(kn, dt), dev_bits(vn, dt), kd, vd,
+                            torch.from_numpy(tab).cuda(), torch.from_numpy(lens).cuda(),
+                            float(scale), out)
+        torch.cuda.synchronize()
+        k, v = oracle.kv_append(k, v, kn, vn, np.array(slots))
+        assert np.array_equal(host_bits(kd), k) and np.array_equal(host_bits(vd), v), step
+        ref = oracle.decode(qb, k, v, tab, lens, scale, dt, dt)
+        assert_close(host_bits(out), ref, dt, f"step {step} ({B} sequences)")
+
+        # finished requests give their blocks back
+        for seq in [s for s in live if s[2] == 1]:
+            pool.release(seq[0])
+            model.release(seq[0])
+        live = [s for s in live if s[2] > 1]
+        for seq in live:
+            seq[2] -= 1
+        counts_agree()
+
+    # a verification pass: three draft tokens per live sequence, causal over the cache
+    assert live
+    T = 3
+    slots, pairs = [], []
+    for seq in live:
+        for j in range(T):
+            slot, copy = pool.slot_for(seq[0], seq[1] + j, MB)
+            if copy is not None:
+                assert model.write(*copy)
+                pairs.append(copy)
+            elif (seq[1] + j) % BLOCK == 0:
+                model.take([seq[0][-1]])
+            slots.append(slot)
+        seq[1] += T
+    counts_agree()
+    if pairs:
+        pa.pa_copy_blocks(torch.tensor(pairs, dtype=torch.int32).cuda(), kd, vd)
+        k, v, _, _ = oracle.copy_blocks(k, v, None, None, pairs)
+    N = len(slots)
+    kn = workloads.storage_bits(rng.standard_normal((N, Hkv, D)), dt)
+    vn = workloads.storage_bits(rng.standard_normal((N, Hkv, D)), dt)
+    pa.pa_kv_append(dev_bits(kn, dt), dev_bits(vn, dt), torch.tensor(slots).cuda(), kd, vd)
+    k, v = oracle.kv_append(k, v, kn, vn, np.array(slots))
+    B = len(live)
+    tab = np.zeros((B, MB), dtype=np.int32)
+    for i, seq in enumerate(live):
+        tab[i, :len(seq[0])] = seq[0]
+    lens = np.array([seq[1] for seq in live], dtype=np.int32)
+    qs = np.arange(0, (B + 1) * T, T, dtype=np.int32)
+    qb = workloads.storage_bits(rng.standard_normal((N, Hq, D)), dt)
+    qd = dev_bits(qb, dt)
+    out = torch.empty_like(qd)
+    pa.pa_decode_multi(qd, torch.from_numpy(qs).cuda(), kd, vd, torch.from_numpy(tab).cuda(),
+                       torch.from_numpy(lens).cuda(), float(scale), out, T)
+    torch.cuda.synchronize()
+    ref = oracle.decode_multi(qb, qs, k, v, tab, lens, scale, dt, dt)
+    assert_close(host_bits(out), ref, dt, "verification pass")
+
+    for seq in live:
+        pool.release(seq[0])
+        model.release(seq[0])
+    assert pool.free_blocks() == NB == model.free_count()
