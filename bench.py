@@ -222,9 +222,9 @@ def bench_multi(args, dev) -> int:
     launch_s = e0.elapsed_time(e1) / 1e3 / args.steps
     log(f"{args.steps} back-to-back pa_decode_multi calls: {launch_s * 1e6:.1f} us each")
 
-    # the library's choice (pa_internal.hpp multi_plan): more than 16 rows per head, a 16-bit
-    # cache and no fixed partition take the LDS-staged chunk kernel
-    if P == 0 and s.kv_dtype != "fp8_e4m3" and maxT * (Hq // Hkv) > 16:
+    # the library's choice (pa_internal.hpp multi_plan): more than 16 rows per head and no fixed
+    # partition take the LDS-staged chunk kernel
+    if P == 0 and maxT * (Hq // Hkv) > 16:
         kernel = "chunk_kernel"
     else:
         kernel = "multi_kernel"
@@ -448,6 +448,7 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="a single-query workload (default) or a multi-query one: "
                          "verify_b64_h64kv8_d128_bf16_l128to8192_t4, "
+                         "verify_b4_h64kv8_d128_fp8_l32768_t4, "
                          "prefill_b4_h32kv8_d128_bf16_l4608_chunk512")
     ap.add_argument("--partition", type=int, default=None,
                     help="key-partition tokens (default: the workload's, else the library's)")

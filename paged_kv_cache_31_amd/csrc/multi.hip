@@ -182,18 +182,21 @@ __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
 // past the context end are zeroed when staged, so garbage in the last block's unused slots never
 // reaches the products.  With several key partitions the unnormalised result and its (max,
 // exp-sum) go to the workspace for multi_merge_kernel, as in multi_kernel.
-template <int D, int W>
+template <int D, int W, int EB>
 struct ChunkLds {
   // K token rows are unpadded; their 16-byte chunks are permuted per row (kswz) so that the 16
   // rows one operand read touches (rows 0-3, 8-11, 16-19, 24-27 of the step) fall on distinct
-  // banks.  With 2*D-byte rows, rows r and r + 16 would otherwise share banks.
+  // banks.  With 2*D-byte rows, rows r and r + 16 would otherwise share banks.  LDS always holds
+  // 16-bit elements (fp8 codes are widened, exactly, when staged); the fp8 block scales of the
+  // step (K then V, for its two blocks) follow the V tile.
   static constexpr int KSTRIDE = 2 * D;                      // bytes per K token row
   static constexpr int VSTRIDE = 2 * kStepTokens + 16;       // bytes per V dimension row
   static constexpr int KBYTES = kStepTokens * KSTRIDE;
-  static constexpr int BUF = KBYTES + D * VSTRIDE;
-  static constexpr int WORDS = 2 * kBlock * D * 2 / 16;      // 16-byte words of K (or V) a step
-  static constexpr int PER_THREAD = WORDS / (64 * W);
-  static_assert(WORDS % (64 * W) == 0, "whole words per thread");
+  static constexpr int SCALES = KBYTES + D * VSTRIDE;        // 4 floats: k0, k1, v0, v1
+  static constexpr int BUF = SCALES + 16;
+  static constexpr int WORDS = 2 * kBlock * D * EB / 16;     // 16-byte words of K (or V) a step
+  static constexpr int PER_THREAD = (WORDS + 64 * W - 1) / (64 * W);
+  static_assert(WORDS % (64 * W) == 0 || WORDS < 64 * W, "whole words per thread");
 };
 
 // chunk index of 16-byte chunk c of K token row r in LDS
@@ -203,18 +206,20 @@ __device__ __forceinline__ int kswz(int r, int c) {
   else return c ^ (((r >> 1) & 1) | (((r >> 3) & 3) << 1));   // 8 chunks; rows alternate halves
 }
 
-template <int D, int QT, int W, int TPW, int BUFS>
+template <int D, int QT, int KVT, int W, int TPW, int BUFS>
 __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
   typedef Mfma<QT> M;
   typedef typename M::vec8 V8;
   typedef typename M::elem E;
-  typedef ChunkLds<D, W> Lay;
+  constexpr bool FP8 = KVT == DT_FP8;
+  constexpr int EB = FP8 ? 1 : 2;                            // bytes per cache element
+  typedef ChunkLds<D, W, EB> Lay;
   // bf16 P as a hi/lo pair: rounding it once was measured 20% faster on a 512-token prefill
   // chunk but misses the 2e-3 tolerance on short contexts
   constexpr bool SPLIT_P = QT == DT_BF16;
   constexpr int NC = D / 32;
   constexpr int NT = D / 16;
-  constexpr int TB = kBlock * D * 2;                         // bytes of one (block, head) tile
+  constexpr int TB = kBlock * D * EB;                        // bytes of one (block, head) tile
   constexpr int NTHR = 64 * W;
   constexpr int PT = Lay::PER_THREAD;
   constexpr int ROWS_W = 16 * TPW;                           // rows per wave
@@ -292,6 +297,7 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
   static_assert(PT >= 1 && PT <= 4, "one to four staged words per thread");
   struct Words {                                             // a step's words between load and store
     uint4 k0, v0, k1, v1, k2, v2, k3, v3;
+    float sk0, sk1, sv0, sv1;                                // fp8: the two blocks' scales
   };
   Words wa, wb;
   auto fetch_word = [&](int idx, int p0, int p1, uint4& kx, uint4& vx) {
@@ -305,12 +311,56 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
     int p0 = trow[jb0], p1 = trow[jb1];
     p0 = (unsigned)p0 < (unsigned)a.num_blocks ? p0 : 0;
     p1 = (unsigned)p1 < (unsigned)a.num_blocks ? p1 : 0;
+    if constexpr (FP8) {
+      if (tid == 0) {
+        w.sk0 = a.k_scale[(size_t)p0 * Hkv + kvh];
+        w.sk1 = a.k_scale[(size_t)p1 * Hkv + kvh];
+        w.sv0 = a.v_scale[(size_t)p0 * Hkv + kvh];
+        w.sv1 = a.v_scale[(size_t)p1 * Hkv + kvh];
+      }
+      if (Lay::WORDS < NTHR && tid >= Lay::WORDS) return;
+    }
     fetch_word(tid, p0, p1, w.k0, w.v0);
     if constexpr (PT > 1) fetch_word(tid + NTHR, p0, p1, w.k1, w.v1);
     if constexpr (PT > 2) fetch_word(tid + 2 * NTHR, p0, p1, w.k2, w.v2);
     if constexpr (PT > 3) fetch_word(tid + 3 * NTHR, p0, p1, w.k3, w.v3);
   };
+  // V halves of 8 tokens starting at token tv of the step: tokens at or past the end zeroed
+  auto keep_v = [&](uint4 x, int t0, int tv) {
+    const int valid = L - (t0 + tv);
+    if (valid < 8) {
+      auto keep = [&](int k) {
+        return (2 * k < valid ? 0x0000FFFFu : 0u) | (2 * k + 1 < valid ? 0xFFFF0000u : 0u);
+      };
+      x.x &= keep(0);
+      x.y &= keep(1);
+      x.z &= keep(2);
+      x.w &= keep(3);
+    }
+    return x;
+  };
+  auto widen16 = [&](uint32_t w0, uint32_t w1) {
+    return __builtin_bit_cast(uint4, fp8x8_to_vec8<QT>(w0, w1));
+  };
+  auto stage_word8 = [&](int idx, int t0, uint8_t* kb, uint8_t* vb, uint4 kx, uint4 vx) {
+    const int o = 16 * idx, blk = o / TB, off = o - blk * TB;
+    // K: 16 codes of one token row (dims cb .. cb + 15) -> two 16-byte chunks of 16-bit values
+    const int tok = off / D, cb = off - tok * D;
+    const int row = kBlock * blk + tok;
+    uint8_t* kr = kb + row * Lay::KSTRIDE;
+    *reinterpret_cast<uint4*>(kr + 16 * kswz<D>(row, cb / 8)) = widen16(kx.x, kx.y);
+    *reinterpret_cast<uint4*>(kr + 16 * kswz<D>(row, cb / 8 + 1)) = widen16(kx.z, kx.w);
+    // V: one dimension row of the block (16 tokens) -> its two 8-token halves
+    const int d = off / 16, tv = kBlock * blk;
+    uint8_t* vr = vb + d * Lay::VSTRIDE + 2 * tv;
+    *reinterpret_cast<uint4*>(vr) = keep_v(widen16(vx.x, vx.y), t0, tv);
+    *reinterpret_cast<uint4*>(vr + 16) = keep_v(widen16(vx.z, vx.w), t0, tv + 8);
+  };
   auto stage_word = [&](int idx, int t0, uint8_t* kb, uint8_t* vb, uint4 kx, uint4 vx) {
+    if constexpr (FP8) {
+      stage_word8(idx, t0, kb, vb, kx, vx);
+      return;
+    }
     const int o = 16 * idx, blk = o / TB, off = o - blk * TB;
     // K tile: token rows of 2*D bytes
     const int tok = off / (2 * D), cb = off - tok * (2 * D);
@@ -319,22 +369,17 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
     // V tile: dimension rows of 16 tokens (32 bytes); this word holds 8 of them
     const int d = off / 32, h = (off / 16) & 1;
     const int tv = kBlock * blk + 8 * h;
-    const int valid = L - (t0 + tv);                         // tokens of the word before the end
-    if (valid < 8) {
-      auto keep = [&](int k) {
-        return (2 * k < valid ? 0x0000FFFFu : 0u) | (2 * k + 1 < valid ? 0xFFFF0000u : 0u);
-      };
-      vx.x &= keep(0);
-      vx.y &= keep(1);
-      vx.z &= keep(2);
-      vx.w &= keep(3);
-    }
-    *reinterpret_cast<uint4*>(vb + d * Lay::VSTRIDE + 2 * tv) = vx;
+    *reinterpret_cast<uint4*>(vb + d * Lay::VSTRIDE + 2 * tv) = keep_v(vx, t0, tv);
   };
   auto stage = [&](int s, int buf, const Words& w) {
     uint8_t* kb = lds + buf * Lay::BUF;
     uint8_t* vb = kb + Lay::KBYTES;
     const int t0 = kStepTokens * s;
+    if constexpr (FP8) {
+      if (tid == 0)
+        *reinterpret_cast<float4*>(kb + Lay::SCALES) = make_float4(w.sk0, w.sk1, w.sv0, w.sv1);
+      if (Lay::WORDS < NTHR && tid >= Lay::WORDS) return;
+    }
     stage_word(tid, t0, kb, vb, w.k0, w.v0);
     if constexpr (PT > 1) stage_word(tid + NTHR, t0, kb, vb, w.k1, w.v1);
     if constexpr (PT > 2) stage_word(tid + 2 * NTHR, t0, kb, vb, w.k2, w.v2);
@@ -366,6 +411,14 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
   auto softmax_pv = [&](int s, int buf, const f32x4 (&S)[TPW][2]) {
     const int t0 = kStepTokens * s;
     const uint8_t* vb = lds + buf * Lay::BUF + Lay::KBYTES;
+    // fp8: this lane's 8 tokens lie in block grp / 2 of the step; its K scale multiplies the
+    // scores, its V scale the weights (after their sum is taken)
+    float ksc = 1.0f, vsc = 1.0f;
+    if constexpr (FP8) {
+      const float* scl = reinterpret_cast<const float*>(lds + buf * Lay::BUF + Lay::SCALES);
+      ksc = scl[grp >> 1];
+      vsc = scl[2 + (grp >> 1)];
+    }
     const bool partial = t0 + kStepTokens > end_lo;          // wave-uniform
     const int tb = t0 + 8 * grp;
     // Scores stay unscaled until the exponent: the largest scaled score is the scaled largest
@@ -376,6 +429,10 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
       float sc[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) sc[jj] = S[u][jj >> 2][jj & 3];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sc[jj] *= ksc;
+      }
       const float masked = qs >= 0.0f ? -INFINITY : INFINITY;
       if (partial) {
         const int nval = min(max(end_lane[u] - tb, 0), 8);
@@ -408,6 +465,10 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
       if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[u][t] *= alpha;
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pr[jj] *= vsc;
       }
       uint32_t h[4], lo[4];
 #pragma unroll
@@ -517,28 +578,26 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
   }
 }
 
-template <int D, int QT, int W, int TPW, int BUFS>
+template <int D, int QT, int KVT, int W, int TPW, int BUFS>
 static hipError_t launch_chunk(const MultiArgs& a, hipStream_t stream) {
   const long long wgs = (a.total_items + 7) / 8 * 8;
-  hipLaunchKernelGGL((chunk_kernel<D, QT, W, TPW, BUFS>), dim3((unsigned)wgs), dim3(64 * W), 0,
-                     stream, a);
+  hipLaunchKernelGGL((chunk_kernel<D, QT, KVT, W, TPW, BUFS>), dim3((unsigned)wgs), dim3(64 * W),
+                     0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int QT, int KVT>
 static hipError_t launch_multi_t(const MultiArgs& a, hipStream_t stream) {
-  if constexpr (KVT != DT_FP8) {
-    if (a.row_blocks > 0) {
-      const hipError_t e =
-          a.chunk_wide
-              ? launch_chunk<D, QT, kChunkWide.waves, kChunkWide.tiles, 3>(a, stream)
-              : launch_chunk<D, QT, kChunkNarrow.waves, kChunkNarrow.tiles, 2>(a, stream);
-      if (e != hipSuccess || a.num_parts == 1) return e;
-      const long long waves = (long long)a.batch * a.max_query_len * a.num_q_heads;
-      hipLaunchKernelGGL((multi_merge_kernel<D, QT>), dim3((unsigned)((waves + 3) / 4)),
-                         dim3(256), 0, stream, a);
-      return hipGetLastError();
-    }
+  if (a.row_blocks > 0) {
+    const hipError_t e =
+        a.chunk_wide
+            ? launch_chunk<D, QT, KVT, kChunkWide.waves, kChunkWide.tiles, 3>(a, stream)
+            : launch_chunk<D, QT, KVT, kChunkNarrow.waves, kChunkNarrow.tiles, 2>(a, stream);
+    if (e != hipSuccess || a.num_parts == 1) return e;
+    const long long waves = (long long)a.batch * a.max_query_len * a.num_q_heads;
+    hipLaunchKernelGGL((multi_merge_kernel<D, QT>), dim3((unsigned)((waves + 3) / 4)),
+                       dim3(256), 0, stream, a);
+    return hipGetLastError();
   }
   long long wgs = (a.total_items + kMultiWaves - 1) / kMultiWaves;
   wgs = (wgs + 7) / 8 * 8;

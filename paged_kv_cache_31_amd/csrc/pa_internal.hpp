@@ -203,7 +203,8 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
   p.tiles_per_head = (int)((rows + 15) / 16);
   p.row_blocks = 0;
   p.chunk_wide = 0;
-  if (partition_tokens == 0 && !kv_fp8 && rows > 16) {
+  (void)kv_fp8;
+  if (partition_tokens == 0 && rows > 16) {
     const ChunkShape c = rows > 64 ? kChunkWide : kChunkNarrow;
     const int block_rows = 16 * c.waves * c.tiles;
     p.chunk_wide = rows > 64 ? 1 : 0;

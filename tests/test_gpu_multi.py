@@ -108,14 +108,19 @@ CHUNK = [
     ("f16", 2, 3, 128, (700, 77, 1025), (130, 77, 50)),
     ("bf16", 1, 8, 128, (40, 1000, 333), (40, 17, 300)),
     ("bf16", 2, 4, 64, (20, 600, 5), (64, 35, 32)),          # more queries than context
+    ("f16", 2, 8, 64, (300, 45, 1000), (8, 3, 5)),           # narrow shape, partitions
 ]
 
 
 @pytest.mark.parametrize("case", CHUNK, ids=lambda c: f"{c[0]}-kv{c[1]}g{c[2]}d{c[3]}")
-def test_prefill_chunk_shapes(case):
+@pytest.mark.parametrize("fp8", [False, True], ids=["16bit", "fp8"])
+def test_prefill_chunk_shapes(case, fp8):
+    """The same shapes over a 16-bit cache and over an fp8 one (codes widened when staged,
+    block scales applied per lane)."""
     qd, hkv, g, d, lens, T = case
-    m = Multi(qd, qd, hkv, g, d, lens, T, seed=110 + CHUNK.index(case), spare_rows=2)
-    m.check(m.run(), f"chunk {case}")
+    kv = "fp8_e4m3" if fp8 else qd
+    m = Multi(qd, kv, hkv, g, d, lens, T, seed=110 + CHUNK.index(case), spare_rows=2)
+    m.check(m.run(), f"chunk {case} {kv}")
 
 
 def test_more_queries_than_context_and_loose_bounds():

@@ -313,6 +313,10 @@ MULTI_SPECS: dict[str, tuple[Spec, int]] = {
     "verify_b64_h64kv8_d128_bf16_l128to8192_t4": (
         Spec("verify_b64_h64kv8_d128_bf16_l128to8192_t4", 64, 64, 8, 128, "bf16", "bf16",
              ("uniform", 128, 8192), seed=2), 4),
+    # Speculative verification on the long-context fp8 batch: 4 draft tokens per sequence.
+    "verify_b4_h64kv8_d128_fp8_l32768_t4": (
+        Spec("verify_b4_h64kv8_d128_fp8_l32768_t4", 4, 64, 8, 128, "bf16", "fp8_e4m3",
+             ("fixed", 32768), seed=4), 4),
     # Chunked prefill: 4 prompts whose next 512-token chunk runs against 4096 cached tokens.
     "prefill_b4_h32kv8_d128_bf16_l4608_chunk512": (
         Spec("prefill_b4_h32kv8_d128_bf16_l4608_chunk512", 4, 32, 8, 128, "bf16", "bf16",
