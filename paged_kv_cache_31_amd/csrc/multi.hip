@@ -119,7 +119,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // One wave per (sequence b, query token i, query head h): merges the num_parts partial results
 // of that row by log-sum-exp and writes the normalised output.  Every partition of a row's tile
-// was written by multi_kernel (an empty one as max -inf, sum 0, output 0).
+// was written by multi_kernel or chunk_kernel (an empty one as max -inf, sum 0, output 0).
 template <int D, int QT>
 __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
   typedef typename Mfma<QT>::elem E;
@@ -153,11 +153,18 @@ __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
     float s = 0.0f;
     for (int p = lane; p < NP; p += 64) s += fast_exp2(ml[2 * p] - M) * ml[2 * p + 1];
     den = wave_sum(s);
+    // Partitions without keys were written as max -inf, sum 0 and output 0, so they add
+    // exactly 0 here; no branch, so that the unrolled loads stay in flight together.
+#pragma unroll 8
     for (int p = 0; p < NP; ++p) {
       const float wt = fast_exp2(ml[2 * p] - M);
-      if (wt == 0.0f) continue;                        // partitions without keys
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) o[k] += wt * pacc[(size_t)p * D + lane * DPL + k];
+      if constexpr (DPL == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(pacc + (size_t)p * D + 2 * lane);
+        o[0] += wt * x.x;
+        o[1] += wt * x.y;
+      } else {
+        o[0] += wt * pacc[(size_t)p * D + lane];
+      }
     }
   }
   E* out = reinterpret_cast<E*>(a.out) + row * D + lane * DPL;
@@ -253,6 +260,7 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
   auto end_of = [&](int ii) { return min(window(ii), cap); };
   const int s0 = j0 >> 1;                                    // j0 is even
   const int nsteps = j1 > j0 ? ((j1 - j0 + 1) >> 1) : 0;
+  const int se_ = s0 + nsteps;                               // steps [s0, se_)
 
   // this wave's rows: TPW tiles of 16 columns; columns past the last row repeat it
   const int rw0 = r0 + ROWS_W * wave;
@@ -306,21 +314,24 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
     kx = *reinterpret_cast<const uint4*>(kc + tile);
     vx = *reinterpret_cast<const uint4*>(vc + tile);
   };
+  // Every fetch issues the same loads whatever the step (a step past the range reloads the last
+  // one; threads past the step's words reload a word), so that the count of loads in flight is
+  // the same on every path and the wait before staging a step leaves the later steps' loads in
+  // flight instead of draining them all.
   auto fetch = [&](int s, Words& w) {
+    s = max(min(s, se_ - 1), 0);      // an empty range reloads a block its table holds
     const int jb0 = 2 * s, jb1 = 2 * s + 1 < j1 ? 2 * s + 1 : 2 * s;
     int p0 = trow[jb0], p1 = trow[jb1];
     p0 = (unsigned)p0 < (unsigned)a.num_blocks ? p0 : 0;
     p1 = (unsigned)p1 < (unsigned)a.num_blocks ? p1 : 0;
     if constexpr (FP8) {
-      if (tid == 0) {
-        w.sk0 = a.k_scale[(size_t)p0 * Hkv + kvh];
-        w.sk1 = a.k_scale[(size_t)p1 * Hkv + kvh];
-        w.sv0 = a.v_scale[(size_t)p0 * Hkv + kvh];
-        w.sv1 = a.v_scale[(size_t)p1 * Hkv + kvh];
-      }
-      if (Lay::WORDS < NTHR && tid >= Lay::WORDS) return;
+      w.sk0 = a.k_scale[(size_t)p0 * Hkv + kvh];
+      w.sk1 = a.k_scale[(size_t)p1 * Hkv + kvh];
+      w.sv0 = a.v_scale[(size_t)p0 * Hkv + kvh];
+      w.sv1 = a.v_scale[(size_t)p1 * Hkv + kvh];
     }
-    fetch_word(tid, p0, p1, w.k0, w.v0);
+    const int t0w = Lay::WORDS < NTHR ? tid % Lay::WORDS : tid;
+    fetch_word(t0w, p0, p1, w.k0, w.v0);
     if constexpr (PT > 1) fetch_word(tid + NTHR, p0, p1, w.k1, w.v1);
     if constexpr (PT > 2) fetch_word(tid + 2 * NTHR, p0, p1, w.k2, w.v2);
     if constexpr (PT > 3) fetch_word(tid + 3 * NTHR, p0, p1, w.k3, w.v3);
@@ -504,12 +515,12 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
     // sets; the loop is unrolled by two so each keeps its registers).  A wave whose rows see
     // none of a step's keys skips its products.
     auto buf_of = [&](int s) { return (s - s0) % 3; };
-    if (s0 < se) fetch(s0, wa);
-    if (s0 + 1 < se) fetch(s0 + 1, wb);
+    fetch(s0, wa);
+    fetch(s0 + 1, wb);
     if (s0 < se) stage(s0, 0, wa);
-    if (s0 + 2 < se) fetch(s0 + 2, wa);
+    fetch(s0 + 2, wa);
     if (s0 + 1 < se) stage(s0 + 1, 1, wb);
-    if (s0 + 3 < se) fetch(s0 + 3, wb);
+    fetch(s0 + 3, wb);
     __syncthreads();
     f32x4 Sa[TPW][2], Sb[TPW][2];
     if (s0 < se && active(s0)) scores(0, Sa);
@@ -517,7 +528,7 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
       if (s + 1 < se && active(s + 1)) scores(buf_of(s + 1), Sn);
       if (active(s)) softmax_pv(s, buf_of(s), Sc);
       if (s + 2 < se) stage(s + 2, buf_of(s + 2), w);
-      if (s + 4 < se) fetch(s + 4, w);
+      fetch(s + 4, w);
       __syncthreads();
     };
     for (int s = s0; s < se;) {
@@ -530,12 +541,12 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
     // Two buffers (step s in buffer (s - s0) % 2): step s is computed while step s + 1 is
     // stored from registers into the other buffer and step s + 2 is loaded into the registers
     // step s has left; unrolled by two for the register sets.
-    if (s0 < se) fetch(s0, wa);
-    if (s0 + 1 < se) fetch(s0 + 1, wb);
+    fetch(s0, wa);
+    fetch(s0 + 1, wb);
     if (s0 < se) stage(s0, 0, wa);
     __syncthreads();
     auto iteration = [&](int s, int buf, Words& wn, Words& wf) {
-      if (s + 2 < se) fetch(s + 2, wf);
+      fetch(s + 2, wf);
       if (active(s)) {
         f32x4 S[TPW][2];
         scores(buf, S);
