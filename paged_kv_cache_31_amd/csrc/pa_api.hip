@@ -80,8 +80,7 @@ int multi_len_cap(const pa_multi_desc* d) {
 
 pa::MultiPlan multi_plan_of(const pa_multi_desc* d) {
   return pa::multi_plan(d->batch, d->cache.num_kv_heads, d->num_q_heads / d->cache.num_kv_heads,
-                        d->max_query_len, multi_len_cap(d), d->partition_tokens,
-                        d->cache.kv_dtype == PA_FP8_E4M3);
+                        d->max_query_len, multi_len_cap(d), d->partition_tokens);
 }
 
 // Upper bound of the flattened (sequence, KV head, block) space.

@@ -150,8 +150,9 @@ struct MultiArgs {
 
 constexpr int kMultiWaves = 4;             // waves per multi_kernel workgroup
 constexpr long kMultiTargetWaves = 4096;   // waves the automatic partition aims for (multi_kernel)
-// chunk_kernel (narrow): one round of resident workgroups, 4 per CU of 2 waves on 256 CUs; a
-// round and a half (one partition more) was measured 17% slower, two rounds 6%
+// chunk_kernel (narrow): one round of resident workgroups, 4 per CU of 2 waves on 256 CUs.
+// Measured on the two verification workloads with targets 512 ... 16384 waves: fewer leave CUs
+// idle (up to 2.3x slower), more add partitions and their partial results (5-50% slower).
 constexpr long kChunkTargetWaves = 2048;
 constexpr int kMultiMinPartBlocks = 16;    // automatic partitions are at least 256 tokens
 
@@ -196,14 +197,13 @@ inline void multi_parts(MultiPlan& p, long long base, long long target, long lon
 
 // A pure function of the descriptor, so the workspace size is known without a GPU.
 inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_query_len,
-                            int len_cap, int partition_tokens, bool kv_fp8) {
+                            int len_cap, int partition_tokens) {
   MultiPlan p;
   const long long rows = (long long)max_query_len * group;
   const long long maxblk = ((long long)len_cap + kBlock - 1) / kBlock;
   p.tiles_per_head = (int)((rows + 15) / 16);
   p.row_blocks = 0;
   p.chunk_wide = 0;
-  (void)kv_fp8;
   if (partition_tokens == 0 && rows > 16) {
     const ChunkShape c = rows > 64 ? kChunkWide : kChunkNarrow;
     const int block_rows = 16 * c.waves * c.tiles;
