@@ -283,3 +283,45 @@ def test_copy_blocks_rejects():
     assert call(c, ks=FAKE) == pa.PA_ERR_INVALID_ARG       # scales only for fp8
     assert call(c8) == pa.PA_ERR_INVALID_ARG               # fp8 needs them
     assert pa.status_string(pa.PA_ERR_OUT_OF_BLOCKS) == "no free block in the pool"
+
+
+def test_pool_rejects_bad_arguments_from_c():
+    """The pool's C entry points refuse null handles and pointers, sizes below zero and tables
+    naming blocks that are free or outside the pool, without changing the pool."""
+    lib = pa.lib()
+    i32, vp = ctypes.c_int32, ctypes.c_void_p
+    p = vp()
+    assert lib.pa_pool_create(0, ctypes.byref(p)) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_pool_create(8, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_pool_create(8, ctypes.byref(p)) == pa.PA_OK
+    try:
+        blocks = (i32 * 4)()
+        assert lib.pa_pool_alloc(None, 1, blocks) == pa.PA_ERR_INVALID_ARG
+        assert lib.pa_pool_alloc(p, -1, blocks) == pa.PA_ERR_INVALID_ARG
+        assert lib.pa_pool_alloc(p, 1, None) == pa.PA_ERR_INVALID_ARG
+        assert lib.pa_pool_alloc(p, 0, None) == pa.PA_OK          # nothing asked, nothing written
+        assert lib.pa_pool_alloc(p, 2, blocks) == pa.PA_OK
+        assert lib.pa_pool_free_blocks(p) == 6 and lib.pa_pool_free_blocks(None) == -1
+        assert lib.pa_pool_share(p, 1, None) == pa.PA_ERR_INVALID_ARG
+        assert lib.pa_pool_release(p, -2, blocks) == pa.PA_ERR_INVALID_ARG
+        t, c = i32(), i32()
+        assert lib.pa_pool_write(p, blocks[0], None, ctypes.byref(c)) == pa.PA_ERR_INVALID_ARG
+        assert lib.pa_pool_write(p, 7, ctypes.byref(t), ctypes.byref(c)) == pa.PA_ERR_INVALID_ARG
+        # slot_for: a table naming a free block, or a position that skips a block, is refused
+        table = (i32 * 4)(blocks[0], 7, 0, 0)
+        nb, slot, src, dst = i32(2), ctypes.c_int64(), i32(), i32()
+        args = lambda pos, n=ctypes.byref(nb): (p, table, n, 4, pos, ctypes.byref(slot),
+                                               ctypes.byref(src), ctypes.byref(dst))
+        assert lib.pa_pool_slot_for(*args(20)) == pa.PA_ERR_INVALID_ARG   # block 7 is free
+        table[1] = blocks[1]
+        assert lib.pa_pool_slot_for(*args(48)) == pa.PA_ERR_INVALID_ARG   # skips block 2
+        assert lib.pa_pool_slot_for(*args(5, None)) == pa.PA_ERR_INVALID_ARG
+        nb.value = 5
+        assert lib.pa_pool_slot_for(*args(5)) == pa.PA_ERR_INVALID_ARG    # more than max_blocks
+        nb.value = 2
+        assert lib.pa_pool_slot_for(*args(32)) == pa.PA_OK                # opens block 2
+        assert nb.value == 3 and slot.value == table[2] * 16 and src.value == -1
+        assert [lib.pa_pool_refcount(p, b) for b in range(8)].count(1) == 3
+    finally:
+        assert lib.pa_pool_destroy(p) == pa.PA_OK
+    assert lib.pa_pool_destroy(None) == pa.PA_OK
