@@ -280,8 +280,6 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
   typedef typename St::E E;
   constexpr int NC = St::NC;
   constexpr int NT = St::NT;
-  // the merge phase gives wave w the 16-dim tiles w, w + kWaves, ... (none when w >= NT)
-  constexpr int TPW = (NT + kWaves - 1) / kWaves;
 
   __shared__ int sm_wave_sum[kWaves];
   __shared__ int sm_start_b[kWaves], sm_start_off[kWaves], sm_start_L[kWaves];
@@ -445,97 +443,134 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
   }
   __syncthreads();
 
-  // ---- 3. Merge the cut pieces of the workgroup's chunks, in chunk order.  Each wave now
-  // handles tiles wave, wave + kWaves, ... of every piece.  A group of parts of one sequence
-  // head that covers all its blocks is written out.  A group cut at the workgroup boundary (at
-  // most two: one continuing from before the range, one running past its end) is published;
-  // then, after one wait and one round of arrival counts for both, the last workgroup to publish
-  // a part of a sequence head merges all of them.
+  // ---- 3. Merge the cut pieces of the workgroup's chunks.  The slots (each wave's first and
+  // last piece, in chunk order) of one sequence head are consecutive among the used slots and
+  // form a group.  The waves take the groups in turn (wave w: groups w, w + kWaves, ...) and
+  // merge all 16-dim tiles of a group, so groups are merged in parallel and the per-group work
+  // (slot search, weights) is done once.  A group that covers all blocks of its sequence head is
+  // written out.  A group cut
+  // at the workgroup boundary (at most two: the first group, continuing from before the range,
+  // and the last, running past its end) is published; then, after one wait and one round of
+  // arrival counts for both, the last workgroup to publish a part of a sequence head merges all
+  // of them.
   const int WGB = kWaves * Cw;                      // blocks per workgroup range
-  int gb = -1, gkvh = 0, gj0 = 0, gj1 = 0, gnblk = 0, gskip = 0, gs0 = 0;
-  float gm = -INFINITY, gl = 0.0f;
-  f32x4 go[TPW];
-  auto tile_of = [&](int t) { return wave + kWaves * t; };   // < NT: this wave's t-th tile
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) go[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int NS = 2 * kWaves;                    // slots
+  static_assert(NS <= 64, "one slot per lane");
+  PieceMeta mt{-1, 0, 0, 0, 0, 0, 0};
+  if (lane < NS) mt = sm_meta[lane >> 1][lane & 1];
+  const bool used = lane < NS && mt.b >= 0;
+  const uint64_t used_mask = __ballot(used);
+  const uint64_t before_me = used_mask & ((1ull << lane) - 1ull);
+  const int prev = before_me ? 63 - __clzll((long long)before_me) : lane;
+  const int prev_b = __shfl(mt.b, prev), prev_kvh = __shfl(mt.kvh, prev);
+  const uint64_t start_mask =
+      __ballot(used && (prev == lane || prev_b != mt.b || prev_kvh != mt.kvh));
+  const int ngroups = __popcll(start_mask);
+  // group index of this lane's slot (lane 63: the shift gives 0 and the mask all ones)
+  const int gid = __popcll(start_mask & ((2ull << lane) - 1ull)) - 1;
 
-  // the cut groups this workgroup publishes (at most two), field by field in registers
-  int npub = 0, pb_b[2] = {0, 0}, pb_kvh[2] = {0, 0}, pb_skip[2] = {0, 0}, pb_s0[2] = {0, 0};
-  int pb_c0[2] = {0, 0}, pb_c1[2] = {0, 0};
-
-  auto emit = [&]() {
-    if (gj0 == gskip && gj1 == gnblk) {
-      if (col < G && wave < NT) {
-        const size_t row = (size_t)gb * Hq + gkvh * G + col;
-        if (gskip > 0) fold_prefix<D>(a, row, prefix_parts(gskip), grp, wave, kWaves, gm, gl, go);
-        E* out = reinterpret_cast<E*>(a.out) + row * D + 4 * grp;
-#pragma unroll
-        for (int t = 0; t < TPW; ++t)
-          if (tile_of(t) < NT)
-            *reinterpret_cast<uint2*>(out + 16 * tile_of(t)) =
-                make_uint2(pack2<QT>(go[t][0] / gl, go[t][1] / gl),
-                           pack2<QT>(go[t][2] / gl, go[t][3] / gl));
-      }
-    } else {
-      // slot 1 holds the group whose sequence head starts strictly inside this workgroup's
-      // range (it runs past the end); slot 0 the one that started at or before the range start
-      const int wslot = gs0 > (int)blockIdx.x * WGB ? 1 : 0;
-      const size_t ps = ((size_t)blockIdx.x * 2 + wslot) * G + col;
-      if (col < G) {                                // device-coherent stores
-#pragma unroll
-        for (int t = 0; t < TPW; ++t)
-          if (tile_of(t) < NT)
-            store_coherent(a.ws_acc + ps * D + 16 * tile_of(t) + 4 * grp, go[t]);
-        if (wave == 0 && grp == 0) {
-          store_coherent(a.ws_ml + ps * 2, gm);
-          store_coherent(a.ws_ml + ps * 2 + 1, gl);
-        }
-      }
-      const int c0 = gs0 / WGB, c1 = (gs0 + (gnblk - gskip) - 1) / WGB;
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-        if (x == npub) {
-          pb_b[x] = gb;
-          pb_kvh[x] = gkvh;
-          pb_skip[x] = gskip;
-          pb_s0[x] = gs0;
-          pb_c0[x] = c0;
-          pb_c1[x] = c1;
-        }
-      ++npub;
-    }
+  struct Group {
+    uint64_t slots;
+    int b, kvh, j0, j1, nblk, skip, s0;
+    bool whole;
+  };
+  auto group = [&](int g) {
+    Group r;
+    r.slots = __ballot(used && gid == g);
+    const int f = __builtin_ctzll(r.slots), l = 63 - __builtin_clzll(r.slots);
+    r.b = __builtin_amdgcn_readlane(mt.b, f);
+    r.kvh = __builtin_amdgcn_readlane(mt.kvh, f);
+    r.j0 = __builtin_amdgcn_readlane(mt.j0, f);
+    r.j1 = __builtin_amdgcn_readlane(mt.j1, l);
+    r.nblk = __builtin_amdgcn_readlane(mt.nblk, f);
+    r.skip = __builtin_amdgcn_readlane(mt.skip, f);
+    r.s0 = __builtin_amdgcn_readlane(mt.s0, f);
+    r.whole = r.j0 == r.skip && r.j1 == r.nblk;
+    return r;
   };
 
-  for (int k = 0; k < 2 * kWaves; ++k) {
-    const PieceMeta mt = sm_meta[k >> 1][k & 1];
-    if (mt.b < 0) continue;
-    const float pm = sm_pm[k >> 1][k & 1][col], pl = sm_pl[k >> 1][k & 1][col];
-    if (mt.b == gb && mt.kvh == gkvh) {
+  for (int g = wave; g < ngroups; g += kWaves) {
+    const Group gr = group(g);
+    // log-sum-exp over the group's slots in chunk order; the next slot's LDS reads are issued
+    // before the current one is folded in (the last round reads its own slot again)
+    uint64_t rest = gr.slots;
+    int k = __builtin_ctzll(rest);
+    rest &= rest - 1;
+    float pm = sm_pm[k >> 1][k & 1][col], pl = sm_pl[k >> 1][k & 1][col];
+    f32x4 pa[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pa[t] = sm_pacc[k >> 1][k & 1][t][lane];
+    float gm = -INFINITY, gl = 0.0f;
+    f32x4 go[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) go[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (;;) {
+      const bool more = rest != 0;
+      const int kn = more ? __builtin_ctzll(rest) : k;
+      const float pmn = sm_pm[kn >> 1][kn & 1][col], pln = sm_pl[kn >> 1][kn & 1][col];
+      f32x4 pan[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) pan[t] = sm_pacc[kn >> 1][kn & 1][t][lane];
       const float M_ = fmaxf(gm, pm);
       const float x = fast_exp2(gm - M_), y = fast_exp2(pm - M_);
       gl = gl * x + pl * y;
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
-        if (tile_of(t) < NT) go[t] = go[t] * x + sm_pacc[k >> 1][k & 1][tile_of(t)][lane] * y;
+      for (int t = 0; t < NT; ++t) go[t] = go[t] * x + pa[t] * y;
       gm = M_;
-      gj1 = mt.j1;
-    } else {
-      if (gb >= 0) emit();
-      gb = mt.b;
-      gkvh = mt.kvh;
-      gj0 = mt.j0;
-      gj1 = mt.j1;
-      gnblk = mt.nblk;
-      gskip = mt.skip;
-      gs0 = mt.s0;
-      gm = pm;
-      gl = pl;
+      if (!more) break;
+      rest &= rest - 1;
+      k = kn;
+      pm = pmn;
+      pl = pln;
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
-        if (tile_of(t) < NT) go[t] = sm_pacc[k >> 1][k & 1][tile_of(t)][lane];
+      for (int t = 0; t < NT; ++t) pa[t] = pan[t];
+    }
+    if (col >= G) continue;
+    if (gr.whole) {
+      const size_t row = (size_t)gr.b * Hq + gr.kvh * G + col;
+      if (gr.skip > 0) fold_prefix<D>(a, row, prefix_parts(gr.skip), grp, 0, 1, gm, gl, go);
+      E* out = reinterpret_cast<E*>(a.out) + row * D + 4 * grp;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        *reinterpret_cast<uint2*>(out + 16 * t) =
+            make_uint2(pack2<QT>(go[t][0] / gl, go[t][1] / gl),
+                       pack2<QT>(go[t][2] / gl, go[t][3] / gl));
+    } else {
+      // slot 1 holds the group whose sequence head starts strictly inside this workgroup's
+      // range (it runs past the end); slot 0 the one that started at or before the range start
+      const int wslot = gr.s0 > (int)blockIdx.x * WGB ? 1 : 0;
+      const size_t ps = ((size_t)blockIdx.x * 2 + wslot) * G + col;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)                 // device-coherent stores
+        store_coherent(a.ws_acc + ps * D + 16 * t + 4 * grp, go[t]);
+      if (grp == 0) {
+        store_coherent(a.ws_ml + ps * 2, gm);
+        store_coherent(a.ws_ml + ps * 2 + 1, gl);
+      }
     }
   }
-  if (gb >= 0) emit();
+
+  // the cut groups this workgroup publishes (at most two), field by field in registers
+  int npub = 0, pb_b[2] = {0, 0}, pb_kvh[2] = {0, 0}, pb_skip[2] = {0, 0}, pb_s0[2] = {0, 0};
+  int pb_c0[2] = {0, 0}, pb_c1[2] = {0, 0};
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if (x >= ngroups) break;
+    const Group gr = group(x == 0 ? 0 : ngroups - 1);
+    if (gr.whole) continue;
+    const int c0 = gr.s0 / WGB, c1 = (gr.s0 + (gr.nblk - gr.skip) - 1) / WGB;
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+      if (y == npub) {
+        pb_b[y] = gr.b;
+        pb_kvh[y] = gr.kvh;
+        pb_skip[y] = gr.skip;
+        pb_s0[y] = gr.s0;
+        pb_c0[y] = c0;
+        pb_c1[y] = c1;
+      }
+    ++npub;
+  }
   if (npub == 0) return;
 
   // Wait for the published parts to complete, then count them: the counter of a sequence head
