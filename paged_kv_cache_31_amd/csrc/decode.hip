@@ -749,13 +749,15 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const bool act = first[v] == INT_MAX && j0 < len[v];   // wave-uniform
-        x[v] = act && j < len[v] ? rm[v][j] : 0;
-        y[v] = act && j < len[v] ? rl[v][j] : 0;
+        // unconditional loads (clamped into the row), so that they are all in flight at once
+        const int jc = min(j, max(len[v] - 1, 0));
+        x[v] = rm[v][jc];
+        y[v] = rl[v][jc];
       }
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const bool act = first[v] == INT_MAX && j0 < len[v];
-        const unsigned long long diff = __ballot(act && x[v] != y[v]);
+        const unsigned long long diff = __ballot(act && j < len[v] && x[v] != y[v]);
         if (diff) first[v] = j0 + __ffsll((long long)diff) - 1;
         live |= first[v] == INT_MAX && j0 + 64 < len[v];
       }
@@ -810,18 +812,33 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int b = tid * PER + q;
-      if (mc[q] > 0) h_mbase[s_slot[b]] = mb;
+      if (mc[q] > 0) {
+        h_mbase[s_slot[b]] = mb;
+        h_key[s_slot[b]] = 0;                       // rank counter of the member list below
+      }
       s_ubase[b] = ub;
       mb += mc[q];
       ub += uc[q];
     }
   }
   __syncthreads();
-  for (int i = tid; i < nmem; i += NTH) {
-    const int slot = s_mslot[i];
-    int rank = 0;
-    for (int j = 0; j < i; ++j) rank += s_mslot[j] == slot;
-    s_mlist[h_mbase[slot] + rank] = s_mseq[i];
+  // member ranks within their groups: the first wave walks the members in sequence order, 64
+  // at a time, one ballot per distinct group in the round
+  if (wave == 0) {
+    for (int i0 = 0; i0 < nmem; i0 += 64) {
+      const int i = i0 + lane;
+      const int slot = i < nmem ? s_mslot[i] : -1;
+      uint64_t todo = __ballot(slot >= 0);
+      while (todo) {
+        const int sl = __builtin_amdgcn_readlane(slot, __builtin_ctzll(todo));
+        const uint64_t same = __ballot(slot == sl);
+        const int base = h_key[sl];
+        if (slot == sl) s_mlist[h_mbase[sl] + base + __popcll(same & ((1ull << lane) - 1ull))] =
+            s_mseq[i];
+        if (lane == 0) h_key[sl] = base + __popcll(same);
+        todo &= ~same;
+      }
+    }
   }
   if (blockIdx.x == 0) {                            // shared blocks each sequence skips
 #pragma unroll
