@@ -106,9 +106,10 @@ __device__ __forceinline__ void fold_prefix(const DecodeArgs& a, size_t row, int
   }
 }
 
-// Stores the new token of sequence b, KV head kvh (k_new/v_new [B][Hkv][D]) into offset off of
-// physical block blk, one wave: the K row is contiguous, the V elements are strided (dim-major
-// tile).  A block id outside the pool skips the store, as pa_kv_append skips such a slot.
+// Stores the K row of the new token of sequence b, KV head kvh (k_new [B][Hkv][D]) into offset
+// off of physical block blk, one wave (the row is contiguous in the token-major K tile).  Its V
+// element goes in with the stepper's read of the block (VAppend).  A block id outside the pool
+// skips the store, as pa_kv_append skips such a slot (the stepper reads block 0 instead).
 template <int D, int KVT>
 __device__ __forceinline__ void append_token(const DecodeArgs& a, int b, int kvh, int blk, int off,
                                              int lane) {
@@ -117,17 +118,9 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, int b, int kvh
   const size_t row = ((size_t)b * a.num_kv_heads + kvh) * D * EB;
   const size_t tile = ((size_t)blk * a.num_kv_heads + kvh) * kBlock * D * EB;
   uint8_t* kc = reinterpret_cast<uint8_t*>(const_cast<void*>(a.k_cache));
-  uint8_t* vc = reinterpret_cast<uint8_t*>(const_cast<void*>(a.v_cache));
   if (lane < D * EB / 16)
     *reinterpret_cast<uint4*>(kc + tile + (size_t)off * D * EB + 16 * lane) =
         *reinterpret_cast<const uint4*>(a.k_new + row + 16 * lane);
-  for (int d = lane; d < D; d += 64) {
-    if constexpr (EB == 2)
-      *reinterpret_cast<uint16_t*>(vc + tile + ((size_t)d * kBlock + off) * 2) =
-          *reinterpret_cast<const uint16_t*>(a.v_new + row + 2 * d);
-    else
-      vc[tile + (size_t)d * kBlock + off] = a.v_new[row + d];
-  }
 }
 
 // Parts merged with one round of loads per thread (more are staged through LDS in batches).
@@ -400,7 +393,16 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
     f32x4 acc[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    st.run(qB, trow, kvh, j0, j1, end_tok, 0, 1, m_run, l_run, acc, append);
+    if (append && (unsigned)trow[(L - 1) / kBlock] < (unsigned)a.num_blocks) {
+      constexpr int EB = KVT == DT_FP8 ? 1 : 2;
+      VAppend ap;
+      ap.vnew = a.v_new + ((size_t)b * Hkv + kvh) * D * EB;
+      ap.blk = (L - 1) / kBlock;
+      ap.off = (L - 1) % kBlock;
+      st.run_append(qB, trow, kvh, j0, j1, end_tok, m_run, l_run, acc, true, ap);
+    } else {
+      st.run(qB, trow, kvh, j0, j1, end_tok, 0, 1, m_run, l_run, acc);
+    }
 
     // ---- finish the piece: whole sequence head -> output; cut piece -> LDS slot
     l_run = sum_across_rows(l_run);

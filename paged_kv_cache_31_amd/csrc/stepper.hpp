@@ -11,11 +11,24 @@ template <int D, bool FP8> struct StepRegs;
 template <int D> struct StepRegs<D, false> {
   uint4 k[2][D / 32];   // per 16-token row set m: one 16-byte load per 32-dim chunk
   uint4 v[D / 16];      // per 16-dim tile: 8 tokens x 16-bit
+  int pb0, pb1;         // physical blocks of the step
 };
 template <int D> struct StepRegs<D, true> {
   uint4 k[2][D / 64];   // one 16-byte load covers two 32-dim chunks of 8 codes
   uint2 v[D / 16];      // 8 tokens x 1 byte
   float ks, vs;         // block scales of this lane's block
+  int pb0, pb1;
+};
+
+// A token appended by the launch that reads its block (no other wave reads that block in the
+// launch).  Its V element is written into the wave's registers of the block's V tile, which is
+// then stored back whole: a dim-major tile holds one element of a token per 16-token row, so
+// storing the element alone would leave every cache line of the tile partly written, and later
+// reads of partly written lines were measured to be far slower than of whole ones.
+struct VAppend {
+  const uint8_t* vnew = nullptr;   // the head's new V row (head_dim elements); nullptr: none
+  int blk = -1;                    // logical block of the new token
+  int off = 0;                     // its slot in the block
 };
 
 template <typename V8>
@@ -113,8 +126,17 @@ struct Stepper {
                                       int j1, int end_tok, int s_first, int stride,
                                       float& m_run, float& l_run, f32x4 (&acc)[NT],
                                       bool wait_stores = false) const {
-    walk(qB, trow, kvh, j0, j1, end_tok, end_tok, end_tok, s_first, stride, m_run, l_run, acc,
-         wait_stores);
+    walk<false>(qB, trow, kvh, j0, j1, end_tok, end_tok, end_tok, s_first, stride, m_run, l_run,
+                acc, wait_stores, VAppend());
+  }
+  // The same with a token appended to one of the range's blocks (a separate instance, so that
+  // the plain loop carries none of the append's registers).
+  __device__ __forceinline__ void run_append(const V8 (&qB)[NC], const int32_t* trow, int kvh,
+                                             int j0, int j1, int end_tok, float& m_run,
+                                             float& l_run, f32x4 (&acc)[NT], bool wait_stores,
+                                             VAppend ap) const {
+    walk<true>(qB, trow, kvh, j0, j1, end_tok, end_tok, end_tok, 0, 1, m_run, l_run, acc,
+               wait_stores, ap);
   }
 
   // The same walk with a window per query column: this lane's column sees tokens below
@@ -124,13 +146,15 @@ struct Stepper {
                                             int j0, int j1, int end_lane, int end_lo, int end_v,
                                             float& m_run, float& l_run,
                                             f32x4 (&acc)[NT]) const {
-    walk(qB, trow, kvh, j0, j1, end_lane, end_lo, end_v, 0, 1, m_run, l_run, acc, false);
+    walk<false>(qB, trow, kvh, j0, j1, end_lane, end_lo, end_v, 0, 1, m_run, l_run, acc, false,
+                VAppend());
   }
 
+  template <bool APP>
   __device__ __forceinline__ void walk(const V8 (&qB)[NC], const int32_t* trow, int kvh, int j0,
                                        int j1, int end_tok, int end_lo, int end_v, int s_first,
                                        int stride, float& m_run, float& l_run,
-                                       f32x4 (&acc)[NT], bool wait_stores) const {
+                                       f32x4 (&acc)[NT], bool wait_stores, VAppend ap) const {
     const int nsteps = (j1 - j0 + 1) >> 1;
     if (s_first >= nsteps) return;
 
@@ -149,8 +173,26 @@ struct Stepper {
     ids_of(s_first, nid0, nid1);
     if (wait_stores && nsteps - s_first <= 2 * stride) wait_memory_ops();
 
+    // the appended token's V element for each of this lane's 16-dim tiles (dim 16i + col),
+    // packed PK to a register
+    constexpr int PK = FP8 ? 4 : 2;
+    uint32_t vn[(NT + PK - 1) / PK];
+    if constexpr (APP) {
+#pragma unroll
+      for (int i = 0; i < (NT + PK - 1) / PK; ++i) vn[i] = 0u;
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        vn[i / PK] |= (FP8 ? (uint32_t)ap.vnew[16 * i + col]
+                           : (uint32_t)reinterpret_cast<const uint16_t*>(ap.vnew)[16 * i + col])
+                      << (32 / PK * (i % PK));
+    }
+
     auto issue = [&](StepRegs<D, FP8>& r, int s) {
       const int pb0 = nid0, pb1 = nid1;
+      if constexpr (APP) {
+        r.pb0 = pb0;
+        r.pb1 = pb1;
+      }
       ids_of(s + stride, nid0, nid1);              // prefetch the next step's block ids
       const int kb = k_hi ? pb1 : pb0;
       const int vb = v_hi ? pb1 : pb0;
@@ -177,6 +219,45 @@ struct Stepper {
       const int t0 = kBlock * (j0 + 2 * s);
       const int tb = t0 + tb_lane;
       const bool partial = t0 + kStepTokens > (ROWS ? end_lo : end_tok);   // wave-uniform
+
+      // the appended token: into the registers of its block's V tile, then the tile back whole
+      if constexpr (APP) {
+        const int bj = ap.blk - (j0 + 2 * s);                          // wave-uniform
+        if (bj == 0 || bj == 1) {
+          const bool mine = (grp >> 1) == bj;
+          if (mine && (grp & 1) == (ap.off >> 3)) {
+            const int e = ap.off & 7;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+              const uint32_t val = (vn[i / PK] >> (32 / PK * (i % PK))) & (FP8 ? 0xFFu : 0xFFFFu);
+              if constexpr (FP8) {
+                const int sh = 8 * (e & 3);
+                const uint32_t m8 = ~(0xFFu << sh), b8 = val << sh;
+                if (e < 4) r.v[i].x = (r.v[i].x & m8) | b8;
+                else r.v[i].y = (r.v[i].y & m8) | b8;
+              } else {
+                const int sh = 16 * (e & 1);
+                const uint32_t m16 = ~(0xFFFFu << sh), b16 = val << sh;
+                if ((e >> 1) == 0) r.v[i].x = (r.v[i].x & m16) | b16;
+                else if ((e >> 1) == 1) r.v[i].y = (r.v[i].y & m16) | b16;
+                else if ((e >> 1) == 2) r.v[i].z = (r.v[i].z & m16) | b16;
+                else r.v[i].w = (r.v[i].w & m16) | b16;
+              }
+            }
+          }
+          if (mine) {
+            uint8_t* vp = const_cast<uint8_t*>(vc) +
+                          ((size_t)(bj ? r.pb1 : r.pb0) * Hkv + kvh) * TILE + v_lane_off;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+              if constexpr (FP8)
+                *reinterpret_cast<uint2*>(vp + i * 16 * kBlock * EB) = r.v[i];
+              else
+                *reinterpret_cast<uint4*>(vp + i * 16 * kBlock * EB) = r.v[i];
+            }
+          }
+        }
+      }
 
       // scores of 8 tokens (tb + jj) for head col
       f32x4 S[2];
