@@ -39,6 +39,42 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   reinterpret_cast<E*>(a.v_cache)[(tile * D + t) * kBlock + off] = v;
 }
 
+// ---- The append of a decode step taken out of the decode launch (pa_decode_append with many
+// appends per decode wave): token L-1 of every sequence, its slot read from the block table, one
+// workgroup per (sequence, KV head) and one thread per dimension as in append_kernel.
+template <int EB>
+__global__ __launch_bounds__(128) void append_last_kernel(LastAppendArgs a) {
+  typedef typename std::conditional<EB == 2, uint16_t, uint8_t>::type E;
+  const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;   // t < head_dim
+  const int H = a.num_kv_heads, D = a.head_dim;
+  const int kvecs = D * EB / 16;
+  const size_t row = (size_t)b * H + h;
+
+  const E v = reinterpret_cast<const E*>(a.v_new)[row * D + t];
+  uint4 k = make_uint4(0u, 0u, 0u, 0u);
+  if (t < kvecs) k = reinterpret_cast<const uint4*>(a.k_new)[row * kvecs + t];
+
+  const int L = min(max(a.context_lens[b], 0), a.len_cap);
+  if (L == 0) return;                                     // no token: nothing appended
+  const int blk = a.block_tables[(size_t)b * a.max_blocks_per_seq + (L - 1) / kBlock];
+  if ((unsigned)blk >= (unsigned)a.num_blocks) return;   // outside the pool: skipped
+  const int off = (L - 1) % kBlock;
+  const size_t tile = (size_t)blk * H + h;
+  if (t < kvecs)
+    reinterpret_cast<uint4*>(a.k_cache + (tile * kBlock + off) * D * EB)[t] = k;
+  reinterpret_cast<E*>(a.v_cache)[(tile * D + t) * kBlock + off] = v;
+}
+
+hipError_t launch_append_last(const LastAppendArgs& a, int batch, int elem_bytes,
+                              hipStream_t stream) {
+  const dim3 grid(batch, a.num_kv_heads);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(append_last_kernel<2>, grid, dim3(a.head_dim), 0, stream, a);
+  else
+    hipLaunchKernelGGL(append_last_kernel<1>, grid, dim3(a.head_dim), 0, stream, a);
+  return hipGetLastError();
+}
+
 // ---- Quantising append into an fp8 (OCP e4m3fn) cache with per-(block, KV head) scales.
 //
 // The fp8 KV cache stores value = code * scale (design.babushkai.com "GPU推論の内部構造", KV-cache

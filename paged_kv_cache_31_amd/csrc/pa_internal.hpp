@@ -26,6 +26,21 @@ struct AppendArgs {
   int head_dim;
 };
 
+// The append of a decode step (token L-1 of every sequence, slots from the block tables).
+struct LastAppendArgs {
+  const uint8_t* k_new;        // [batch][num_kv_heads][head_dim]
+  const uint8_t* v_new;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  int num_blocks;
+  int num_kv_heads;
+  int head_dim;
+  int max_blocks_per_seq;
+  int len_cap;
+};
+
 struct QuantAppendArgs {
   const uint8_t* k_new;  // [T][num_kv_heads][head_dim] 16-bit
   const uint8_t* v_new;
@@ -244,6 +259,8 @@ struct CopyArgs {
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t stream);
 
 hipError_t launch_append(const AppendArgs& a, int num_tokens, int elem_bytes, hipStream_t stream);
+hipError_t launch_append_last(const LastAppendArgs& a, int batch, int elem_bytes,
+                              hipStream_t stream);
 hipError_t launch_append_quant(const QuantAppendArgs& a, int num_tokens, bool bf16_src,
                                bool first_token_scale, hipStream_t stream);
 // Enqueues the decode; with a.ws_skip set, the prefix kernel runs first (prefix_wgs workgroups).

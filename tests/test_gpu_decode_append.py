@@ -60,6 +60,27 @@ def test_fused_equals_append_then_decode(case):
     assert_close(out_fused, ref, qd, label=f"fused {case}")
 
 
+@pytest.mark.parametrize("kvd", ["bf16", "fp8_e4m3"])
+def test_dense_appends(kvd):
+    """64 short sequences x 8 KV heads: one append per launched wave or more, so the step's
+    append runs as a launch of its own before the decode; the caches and the output must be
+    the same as in every other case."""
+    rng = np.random.default_rng(89)
+    lens = tuple(int(x) for x in rng.integers(1, 40, size=64))
+    spec = Spec("dense", 64, 32, 8, 128, "bf16", kvd, ("list", lens), pool=("times", 2),
+                seed=89)
+    wl = workloads.make(spec)
+    fused = Dev(wl)
+    out_fused = _fused(fused, 0, False)
+    ref, k_ref, v_ref = oracle_after_append(wl)
+    assert np.array_equal(host_bits(fused.k_cache), k_ref)
+    assert np.array_equal(host_bits(fused.v_cache), v_ref)
+    split = Dev(wl)
+    split.append()
+    assert np.array_equal(out_fused, split.decode())
+    assert_close(out_fused, ref, "bf16", label=f"dense appends {kvd}")
+
+
 def test_block_outside_the_pool_is_not_written():
     spec = Spec("oob", 3, 8, 2, 128, "bf16", "bf16", ("list", (40, 17, 5)), pool=("times", 2),
                 seed=88)
