@@ -750,7 +750,6 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
       bool live = false;
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
-        const bool act = first[v] == INT_MAX && j0 < len[v];   // wave-uniform
         // unconditional loads (clamped into the row), so that they are all in flight at once
         const int jc = min(j, max(len[v] - 1, 0));
         x[v] = rm[v][jc];

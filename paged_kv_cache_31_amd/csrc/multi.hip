@@ -106,31 +106,27 @@ __global__ __launch_bounds__(64 * kMultiWaves, 2) void multi_kernel(MultiArgs a)
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-// One wave per (sequence b, query token i, query head h): merges the num_parts partial results
-// of that row by log-sum-exp and writes the normalised output.  Every partition of a row's tile
-// was written by multi_kernel or chunk_kernel (an empty one as max -inf, sum 0, output 0).
-template <int D, int QT>
+// Merges the num_parts partial results of each output row (sequence b, query token i, query
+// head h) by log-sum-exp and writes the normalised output.  D/DPL lanes take a row (DPL dims
+// each): with few partitions, 16 dims a lane and 64/(D/16) rows a wave, so that one round of
+// waves covers a large batch; with many, 2 dims a lane, so that the partitions of a row are
+// split over more lanes.  Every partition of a row's tile was written by multi_kernel or
+// chunk_kernel (an empty one as max -inf, sum 0, output 0: it adds exactly 0).
+template <int D, int QT, int DPL>
 __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
   typedef typename Mfma<QT>::elem E;
-  constexpr int DPL = D / 64;                          // dims per lane
+  static_assert(DPL == 2 || DPL == 16, "dims per lane");
+  constexpr int LPR = D / DPL;                         // lanes per row
+  constexpr int RPW = 64 / LPR > 0 ? 64 / LPR : 1;     // rows per wave
   const int lane = threadIdx.x & 63;
+  const int sub = lane / LPR, slice = lane % LPR;      // row of the wave, DPL-dim slice
   const long long w = (long long)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
   const int Hq = a.num_q_heads;
   const long long per_seq = (long long)a.max_query_len * Hq;
-  if (w >= (long long)a.batch * per_seq) return;
-  const int b = (int)(w / per_seq);
-  const int rem = (int)(w - (long long)b * per_seq);
+  const long long rr = w * RPW + sub;
+  if (sub >= RPW || rr >= (long long)a.batch * per_seq) return;
+  const int b = (int)(rr / per_seq);
+  const int rem = (int)(rr - (long long)b * per_seq);
   const int i = rem / Hq, h = rem - i * Hq;
   const int q0 = a.query_start[b];
   const int T = min(max(a.query_start[b + 1] - q0, 0), a.max_query_len);
@@ -140,39 +136,68 @@ __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
   const size_t row = (size_t)n * Hq + h;
   const int NP = a.num_parts;
   const float* ml = a.ws_ml + row * NP * 2;
-  const float* pacc = a.ws_acc + row * NP * D;
+  const float* pacc = a.ws_acc + row * NP * D + DPL * slice;
 
   float M = -INFINITY;
-  for (int p = lane; p < NP; p += 64) M = fmaxf(M, ml[2 * p]);
-  M = wave_max(M);
+  for (int p = 0; p < NP; ++p) M = fmaxf(M, ml[2 * p]);
   float o[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) o[k] = 0.0f;
   float den = 1.0f;
   if (M != -INFINITY) {
-    float s = 0.0f;
-    for (int p = lane; p < NP; p += 64) s += fast_exp2(ml[2 * p] - M) * ml[2 * p + 1];
-    den = wave_sum(s);
-    // Partitions without keys were written as max -inf, sum 0 and output 0, so they add
-    // exactly 0 here; no branch, so that the unrolled loads stay in flight together.
-#pragma unroll 8
+    den = 0.0f;
+#pragma unroll 4
     for (int p = 0; p < NP; ++p) {
       const float wt = fast_exp2(ml[2 * p] - M);
+      den += wt * ml[2 * p + 1];
       if constexpr (DPL == 2) {
-        const float2 x = *reinterpret_cast<const float2*>(pacc + (size_t)p * D + 2 * lane);
+        const float2 x = *reinterpret_cast<const float2*>(pacc + (size_t)p * D);
         o[0] += wt * x.x;
         o[1] += wt * x.y;
       } else {
-        o[0] += wt * pacc[(size_t)p * D + lane];
+        const f32x4* x = reinterpret_cast<const f32x4*>(pacc + (size_t)p * D);
+#pragma unroll
+        for (int k = 0; k < DPL / 4; ++k) {
+          const f32x4 v = x[k];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[4 * k + e] += wt * v[e];
+        }
       }
     }
   }
-  E* out = reinterpret_cast<E*>(a.out) + row * D + lane * DPL;
+  E* out = reinterpret_cast<E*>(a.out) + row * D + DPL * slice;
   if constexpr (DPL == 2) {
     *reinterpret_cast<uint32_t*>(out) = pack2<QT>(o[0] / den, o[1] / den);
   } else {
-    out[0] = (E)(o[0] / den);
+#pragma unroll
+    for (int k = 0; k < DPL; k += 8)
+      *reinterpret_cast<uint4*>(out + k) =
+          make_uint4(pack2<QT>(o[k] / den, o[k + 1] / den), pack2<QT>(o[k + 2] / den, o[k + 3] / den),
+                     pack2<QT>(o[k + 4] / den, o[k + 5] / den),
+                     pack2<QT>(o[k + 6] / den, o[k + 7] / den));
   }
+}
+
+// Partitions up to which the merge gives a lane 16 dims of a row (else 2).
+constexpr int kMergeWideParts = 4;
+
+template <int D, int QT>
+static hipError_t launch_merge(const MultiArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.batch * a.max_query_len * a.num_q_heads;
+  if (a.num_parts <= kMergeWideParts) {
+    constexpr int RPW = 64 / (D / 16);
+    const long long wgs = ((rows + RPW - 1) / RPW + 3) / 4;
+    if (wgs > 0)
+      hipLaunchKernelGGL((multi_merge_kernel<D, QT, 16>), dim3((unsigned)wgs), dim3(256), 0,
+                         stream, a);
+  } else {
+    constexpr int RPW = 64 / (D / 2) > 0 ? 64 / (D / 2) : 1;
+    const long long wgs = ((rows + RPW - 1) / RPW + 3) / 4;
+    if (wgs > 0)
+      hipLaunchKernelGGL((multi_merge_kernel<D, QT, 2>), dim3((unsigned)wgs), dim3(256), 0,
+                         stream, a);
+  }
+  return hipGetLastError();
 }
 
 // ---- Many query rows per (sequence, KV head): prefill chunks, verification of several drafts.
@@ -605,10 +630,7 @@ static hipError_t launch_multi_t(const MultiArgs& a, hipStream_t stream) {
             ? launch_chunk<D, QT, KVT, kChunkWide.waves, kChunkWide.tiles, 3>(a, stream)
             : launch_chunk<D, QT, KVT, kChunkNarrow.waves, kChunkNarrow.tiles, 2>(a, stream);
     if (e != hipSuccess || a.num_parts == 1) return e;
-    const long long waves = (long long)a.batch * a.max_query_len * a.num_q_heads;
-    hipLaunchKernelGGL((multi_merge_kernel<D, QT>), dim3((unsigned)((waves + 3) / 4)),
-                       dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch_merge<D, QT>(a, stream);
   }
   long long wgs = (a.total_items + kMultiWaves - 1) / kMultiWaves;
   wgs = (wgs + 7) / 8 * 8;
@@ -618,15 +640,7 @@ static hipError_t launch_multi_t(const MultiArgs& a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.num_parts > 1) {
-    const long long waves = (long long)a.batch * a.max_query_len * a.num_q_heads;
-    const long long mwgs = (waves + 3) / 4;
-    if (mwgs > 0) {
-      hipLaunchKernelGGL((multi_merge_kernel<D, QT>), dim3((unsigned)mwgs), dim3(256), 0, stream,
-                         a);
-      return hipGetLastError();
-    }
-  }
+  if (a.num_parts > 1) return launch_merge<D, QT>(a, stream);
   return hipSuccess;
 }
 
