@@ -23,8 +23,9 @@
 //    (sequence, KV head) inside the chunk): a piece that is a whole sequence head is normalised
 //    and written out; a cut piece keeps its running max, exp-sum and unnormalised output.
 //  * Log-sum-exp merge in two levels, inside this one kernel.  The eight waves of a workgroup
-//    own eight consecutive chunks; their cut pieces meet in LDS and are merged in chunk order, so a
-//    sequence head that ends inside the workgroup is written out there.  A piece cut at a
+//    own eight consecutive chunks; their cut pieces meet in LDS, the pieces of one sequence head
+//    are merged in chunk order (the waves take different heads at once), and a sequence head
+//    that ends inside the workgroup is written out there.  A piece cut at a
 //    workgroup boundary is published to the workspace with device-coherent stores, and an atomic
 //    counter per boundary elects the last workgroup to arrive, which reads all parts of that
 //    sequence head back with device-coherent loads, merges them in logical order and resets the
@@ -382,7 +383,9 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
     const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
 
     // Fused append: the piece that holds the sequence head's last block (no other wave reads
-    // it in this launch) first stores the new token L-1 of this KV head into its slot.
+    // it in this launch) appends token L-1 of this KV head: its K row is stored before the
+    // loads; its V element goes into the registers of the block's V tile, which the stepper's
+    // append instance stores back whole.
     const bool append = a.k_new != nullptr && j1 == nblk;
     if (append) append_token<D, KVT>(a, b, kvh, trow[(L - 1) / kBlock], (L - 1) % kBlock, lane);
 
