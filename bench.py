@@ -69,7 +69,8 @@ def cpu_baseline(wl, decode_bytes_fn, append_bytes, min_s: float = 10.0,
 
 
 DECODE_SOURCES = ("decode.hip", "stepper.hpp", "device_common.hpp", "pa_internal.hpp")
-MULTI_SOURCES = ("multi.hip", "stepper.hpp", "device_common.hpp", "pa_internal.hpp")
+MULTI_SOURCES = ("multi.hip", "multi_split.hip", "stepper.hpp", "device_common.hpp",
+                 "pa_internal.hpp")
 
 
 def traffic_record(workload: str, sources=DECODE_SOURCES):
@@ -185,7 +186,7 @@ def bench_multi(args, dev) -> int:
     P = args.partition or 0
     desc = pa.multi_desc(base["q"], base["k"], tables, maxT, wl.max_context_len, P)
     ws_bytes = pa.pa_decode_multi_workspace_size(desc)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    workspace = pa.new_workspace(max(ws_bytes, 1), dev)
     torch.cuda.synchronize()
     log(f"uploaded: {R} pool copies of {pool_bytes / 2**30:.2f} GiB; workspace {ws_bytes} B")
 
@@ -222,14 +223,16 @@ def bench_multi(args, dev) -> int:
     launch_s = e0.elapsed_time(e1) / 1e3 / args.steps
     log(f"{args.steps} back-to-back pa_decode_multi calls: {launch_s * 1e6:.1f} us each")
 
-    # the library's choice (pa_internal.hpp multi_plan): more than 16 rows per head and no fixed
-    # partition take the LDS-staged chunk kernel
-    if P == 0 and maxT * (Hq // Hkv) > 16:
-        kernel = "chunk_kernel"
+    # the library's choice (pa_internal.hpp multi_plan): without a fixed partition, heads of one
+    # row tile (two with an fp8 cache or head_dim 64) take the balanced split kernel, larger ones
+    # the LDS-staged chunk kernel
+    tiles = (maxT * (Hq // Hkv) + 15) // 16
+    if P == 0 and tiles <= (2 if s.kv_dtype == "fp8_e4m3" or D == 64 else 1):
+        kernel = "multi_split_kernel"
     else:
-        kernel = "multi_kernel"
-    if ws_bytes > 0:
-        kernel += "+multi_merge_kernel"
+        kernel = "chunk_kernel" if P == 0 and tiles > 1 else "multi_kernel"
+        if ws_bytes > 0:
+            kernel += "+multi_merge_kernel"
     step_s = ms_per_step / 1e3
     if mfma:
         peak, unit = PEAK_TFLOPS[s.q_dtype], "TFLOP/s"

@@ -106,8 +106,7 @@ typedef struct pa_multi_desc {
   int32_t total_queries;      /* rows of q and out, >= 0 */
   int32_t max_query_len;      /* host-side bound on query_start[b+1] - query_start[b], > 0 */
   int32_t partition_tokens;   /* key partition per row tile, a multiple of 32 in [32, 65536];
-                                 0 = chosen from the shape (one partition when there are rows
-                                 enough to fill the GPU) */
+                                 0 = chosen from the shape (see pa_decode_multi) */
   int32_t q_dtype;            /* PA_F16 or PA_BF16; the output has the same dtype */
 } pa_multi_desc;
 
@@ -220,9 +219,20 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
  * Row i of sequence b sits at position p = L_b - T_b + i and gets
  * softmax(scale * q . K[0..p]^T) . V[0..p] with query head h reading KV head h / group; a row
  * with p < 0 sees no token and is zero.  fp32 accumulation; within 2e-3 absolute + 2e-3 relative
- * of the exact result.  The workspace (pa_decode_multi_workspace_size bytes, 16-byte aligned) is
- * needed only when a row tile's keys are cut into several partitions; its contents need no
- * initialisation.  Calls sharing a workspace must be ordered on one stream.
+ * of the exact result, and the same bits on every call with the same inputs.
+ *
+ * With partition_tokens 0, heads of at most 16 query rows (T_b * group), and of at most 32 with
+ * an fp8 cache or head_dim 64, get the decode's balanced split-KV: equal chunks of the batch's
+ * (sequence, KV head, block) space, one per wave, each wave holding all row tiles of a head,
+ * partial results merged by log-sum-exp inside the kernel.  Larger heads take a kernel that
+ * stages K/V in LDS for blocks of rows; a fixed partition_tokens cuts every row tile's keys into
+ * partitions merged by a second kernel.
+ *
+ * The workspace (pa_decode_multi_workspace_size bytes, 16-byte aligned; none when the size is
+ * 0) follows pa_decode's contract: zero-filled once before its first use, its first 256 KiB are
+ * arrival counters that every call leaves at zero, the rest is scratch; one workspace may serve
+ * pa_decode and pa_decode_multi calls alike.  Calls sharing a workspace must not overlap.  A
+ * call with total_queries 0 does nothing and needs no workspace.
  */
 pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q, const int32_t* query_start,
                           const void* k_cache, const void* v_cache, const float* k_scale,

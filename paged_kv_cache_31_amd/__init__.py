@@ -228,7 +228,8 @@ _workspaces: dict = {}
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """A pa_decode workspace: zero-filled once (the kernel keeps its counters at zero)."""
+    """A pa_decode / pa_decode_multi workspace: zero-filled once (the kernels leave their arrival
+    counters at zero)."""
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
@@ -344,7 +345,7 @@ class MultiCall:
         need = pa_decode_multi_workspace_size(self._desc)
         st = _stream(stream)
         if workspace is None and need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _workspace(need, q.device, st.value or 0)
         wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         self._keep = (q, query_start, k_cache, v_cache, block_tables, context_lens, out, k_scale,
                       v_scale, workspace)

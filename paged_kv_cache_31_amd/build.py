@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "multi.hip", "pool.cpp"]
+SOURCES = ["pa_api.hip", "append.hip", "decode.hip", "multi.hip", "multi_split.hip", "pool.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -16,10 +16,12 @@
 // KV head, partition) are consecutive items, so they share workgroups, and consecutive logical
 // workgroups are placed on one XCD (the hardware deals workgroups to the eight XCDs in turn), so
 // the re-reads of a K/V block by the tiles of one head hit that XCD's L2 rather than HBM; K/V
-// loads are therefore cached, not streamed.  Long contexts with few rows (speculative
-// verification) are split into key partitions whose partial results (running max, exp-sum,
-// unnormalised output) go to the workspace and are merged by log-sum-exp in a second kernel;
-// with one partition the kernel normalises and writes the output itself.
+// loads are therefore cached, not streamed.  This kernel serves calls with a fixed key
+// partition: each tile's keys are cut into partitions whose partial results (running max,
+// exp-sum, unnormalised output) go to the workspace and are merged by log-sum-exp in a second
+// kernel; with one partition the kernel normalises and writes the output itself.  Without a
+// fixed partition, heads of few rows take the balanced split (multi_split_kernel) and larger
+// ones chunk_kernel below.
 #include "device_common.hpp"
 #include "pa_internal.hpp"
 #include "stepper.hpp"

@@ -78,9 +78,31 @@ int multi_len_cap(const pa_multi_desc* d) {
   return (int)cap;
 }
 
+// Resident multi_split_kernel workgroups on the current device, cached per device and instance.
+int64_t resident_split_wgs(const pa_multi_desc* d, int rt) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, int>, int64_t> cache;
+  const auto key = std::make_tuple(dev, (int)d->cache.head_dim, (int)d->q_dtype,
+                                   (int)d->cache.kv_dtype, rt);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const int per_cu = pa::multi_split_workgroups_per_cu(d->cache.head_dim, d->q_dtype,
+                                                       d->cache.kv_dtype, rt);
+  const int64_t wgs = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  cache[key] = wgs;
+  return wgs;
+}
+
 pa::MultiPlan multi_plan_of(const pa_multi_desc* d) {
   return pa::multi_plan(d->batch, d->cache.num_kv_heads, d->num_q_heads / d->cache.num_kv_heads,
-                        d->max_query_len, multi_len_cap(d), d->partition_tokens);
+                        d->max_query_len, multi_len_cap(d), d->partition_tokens,
+                        d->cache.head_dim, d->cache.kv_dtype == PA_FP8_E4M3);
 }
 
 // Upper bound of the flattened (sequence, KV head, block) space.
@@ -283,9 +305,9 @@ PA_EXPORT pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q,
   const pa::MultiPlan p = multi_plan_of(desc);
   const size_t need = pa::multi_workspace_bytes(p, desc->total_queries, desc->num_q_heads,
                                                 desc->cache.head_dim);
+  if (desc->total_queries == 0) return PA_OK;                // no rows: nothing to do
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
     return PA_ERR_WORKSPACE;
-  if (desc->total_queries == 0) return PA_OK;
 
   pa::MultiArgs a;
   a.q = q;
@@ -297,11 +319,25 @@ PA_EXPORT pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  const size_t rows = (size_t)desc->total_queries * desc->num_q_heads * p.num_parts;
-  a.ws_acc = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                pa::align256(rows * desc->cache.head_dim * 4))
-                     : nullptr;
+  a.split_rt = p.split_rt;
+  a.total_lanes = 0;
+  a.ws_cnt = nullptr;
+  if (p.split_rt > 0) {
+    const pa::SplitLayout lay = pa::split_layout(p, desc->cache.head_dim);
+    int64_t wgs = resident_split_wgs(desc, p.split_rt);
+    if (wgs > p.split_wgs) wgs = p.split_wgs;
+    a.total_lanes = (int)(wgs * pa::kWaves);
+    a.ws_cnt = static_cast<int*>(workspace);
+    a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.acc);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml);
+  } else if (need > 0) {
+    const pa::PartsLayout lay =
+        pa::parts_layout(p, desc->total_queries, desc->num_q_heads, desc->cache.head_dim);
+    a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.acc);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml);
+  } else {
+    a.ws_acc = a.ws_ml = nullptr;
+  }
   a.batch = desc->batch;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->cache.num_kv_heads;
@@ -318,8 +354,12 @@ PA_EXPORT pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q,
   a.row_blocks = p.row_blocks;
   a.chunk_wide = p.chunk_wide;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = pa::launch_multi(a, desc->cache.head_dim, desc->q_dtype, desc->cache.kv_dtype,
-                                  static_cast<hipStream_t>(stream));
+  hipError_t e =
+      p.split_rt > 0
+          ? pa::launch_multi_split(a, desc->cache.head_dim, desc->q_dtype, desc->cache.kv_dtype,
+                                   static_cast<hipStream_t>(stream))
+          : pa::launch_multi(a, desc->cache.head_dim, desc->q_dtype, desc->cache.kv_dtype,
+                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_hip_error = (int32_t)e;
     return PA_ERR_HIP;

@@ -160,6 +160,10 @@ struct MultiArgs {
   long long total_items;
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
   int chunk_wide;              // chunk_kernel shape: 1 kChunkWide, 0 kChunkNarrow
+  // Balanced split (multi_split_kernel): split_rt > 0 row tiles per head, all in one wave.
+  int split_rt;
+  int total_lanes;             // chunks of the flattened block space (= launched waves)
+  int* ws_cnt;                 // [kMaxWorkgroups] arrival counters, zero between calls
   float qk_scale_log2;
 };
 
@@ -186,7 +190,17 @@ struct MultiPlan {
   long long items;             // waves (multi_kernel) or workgroups (chunk_kernel)
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
   int chunk_wide;              // chunk_kernel shape: 1 wide, 0 narrow
+  int split_rt;                // > 0: multi_split_kernel with this many row tiles per head
+  long long split_wgs;         // multi_split_kernel: most workgroups a launch may use
 };
+
+// multi_split_kernel takes heads of one row tile, and of two where a wave's registers hold both
+// tiles' accumulators and query operands next to the K/V steps in flight (fp8 caches or
+// head_dim 64: no spills; two tiles of 16-bit K/V at head_dim 128 would spill, so those heads
+// go to chunk_kernel).  It launches one workgroup per resident slot, at most
+// kMaxSplitWorkgroups (a workspace bound known without a GPU: twice the 256 CUs of an MI355X).
+inline int split_max_tiles(int head_dim, bool fp8_kv) { return fp8_kv || head_dim == 64 ? 2 : 1; }
+constexpr long kMaxSplitWorkgroups = 512;
 
 // Key partitions for `base` independent units so that about `target` units run, each at least
 // kMultiMinPartBlocks blocks long; part_blocks is even.
@@ -212,13 +226,28 @@ inline void multi_parts(MultiPlan& p, long long base, long long target, long lon
 
 // A pure function of the descriptor, so the workspace size is known without a GPU.
 inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_query_len,
-                            int len_cap, int partition_tokens) {
+                            int len_cap, int partition_tokens, int head_dim, bool fp8_kv) {
   MultiPlan p;
   const long long rows = (long long)max_query_len * group;
   const long long maxblk = ((long long)len_cap + kBlock - 1) / kBlock;
   p.tiles_per_head = (int)((rows + 15) / 16);
   p.row_blocks = 0;
   p.chunk_wide = 0;
+  p.split_rt = 0;
+  p.split_wgs = 0;
+  if (partition_tokens == 0 && p.tiles_per_head <= split_max_tiles(head_dim, fp8_kv)) {
+    // balanced split: one chunk per wave, all row tiles of a head in the wave; at least two
+    // blocks per chunk, so the space never needs more than half its blocks in chunks
+    p.split_rt = p.tiles_per_head;
+    const long long lanes_max = ((long long)batch * num_kv_heads * maxblk + 1) / 2;
+    long long wgs = (lanes_max + kWaves - 1) / kWaves;
+    if (wgs > kMaxSplitWorkgroups) wgs = kMaxSplitWorkgroups;
+    p.split_wgs = wgs < 1 ? 1 : wgs;
+    p.num_parts = 1;
+    p.part_blocks = (int)(maxblk + (maxblk & 1));
+    p.items = 0;
+    return p;
+  }
   if (partition_tokens == 0 && rows > 16) {
     const ChunkShape c = rows > 64 ? kChunkWide : kChunkNarrow;
     const int block_rows = 16 * c.waves * c.tiles;
@@ -239,11 +268,40 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
   p.items = (long long)batch * num_kv_heads * p.num_parts * p.tiles_per_head;
   return p;
 }
+// Balanced split workspace: the arrival counters (the same fixed region as the decode's), then
+// two published parts per (workgroup, row tile): an fp32 output row per column and its max and
+// exp-sum.
+struct SplitLayout {
+  size_t acc, ml, total;
+};
+inline SplitLayout split_layout(const MultiPlan& p, int head_dim) {
+  SplitLayout w;
+  const size_t cols = (size_t)p.split_wgs * 2 * p.split_rt * 16;
+  w.acc = align256((size_t)kMaxWorkgroups * sizeof(int));
+  w.ml = w.acc + align256(cols * head_dim * sizeof(float));
+  w.total = w.ml + align256(cols * 2 * sizeof(float));
+  return w;
+}
+// Fixed partitions: the same counter region first (left untouched, so one zero-filled
+// workspace serves every call on a stream), then per (query row, head, partition) an fp32
+// output row and its max and exp-sum.
+struct PartsLayout {
+  size_t acc, ml, total;
+};
+inline PartsLayout parts_layout(const MultiPlan& p, int total_queries, int num_q_heads,
+                                int head_dim) {
+  PartsLayout w;
+  const size_t rows = (size_t)total_queries * num_q_heads * p.num_parts;
+  w.acc = align256((size_t)kMaxWorkgroups * sizeof(int));
+  w.ml = w.acc + align256(rows * head_dim * sizeof(float));
+  w.total = w.ml + align256(rows * 2 * sizeof(float));
+  return w;
+}
 inline size_t multi_workspace_bytes(const MultiPlan& p, int total_queries, int num_q_heads,
                                     int head_dim) {
+  if (p.split_rt > 0) return split_layout(p, head_dim).total;
   if (p.num_parts <= 1) return 0;
-  const size_t rows = (size_t)total_queries * num_q_heads * p.num_parts;
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+  return parts_layout(p, total_queries, num_q_heads, head_dim).total;
 }
 
 struct CopyArgs {
@@ -269,6 +327,11 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_
 // Enqueues multi_kernel and, with more than one partition, the merge.
 hipError_t launch_multi(const MultiArgs& a, int head_dim, int q_dtype, int kv_dtype,
                         hipStream_t stream);
+// Enqueues multi_split_kernel (a.split_rt row tiles per head, a.total_lanes chunks = waves).
+hipError_t launch_multi_split(const MultiArgs& a, int head_dim, int q_dtype, int kv_dtype,
+                              hipStream_t stream);
+// Resident multi_split_kernel workgroups per CU for this instance (0 if the query fails).
+int multi_split_workgroups_per_cu(int head_dim, int q_dtype, int kv_dtype, int rt);
 // Resident decode workgroups per CU for this kernel instance (0 if the query fails).
 int decode_workgroups_per_cu(int head_dim, int q_dtype, int kv_dtype);
 

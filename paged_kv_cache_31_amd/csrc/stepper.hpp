@@ -115,6 +115,31 @@ struct Stepper {
     }
   }
 
+  // The single-tile form of the walk's per-tile arguments (copies the compiler keeps in the
+  // same registers).
+  struct Tile1 {
+    V8 q[1][NC];
+    int e[1];
+    float m[1], l[1];
+    f32x4 acc[1][NT];
+    __device__ __forceinline__ Tile1(const V8 (&qB)[NC], int end, float m0, float l0,
+                                     const f32x4 (&a0)[NT]) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) q[0][c] = qB[c];
+      e[0] = end;
+      m[0] = m0;
+      l[0] = l0;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[0][i] = a0[i];
+    }
+    __device__ __forceinline__ void back(float& m0, float& l0, f32x4 (&a0)[NT]) const {
+      m0 = m[0];
+      l0 = l[0];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) a0[i] = acc[0][i];
+    }
+  };
+
   // Online-softmax attention over logical blocks [j0, j1) of table row trow for KV head kvh
   // (tokens at or past end_tok are masked), taking the steps s_first, s_first + stride, ... of
   // the range, into the running (m_run, l_run, acc).
@@ -126,8 +151,10 @@ struct Stepper {
                                       int j1, int end_tok, int s_first, int stride,
                                       float& m_run, float& l_run, f32x4 (&acc)[NT],
                                       bool wait_stores = false) const {
-    walk<false>(qB, trow, kvh, j0, j1, end_tok, end_tok, end_tok, s_first, stride, m_run, l_run,
-                acc, wait_stores, VAppend());
+    Tile1 t(qB, end_tok, m_run, l_run, acc);
+    walk<false, 1>(t.q, trow, kvh, j0, j1, t.e, end_tok, end_tok, s_first, stride, t.m, t.l,
+                   t.acc, wait_stores, VAppend());
+    t.back(m_run, l_run, acc);
   }
   // The same with a token appended to one of the range's blocks (a separate instance, so that
   // the plain loop carries none of the append's registers).
@@ -135,8 +162,10 @@ struct Stepper {
                                              int j0, int j1, int end_tok, float& m_run,
                                              float& l_run, f32x4 (&acc)[NT], bool wait_stores,
                                              VAppend ap) const {
-    walk<true>(qB, trow, kvh, j0, j1, end_tok, end_tok, end_tok, 0, 1, m_run, l_run, acc,
-               wait_stores, ap);
+    Tile1 t(qB, end_tok, m_run, l_run, acc);
+    walk<true, 1>(t.q, trow, kvh, j0, j1, t.e, end_tok, end_tok, 0, 1, t.m, t.l, t.acc,
+                  wait_stores, ap);
+    t.back(m_run, l_run, acc);
   }
 
   // The same walk with a window per query column: this lane's column sees tokens below
@@ -146,15 +175,30 @@ struct Stepper {
                                             int j0, int j1, int end_lane, int end_lo, int end_v,
                                             float& m_run, float& l_run,
                                             f32x4 (&acc)[NT]) const {
-    walk<false>(qB, trow, kvh, j0, j1, end_lane, end_lo, end_v, 0, 1, m_run, l_run, acc, false,
-                VAppend());
+    Tile1 t(qB, end_lane, m_run, l_run, acc);
+    walk<false, 1>(t.q, trow, kvh, j0, j1, t.e, end_lo, end_v, 0, 1, t.m, t.l, t.acc, false,
+                   VAppend());
+    t.back(m_run, l_run, acc);
+  }
+  // Several column tiles per wave: tile u's columns take qB[u] and their windows end_lane[u];
+  // every K/V step is loaded once and multiplied into all MT tiles.  end_lo and end_v bound the
+  // windows of all tiles.
+  template <int MT>
+  __device__ __forceinline__ void walk_tiles(const V8 (&qB)[MT][NC], const int32_t* trow,
+                                             int kvh, int j0, int j1, const int (&end_lane)[MT],
+                                             int end_lo, int end_v, float (&m_run)[MT],
+                                             float (&l_run)[MT], f32x4 (&acc)[MT][NT]) const {
+    walk<false, MT>(qB, trow, kvh, j0, j1, end_lane, end_lo, end_v, 0, 1, m_run, l_run, acc,
+                    false, VAppend());
   }
 
-  template <bool APP>
-  __device__ __forceinline__ void walk(const V8 (&qB)[NC], const int32_t* trow, int kvh, int j0,
-                                       int j1, int end_tok, int end_lo, int end_v, int s_first,
-                                       int stride, float& m_run, float& l_run,
-                                       f32x4 (&acc)[NT], bool wait_stores, VAppend ap) const {
+  template <bool APP, int MT>
+  __device__ __forceinline__ void walk(const V8 (&qB)[MT][NC], const int32_t* trow, int kvh,
+                                       int j0, int j1, const int (&end_tok)[MT], int end_lo,
+                                       int end_v, int s_first, int stride, float (&m_run)[MT],
+                                       float (&l_run)[MT], f32x4 (&acc)[MT][NT],
+                                       bool wait_stores, VAppend ap) const {
+    static_assert(!APP || MT == 1, "the append instance takes one tile");
     const int nsteps = (j1 - j0 + 1) >> 1;
     if (s_first >= nsteps) return;
 
@@ -218,7 +262,7 @@ struct Stepper {
     auto compute = [&](StepRegs<D, FP8>& r, int s) {
       const int t0 = kBlock * (j0 + 2 * s);
       const int tb = t0 + tb_lane;
-      const bool partial = t0 + kStepTokens > (ROWS ? end_lo : end_tok);   // wave-uniform
+      const bool partial = t0 + kStepTokens > (ROWS ? end_lo : end_tok[0]);   // wave-uniform
 
       // the appended token: into the registers of its block's V tile, then the tile back whole
       if constexpr (APP) {
@@ -259,11 +303,13 @@ struct Stepper {
         }
       }
 
-      // scores of 8 tokens (tb + jj) for head col
-      f32x4 S[2];
+      // scores of 8 tokens (tb + jj) for column col of every tile; each K operand is widened
+      // once and multiplied into all tiles
+      f32x4 S[MT][2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        S[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < MT; ++u) S[u][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
           V8 kA;
@@ -273,48 +319,49 @@ struct Stepper {
           } else {
             kA = as_vec8<V8>(r.k[m][cc]);
           }
-          S[m] = M::mma(kA, qB[cc], S[m]);
+#pragma unroll
+          for (int u = 0; u < MT; ++u) S[u][m] = M::mma(kA, qB[u][cc], S[u][m]);
         }
       }
       float qs = qk_scale_log2;
       if constexpr (FP8) qs *= r.ks;
-      float sc[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sc[jj] = S[jj >> 2][jj & 3] * qs;
-      int nval = 8, nval_v = 8;
-      if (partial) {
-        nval = min(max(end_tok - tb, 0), 8);
-        nval_v = ROWS ? min(max(end_v - tb, 0), 8) : nval;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (jj >= nval) sc[jj] = -INFINITY;
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
-      mx = max_across_rows(mx);
-      const float m_new = fmaxf(m_run, mx);
-      // a column that has seen no key yet keeps m = -inf; its weights and rescale are then 0
-      const float m_ref = ROWS && m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_ref);
-      float pr[8], psum = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        pr[jj] = fast_exp2(sc[jj] - m_ref);
-        psum += pr[jj];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < NT; ++i) acc[i] *= alpha;
-      if constexpr (FP8) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pr[jj] *= r.vs;
-      }
 
-      // P^T as the B operand: this lane's 8 weights, in token order.
-      uint4 hi_bits, lo_bits;
-      {
+      // per tile: online softmax, rescale, and P^T as the B operand (this lane's 8 weights in
+      // token order; bf16 P as a hi/lo pair)
+      V8 pHi[MT], pLo[MT];
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        float sc[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sc[jj] = S[u][jj >> 2][jj & 3] * qs;
+        if (partial) {
+          const int nval = min(max(end_tok[u] - tb, 0), 8);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+            if (jj >= nval) sc[jj] = -INFINITY;
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
+        mx = max_across_rows(mx);
+        const float m_new = fmaxf(m_run[u], mx);
+        // a column that has seen no key yet keeps m = -inf; its weights and rescale are then 0
+        const float m_ref = ROWS && m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = fast_exp2(m_run[u] - m_ref);
+        float pr[8], psum = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          pr[jj] = fast_exp2(sc[jj] - m_ref);
+          psum += pr[jj];
+        }
+        l_run[u] = l_run[u] * alpha + psum;
+        m_run[u] = m_new;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[u][i] *= alpha;
+        if constexpr (FP8) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) pr[jj] *= r.vs;
+        }
         uint32_t h[4], l[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -324,17 +371,16 @@ struct Stepper {
             l[w] = pack2<QT>(pr[2 * w] - (float)hv[0], pr[2 * w + 1] - (float)hv[1]);
           }
         }
-        hi_bits = make_uint4(h[0], h[1], h[2], h[3]);
-        if constexpr (SPLIT_P) lo_bits = make_uint4(l[0], l[1], l[2], l[3]);
+        pHi[u] = as_vec8<V8>(make_uint4(h[0], h[1], h[2], h[3]));
+        if constexpr (SPLIT_P) pLo[u] = as_vec8<V8>(make_uint4(l[0], l[1], l[2], l[3]));
       }
-      const V8 pHi = as_vec8<V8>(hi_bits);
-      V8 pLo;
-      if constexpr (SPLIT_P) pLo = as_vec8<V8>(lo_bits);
 
       // Masked tokens get weight 0, but slots at or past end_v may hold anything (NaN
-      // included), so their V elements are zeroed before the product.
+      // included), so their V elements are zeroed before the product (each V operand is
+      // widened once and multiplied into all tiles).
       uint32_t vm[4] = {~0u, ~0u, ~0u, ~0u};
       if (partial) {
+        const int nval_v = min(max((ROWS ? end_v : end_tok[0]) - tb, 0), 8);
         if constexpr (FP8) {
           vm[0] = nval_v >= 4 ? ~0u : (nval_v <= 0 ? 0u : (1u << (8 * nval_v)) - 1u);
           vm[1] = nval_v >= 8 ? ~0u : (nval_v <= 4 ? 0u : (1u << (8 * (nval_v - 4))) - 1u);
@@ -350,11 +396,14 @@ struct Stepper {
         if constexpr (FP8) {
           vA = fp8x8_to_vec8<QT>(r.v[i].x & vm[0], r.v[i].y & vm[1]);
         } else {
-          const uint4 u = r.v[i];
-          vA = as_vec8<V8>(make_uint4(u.x & vm[0], u.y & vm[1], u.z & vm[2], u.w & vm[3]));
+          const uint4 u4 = r.v[i];
+          vA = as_vec8<V8>(make_uint4(u4.x & vm[0], u4.y & vm[1], u4.z & vm[2], u4.w & vm[3]));
         }
-        acc[i] = M::mma(vA, pHi, acc[i]);
-        if constexpr (SPLIT_P) acc[i] = M::mma(vA, pLo, acc[i]);
+#pragma unroll
+        for (int u = 0; u < MT; ++u) {
+          acc[u][i] = M::mma(vA, pHi[u], acc[u][i]);
+          if constexpr (SPLIT_P) acc[u][i] = M::mma(vA, pLo[u], acc[u][i]);
+        }
       }
     };
 

@@ -199,20 +199,34 @@ def _mdesc(**kw):
 
 
 def test_multi_workspace_size():
-    """No workspace with one partition per row tile; with several, per (row, head, partition) an
-    fp32 output row plus max and exp-sum, each array 256-byte aligned."""
-    # 4 x 2 x ceil(4*4/16) = 8 row tiles; 4096 / 8 -> 512 partitions wanted, at most
-    # ceil(8 blocks / 16) = 1 allowed
-    assert pa.pa_decode_multi_workspace_size(_mdesc()) == 0
+    """Every layout starts with the 256 KiB of arrival counters.  Balanced split (automatic; one
+    row tile per head, or two with an fp8 cache or head_dim 64): then two parts per (workgroup,
+    row tile, column), an fp32 output row plus max and exp-sum, for one workgroup per 8 two-block
+    chunks of the largest flattened block space, at most 512 workgroups.  Fixed partitions: per
+    (row, head, partition) an output row plus max and exp-sum.  The chunk kernel with one
+    partition needs none."""
+    C = _r(65536 * 4)
+
+    def split(wgs, tiles, d=64):
+        cols = wgs * 2 * tiles * 16
+        return C + _r(cols * d * 4) + _r(cols * 2 * 4)
+
+    size = pa.pa_decode_multi_workspace_size
+    # 4 x 2 heads x 8 blocks = 64 blocks -> 32 chunks -> 4 workgroups; 16 rows: one tile
+    assert size(_mdesc()) == split(4, 1)
+    # 32 rows: two tiles with head_dim 64 or an fp8 cache; 16-bit at head_dim 128: chunk kernel
+    assert size(_mdesc(max_query_len=8)) == split(4, 2)
+    assert size(_mdesc(max_query_len=8, head_dim=128, kv_dtype=pa.PA_FP8_E4M3)) == \
+        split(4, 2, 128)
+    assert size(_mdesc(max_query_len=8, head_dim=128)) == 0
+    # a large space is capped at 512 workgroups
+    assert size(_mdesc(batch=64, max_blocks_per_seq=512, head_dim=128)) == split(512, 1, 128)
+    # more than 32 rows: the chunk kernel, here with one partition and no workspace
+    assert size(_mdesc(max_query_len=16)) == 0
     d = _mdesc(partition_tokens=32, max_blocks_per_seq=10)          # 10 blocks -> 5 partitions
     rows = 16 * 8 * 5
-    assert pa.pa_decode_multi_workspace_size(d) == _r(rows * 64 * 4) + _r(rows * 2 * 4)
-    # automatic: one sequence, one tile, 4096-token table -> partitions of 16 blocks
-    d = _mdesc(batch=1, num_q_heads=2, total_queries=1, max_query_len=1,
-               max_blocks_per_seq=256)
-    rows = 1 * 2 * 16
-    assert pa.pa_decode_multi_workspace_size(d) == _r(rows * 64 * 4) + _r(rows * 2 * 4)
-    assert pa.pa_decode_multi_workspace_size(_mdesc(max_query_len=0)) == 0   # invalid
+    assert size(d) == C + _r(rows * 64 * 4) + _r(rows * 2 * 4)
+    assert size(_mdesc(max_query_len=0)) == 0                       # invalid
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -123,6 +123,29 @@ def test_prefill_chunk_shapes(case, fp8):
     m.check(m.run(), f"chunk {case} {kv}")
 
 
+SPLIT = [
+    # (q dtype, kv dtype, kv heads, group, head_dim, most draft tokens): heads of at most two
+    # row tiles take the balanced split (one wave per chunk holding every tile of a head)
+    ("bf16", "fp8_e4m3", 2, 8, 128, 4),      # two full tiles over fp8 codes
+    ("f16", "fp8_e4m3", 2, 4, 128, 8),
+    ("bf16", "bf16", 2, 8, 128, 2),          # one tile of 16-bit K/V
+    ("f16", "f16", 4, 1, 128, 8),            # one tile, several tokens in it
+    ("f16", "f16", 2, 16, 64, 2),            # two tiles at head_dim 64
+    ("bf16", "bf16", 2, 3, 64, 8),           # a partial second tile
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: f"{c[0]}-{c[1]}-kv{c[2]}g{c[3]}d{c[4]}t{c[5]}")
+def test_balanced_split_shapes(case):
+    """Ragged contexts of 1..2049 tokens cut into chunks of every alignment (pieces ending after
+    an odd number of blocks, heads cut inside and across workgroups), sequences without rows or
+    with more rows than cached tokens; rows no sequence owns stay untouched."""
+    qd, kvd, hkv, g, d, tmax = case
+    T = tuple(min(t, tmax) for t in DRAFT)
+    m = Multi(qd, kvd, hkv, g, d, LENS, T, seed=120 + SPLIT.index(case), spare_rows=3)
+    m.check(m.run(), f"split {case}")
+
+
 def test_more_queries_than_context_and_loose_bounds():
     """Rows before the context are zero; host bounds larger than needed change nothing."""
     m = Multi("bf16", "bf16", 2, 4, 128, (3, 1, 40), (6, 4, 2), seed=101, spare_rows=2)
@@ -169,3 +192,20 @@ def test_full_size_prefill_chunk():
     rng = np.random.default_rng(104)
     m = Multi("bf16", "bf16", 8, 4, 128, [4608] * 4, [512] * 4, seed=104)
     _sampled(m, 6, rng)
+
+
+def test_full_size_fp8_verification():
+    """4 sequences of 32768 fp8 tokens, GQA 64/8, 4 draft tokens each: two row tiles per head in
+    one wave (sampled rows)."""
+    rng = np.random.default_rng(105)
+    m = Multi("bf16", "fp8_e4m3", 8, 8, 128, [32768] * 4, [4] * 4, seed=105)
+    _sampled(m, 2, rng)
+
+
+@pytest.mark.parametrize("kvd,T", [("fp8_e4m3", 4), ("bf16", 2)])
+def test_one_head_over_many_workgroups(kvd, T):
+    """One KV head of 65536 tokens: two-block chunks, so its parts come from hundreds of
+    workgroups and are merged in LDS-staged batches (sampled rows)."""
+    rng = np.random.default_rng(106)
+    m = Multi("bf16", kvd, 1, 8, 128, [65536], [T], seed=106)
+    _sampled(m, 2, rng)
