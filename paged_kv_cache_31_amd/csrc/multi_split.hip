@@ -471,8 +471,52 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   const int WGB = kWaves * Cw;                      // blocks per workgroup range
   for (int g = 0; g < ngroups; ++g) {
     const Group gr = group(g);
-    if ((gr.last >> 1) != wave) continue;           // merged by the wave holding its last piece
-    const bool last_is_first = (gr.last & 1) == 0;
+    // slot 1: the head starts strictly inside this workgroup's range; slot 0: at or before
+    const int wslot = gr.s0 > (int)blockIdx.x * WGB ? 1 : 0;
+    if (gr.last & 1) {
+      // Every piece of the group is parked: all waves merge it, each a share of the (tile,
+      // 16-dim block) pairs, with weights from one pass over the pieces' maxima, so that all
+      // LDS reads of a pair are issued at once.
+      for (int x = wave; x < MT * NT; x += kWaves) {
+        const int u = x / NT, t = x - u * NT;
+        float M_ = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+          if ((gr.slots >> k) & 1) M_ = fmaxf(M_, sm_pm[k >> 1][u][col]);
+        const float Mr = M_ == -INFINITY ? 0.0f : M_;
+        float gl = 0.0f;
+        f32x4 go = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+          if ((gr.slots >> k) & 1) {
+            const float w = fast_exp2(sm_pm[k >> 1][u][col] - Mr);
+            gl += w * sm_pl[k >> 1][u][col];
+            go += w * sm_pacc[k >> 1][u][t][lane];
+          }
+        if (gr.whole) {
+          const TileRows tr(u, col, rows_of(gr.b), G, len_of(gr.b));
+          const long long n = (long long)a.query_start[gr.b] + tr.i;
+          if (tr.real && n >= 0 && n < a.total_queries) {
+            const float inv = gl > 0.0f ? 1.0f / gl : 0.0f;
+            E* o = reinterpret_cast<E*>(a.out) + ((size_t)n * Hq + gr.kvh * G + tr.g) * D +
+                   16 * t + 4 * grp;
+            *reinterpret_cast<uint2*>(o) = make_uint2(pack2<QT>(go[0] * inv, go[1] * inv),
+                                                      pack2<QT>(go[2] * inv, go[3] * inv));
+          }
+        } else {
+          const size_t ps = (((size_t)blockIdx.x * 2 + wslot) * MT + u) * 16 + col;
+          store_coherent(a.ws_acc + ps * D + 16 * t + 4 * grp, go);
+          if (t == 0 && grp == 0) {
+            store_coherent(a.ws_ml + ps * 2, M_);
+            store_coherent(a.ws_ml + ps * 2 + 1, gl);
+          }
+        }
+      }
+      continue;
+    }
+    // The group ends with a first piece, held in the registers of the wave that walked it:
+    // that wave merges the group.
+    if ((gr.last >> 1) != wave) continue;
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
       float gm = -INFINITY, gl = 0.0f;
@@ -485,7 +529,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
         rest &= rest - 1;
         float pm, pl;
         f32x4 pa[NT];
-        if (k == gr.last && last_is_first) {        // this wave's first piece, in registers
+        if (k == gr.last) {                         // this wave's first piece, in registers
           pm = fm[u];
           pl = fl[u];
 #pragma unroll
@@ -510,8 +554,6 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
         if (tr.real && n >= 0 && n < a.total_queries)
           store_row<QT, NT>(a.out, (size_t)n * Hq + gr.kvh * G + tr.g, D, grp, gl, go);
       } else {
-        // slot 1: the head starts strictly inside this workgroup's range; slot 0: at or before
-        const int wslot = gr.s0 > (int)blockIdx.x * WGB ? 1 : 0;
         const size_t ps = (((size_t)blockIdx.x * 2 + wslot) * MT + u) * 16 + col;
 #pragma unroll
         for (int t = 0; t < NT; ++t) store_coherent(a.ws_acc + ps * D + 16 * t + 4 * grp, go[t]);
