@@ -450,14 +450,12 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
 
   // ---- 3. Merge the cut pieces of the workgroup's chunks.  The slots (each wave's first and
   // last piece, in chunk order) of one sequence head are consecutive among the used slots and
-  // form a group.  The waves take the groups in turn (wave w: groups w, w + kWaves, ...) and
-  // merge all 16-dim tiles of a group, so groups are merged in parallel and the per-group work
-  // (slot search, weights) is done once.  A group that covers all blocks of its sequence head is
-  // written out.  A group cut
-  // at the workgroup boundary (at most two: the first group, continuing from before the range,
-  // and the last, running past its end) is published; then, after one wait and one round of
-  // arrival counts for both, the last workgroup to publish a part of a sequence head merges all
-  // of them.
+  // form a group.  The waves take (group, 16-dim tile) pairs in turn, so even a workgroup whose
+  // chunks all belong to one long head merges with every wave.  A group that covers all blocks
+  // of its sequence head is written out.  A group cut at the workgroup boundary (at most two:
+  // the first group, continuing from before the range, and the last, running past its end) is
+  // published; then, after one wait and one round of arrival counts for both, the last
+  // workgroup to publish a part of a sequence head merges all of them.
   const int WGB = kWaves * Cw;                      // blocks per workgroup range
   constexpr int NS = 2 * kWaves;                    // slots
   static_assert(NS <= 64, "one slot per lane");
@@ -494,63 +492,107 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
     return r;
   };
 
-  for (int g = wave; g < ngroups; g += kWaves) {
-    const Group gr = group(g);
-    // log-sum-exp over the group's slots in chunk order; the next slot's LDS reads are issued
-    // before the current one is folded in (the last round reads its own slot again)
-    uint64_t rest = gr.slots;
-    int k = __builtin_ctzll(rest);
-    rest &= rest - 1;
-    float pm = sm_pm[k >> 1][k & 1][col], pl = sm_pl[k >> 1][k & 1][col];
-    f32x4 pa[NT];
+  // With one or two groups (long heads), (group, 16-dim tile) pairs are spread over the waves,
+  // so that every wave merges: a pair's weights come from one pass over the group's maxima,
+  // and its LDS reads are then issued at once.  With more, each wave merges whole groups
+  // (weights and slot search once per group, the next slot's reads in flight); spreading
+  // pairs there was measured slower (mixed batch, 204 -> 210 us: the prefix fold and the
+  // group search are then repeated per tile).
+  if (ngroups <= 2) {
+    for (int x = wave; x < ngroups * NT; x += kWaves) {
+      const int g = x / NT, t = x - g * NT;
+      const Group gr = group(g);
+      float gm = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) pa[t] = sm_pacc[k >> 1][k & 1][t][lane];
-    float gm = -INFINITY, gl = 0.0f;
-    f32x4 go[NT];
+      for (int k = 0; k < NS; ++k)
+        if ((gr.slots >> k) & 1) gm = fmaxf(gm, sm_pm[k >> 1][k & 1][col]);
+      float gl = 0.0f;
+      f32x4 go[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-    for (int t = 0; t < NT; ++t) go[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (;;) {
-      const bool more = rest != 0;
-      const int kn = more ? __builtin_ctzll(rest) : k;
-      const float pmn = sm_pm[kn >> 1][kn & 1][col], pln = sm_pl[kn >> 1][kn & 1][col];
-      f32x4 pan[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) pan[t] = sm_pacc[kn >> 1][kn & 1][t][lane];
-      const float M_ = fmaxf(gm, pm);
-      const float x = fast_exp2(gm - M_), y = fast_exp2(pm - M_);
-      gl = gl * x + pl * y;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) go[t] = go[t] * x + pa[t] * y;
-      gm = M_;
-      if (!more) break;
-      rest &= rest - 1;
-      k = kn;
-      pm = pmn;
-      pl = pln;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) pa[t] = pan[t];
+      for (int k = 0; k < NS; ++k)
+        if ((gr.slots >> k) & 1) {
+          const float w = fast_exp2(sm_pm[k >> 1][k & 1][col] - gm);
+          gl += w * sm_pl[k >> 1][k & 1][col];
+          go[0] += w * sm_pacc[k >> 1][k & 1][t][lane];
+        }
+      if (col >= G) continue;
+      if (gr.whole) {
+        const size_t row = (size_t)gr.b * Hq + gr.kvh * G + col;
+        if (gr.skip > 0) fold_prefix<D>(a, row, prefix_parts(gr.skip), grp, t, 1, gm, gl, go);
+        E* out = reinterpret_cast<E*>(a.out) + row * D + 16 * t + 4 * grp;
+        *reinterpret_cast<uint2*>(out) = make_uint2(pack2<QT>(go[0][0] / gl, go[0][1] / gl),
+                                                    pack2<QT>(go[0][2] / gl, go[0][3] / gl));
+      } else {
+        // slot 1 holds the group whose sequence head starts strictly inside this workgroup's
+        // range (it runs past the end); slot 0 the one that started at or before the range start
+        const int wslot = gr.s0 > (int)blockIdx.x * WGB ? 1 : 0;
+        const size_t ps = ((size_t)blockIdx.x * 2 + wslot) * G + col;
+        store_coherent(a.ws_acc + ps * D + 16 * t + 4 * grp, go[0]);   // device-coherent stores
+        if (t == 0 && grp == 0) {
+          store_coherent(a.ws_ml + ps * 2, gm);
+          store_coherent(a.ws_ml + ps * 2 + 1, gl);
+        }
+      }
     }
-    if (col >= G) continue;
-    if (gr.whole) {
-      const size_t row = (size_t)gr.b * Hq + gr.kvh * G + col;
-      if (gr.skip > 0) fold_prefix<D>(a, row, prefix_parts(gr.skip), grp, 0, 1, gm, gl, go);
-      E* out = reinterpret_cast<E*>(a.out) + row * D + 4 * grp;
+  } else {
+    for (int g = wave; g < ngroups; g += kWaves) {
+      const Group gr = group(g);
+      // log-sum-exp over the group's slots in chunk order; the next slot's LDS reads are issued
+      // before the current one is folded in (the last round reads its own slot again)
+      uint64_t rest = gr.slots;
+      int k = __builtin_ctzll(rest);
+      rest &= rest - 1;
+      float pm = sm_pm[k >> 1][k & 1][col], pl = sm_pl[k >> 1][k & 1][col];
+      f32x4 pa[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        *reinterpret_cast<uint2*>(out + 16 * t) =
-            make_uint2(pack2<QT>(go[t][0] / gl, go[t][1] / gl),
-                       pack2<QT>(go[t][2] / gl, go[t][3] / gl));
-    } else {
-      // slot 1 holds the group whose sequence head starts strictly inside this workgroup's
-      // range (it runs past the end); slot 0 the one that started at or before the range start
-      const int wslot = gr.s0 > (int)blockIdx.x * WGB ? 1 : 0;
-      const size_t ps = ((size_t)blockIdx.x * 2 + wslot) * G + col;
+      for (int t = 0; t < NT; ++t) pa[t] = sm_pacc[k >> 1][k & 1][t][lane];
+      float gm = -INFINITY, gl = 0.0f;
+      f32x4 go[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t)                 // device-coherent stores
-        store_coherent(a.ws_acc + ps * D + 16 * t + 4 * grp, go[t]);
-      if (grp == 0) {
-        store_coherent(a.ws_ml + ps * 2, gm);
-        store_coherent(a.ws_ml + ps * 2 + 1, gl);
+      for (int t = 0; t < NT; ++t) go[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (;;) {
+        const bool more = rest != 0;
+        const int kn = more ? __builtin_ctzll(rest) : k;
+        const float pmn = sm_pm[kn >> 1][kn & 1][col], pln = sm_pl[kn >> 1][kn & 1][col];
+        f32x4 pan[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pan[t] = sm_pacc[kn >> 1][kn & 1][t][lane];
+        const float M_ = fmaxf(gm, pm);
+        const float x = fast_exp2(gm - M_), y = fast_exp2(pm - M_);
+        gl = gl * x + pl * y;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) go[t] = go[t] * x + pa[t] * y;
+        gm = M_;
+        if (!more) break;
+        rest &= rest - 1;
+        k = kn;
+        pm = pmn;
+        pl = pln;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pa[t] = pan[t];
+      }
+      if (col >= G) continue;
+      if (gr.whole) {
+        const size_t row = (size_t)gr.b * Hq + gr.kvh * G + col;
+        if (gr.skip > 0) fold_prefix<D>(a, row, prefix_parts(gr.skip), grp, 0, 1, gm, gl, go);
+        E* out = reinterpret_cast<E*>(a.out) + row * D + 4 * grp;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          *reinterpret_cast<uint2*>(out + 16 * t) =
+              make_uint2(pack2<QT>(go[t][0] / gl, go[t][1] / gl),
+                         pack2<QT>(go[t][2] / gl, go[t][3] / gl));
+      } else {
+        // slot 1 holds the group whose sequence head starts strictly inside this workgroup's
+        // range (it runs past the end); slot 0 the one that started at or before the range start
+        const int wslot = gr.s0 > (int)blockIdx.x * WGB ? 1 : 0;
+        const size_t ps = ((size_t)blockIdx.x * 2 + wslot) * G + col;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)                 // device-coherent stores
+          store_coherent(a.ws_acc + ps * D + 16 * t + 4 * grp, go[t]);
+        if (grp == 0) {
+          store_coherent(a.ws_ml + ps * 2, gm);
+          store_coherent(a.ws_ml + ps * 2 + 1, gl);
+        }
       }
     }
   }
