@@ -209,3 +209,31 @@ def test_one_head_over_many_workgroups(kvd, T):
     rng = np.random.default_rng(106)
     m = Multi("bf16", kvd, 1, 8, 128, [65536], [T], seed=106)
     _sampled(m, 2, rng)
+
+
+def test_one_workspace_serves_every_entry_point():
+    """The binding's workspace of a stream is shared by all calls on it: a fixed-partition call
+    (partial results after the counter region) must leave the arrival counters of the balanced
+    split and of pa_decode at zero, call after call, in any order."""
+    m = Multi("bf16", "fp8_e4m3", 2, 8, 128, LENS, [min(t, 4) for t in DRAFT], seed=107,
+              spare_rows=2)
+    ref = m.reference()
+    wl, s = m.wl, m.spec
+    ks, vs = torch.from_numpy(wl.k_scale).cuda(), torch.from_numpy(wl.v_scale).cuda()
+    # single-query decode of each sequence's last row: the multi-query row at position L - 1
+    has = [b for b in range(s.batch) if m.T[b] > 0]
+    last = np.array([int(m.qs[b + 1]) - 1 for b in has])
+    qd = dev_bits(np.ascontiguousarray(m.q[last]), s.q_dtype)
+    kd, vd = dev_bits(m.k, s.kv_dtype), dev_bits(m.v, s.kv_dtype)
+    tables = torch.from_numpy(np.ascontiguousarray(wl.block_tables[has])).cuda()
+    lens = torch.from_numpy(np.ascontiguousarray(wl.context_lens[has])).cuda()
+    for order in ((32, 0, "decode"), ("decode", 32, 0), (0, "decode", 32)):
+        for step in order:
+            if step == "decode":
+                out = torch.empty_like(qd)
+                pa.pa_decode(qd, kd, vd, tables, lens, float(wl.scale), out, k_scale=ks,
+                             v_scale=vs)
+                torch.cuda.synchronize()
+                assert_close(host_bits(out), ref[last], s.q_dtype, f"decode after {order}")
+            else:
+                m.check(m.run(partition_tokens=step), f"multi P{step} in {order}", ref)
