@@ -221,10 +221,10 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
  * with p < 0 sees no token and is zero.  fp32 accumulation; within 2e-3 absolute + 2e-3 relative
  * of the exact result, and the same bits on every call with the same inputs.
  *
- * With partition_tokens 0, heads of at most 16 query rows (T_b * group), and of at most 32 with
- * an fp8 cache or head_dim 64, get the decode's balanced split-KV: equal chunks of the batch's
- * (sequence, KV head, block) space, one per wave, each wave holding all row tiles of a head,
- * partial results merged by log-sum-exp inside the kernel.  Larger heads take a kernel that
+ * With partition_tokens 0, heads of at most 32 query rows (T_b * group) get the decode's
+ * balanced split-KV: equal chunks of the batch's (sequence, KV head, block) space, each walked
+ * by one wave holding both 16-row tiles of a head (two waves, one tile each, for 16-bit caches
+ * at head_dim 128), partial results merged by log-sum-exp inside the kernel.  Larger heads take a kernel that
  * stages K/V in LDS for blocks of rows; a fixed partition_tokens cuts every row tile's keys into
  * partitions merged by a second kernel.
  *

@@ -86,13 +86,13 @@ constexpr int kSplitMergeStage = 16;    // parts staged in LDS per batch beyond 
 // Merges all published parts of sequence head (b, kvh) (workgroups c0..c1; c0 holds it in its
 // slot 1 unless the head starts exactly at its range) and writes its rows.  Every thread of the
 // workgroup calls it.
-template <int D, int QT, int MT>
+template <int D, int QT, int TT>
 __device__ void merge_split_published(const MultiArgs& a, int b, int kvh, int s0, int c0, int c1,
-                                      int WGB, float (&sm_mw)[kSplitMergeStage][16 * MT],
-                                      float (&sm_ml)[kSplitMergeStage][16 * MT],
-                                      float (&sm_hm)[16 * MT], float (&sm_hl)[16 * MT]) {
+                                      int WGB, float (&sm_mw)[kSplitMergeStage][16 * TT],
+                                      float (&sm_ml)[kSplitMergeStage][16 * TT],
+                                      float (&sm_hm)[16 * TT], float (&sm_hl)[16 * TT]) {
   typedef typename Mfma<QT>::elem E;
-  constexpr int R = 16 * MT;
+  constexpr int R = 16 * TT;
   constexpr int NTH = 64 * kWaves;
   constexpr int EPT = (R * D / 4 + NTH - 1) / NTH;
   const int tid = threadIdx.x;
@@ -104,7 +104,7 @@ __device__ void merge_split_published(const MultiArgs& a, int b, int kvh, int s0
   const int nparts = c1 - c0 + 1;
   auto part_of = [&](int pi, int r) -> size_t {
     const int cc = c0 + pi;
-    return (((size_t)cc * 2 + (pi == 0 ? first_slot : 0)) * MT + r / 16) * 16 + (r & 15);
+    return (((size_t)cc * 2 + (pi == 0 ? first_slot : 0)) * TT + r / 16) * 16 + (r & 15);
   };
   auto out_row = [&](int r) -> long long {      // -1: no row of out
     const long long n = (long long)q0 + r / G;
@@ -208,23 +208,28 @@ __device__ void merge_split_published(const MultiArgs& a, int b, int kvh, int s0
   }
 }
 
-template <int D, int QT, int KVT, int MT>
+template <int D, int QT, int KVT, int MT, int RT>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(MultiArgs a) {
-  typedef Stepper<D, QT, KVT, true, true> St;
+  // RT waves share a chunk (one of them loads a block from HBM, the others find it in the
+  // cache, so only then are the loads cached), each holding MT of the head's TT row tiles
+  typedef Stepper<D, QT, KVT, RT == 1, true> St;
   typedef typename St::V8 V8;
   typedef typename St::E E;
   constexpr int NC = St::NC;
   constexpr int NT = St::NT;
   constexpr int NTH = 64 * kWaves;
+  constexpr int KW = kWaves / RT;                   // chunks per workgroup
+  constexpr int TT = MT * RT;                       // row tiles per head
+  static_assert(kWaves % RT == 0, "waves per chunk");
 
   __shared__ int sm_wave_sum[kWaves];
-  __shared__ int sm_start_b[kWaves], sm_start_off[kWaves];
+  __shared__ int sm_start_b[KW], sm_start_off[KW];
   __shared__ SplitMeta sm_meta[kWaves][2];          // [wave][first cut piece / last cut piece]
   __shared__ float sm_pm[kWaves][MT][16], sm_pl[kWaves][MT][16];
   __shared__ f32x4 sm_pacc[kWaves][MT][NT][64];     // one piece per wave
   __shared__ int sm_last[2];
-  __shared__ float sm_mw[kSplitMergeStage][16 * MT], sm_ml[kSplitMergeStage][16 * MT];
-  __shared__ float sm_hm[16 * MT], sm_hl[16 * MT];
+  __shared__ float sm_mw[kSplitMergeStage][16 * TT], sm_ml[kSplitMergeStage][16 * TT];
+  __shared__ float sm_hm[16 * TT], sm_hl[16 * TT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   int Cw = (W + a.total_lanes - 1) / a.total_lanes;
   Cw = max(2, (Cw + 1) & ~1);
   const int nch = (W + Cw - 1) / Cw;
-  const int c_first = blockIdx.x * kWaves;
+  const int c_first = blockIdx.x * KW;
   {
     int run = before + incl - tot;
     for (int i = 0; i < per; ++i) {
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
       const int L = len_of(b);
       const int nb = Hkv * blocks_of(L);
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < KW; ++w) {
         const long start = (long)(c_first + w) * Cw;
         if (start >= run && start < run + nb) {
           sm_start_b[w] = b;
@@ -297,7 +302,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   // ---- 2. This wave's chunk, piece by piece, all row tiles of a head at once.  A chunk's
   // first piece, if cut and not also its last, is parked in the wave's LDS slot; its last cut
   // piece stays in registers for the merge.
-  const int c = c_first + wave;
+  const int cl = wave / RT, rt = wave - cl * RT;    // chunk of the workgroup; tiles rt*MT + u
+  const int c = c_first + cl;
   const St st(a, lane);
   const int a0 = c * Cw;
   const int a1 = min(a0 + Cw, W);
@@ -305,11 +311,11 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   int pos = a0;
   bool more = false;
   if (c < nch) {
-    b = uniform(sm_start_b[wave]);
+    b = uniform(sm_start_b[cl]);
     L = len_of(b);
     T = rows_of(b);
     nblk = blocks_of(L);
-    const int off = uniform(sm_start_off[wave]);
+    const int off = uniform(sm_start_off[cl]);
     kvh = off / nblk;
     j = off - kvh * nblk;
     more = true;
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
     int end_lo = INT_MAX, end_hi = 0;
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
-      const TileRows tr(u, col, T, G, L);
+      const TileRows tr(rt * MT + u, col, T, G, L);
       const long long n = (long long)q0 + tr.i;
       const bool row_ok = tr.real && n >= 0 && n < a.total_queries;
       st.load_q(qB[u], row_ok ? reinterpret_cast<const E*>(a.q) +
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
     if (j0 == 0 && j1 == nblk) {
 #pragma unroll
       for (int u = 0; u < MT; ++u) {
-        const TileRows tr(u, col, T, G, L);
+        const TileRows tr(rt * MT + u, col, T, G, L);
         const long long n = (long long)q0 + tr.i;
         if (tr.real && n >= 0 && n < a.total_queries)
           store_row<QT, NT>(a.out, (size_t)n * Hq + kvh * G + tr.g, D, grp, l_run[u], acc[u]);
@@ -401,29 +407,34 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   }
   __syncthreads();
 
-  // ---- 3. Merge the cut pieces.  Slot 2w is wave w's first cut piece (parked in LDS), slot
-  // 2w+1 its last (in its registers); in slot order the pieces of one sequence head are
-  // consecutive and form a group.  Only a group's last piece can be a first piece (a first
+  // ---- 3. Merge the cut pieces.  Slots are ordered by tile set (rt), then chunk, then first
+  // / last: slot 2c (of tile set rt) is the first cut piece of the chunk's wave (parked in
+  // LDS), slot 2c+1 its last (in its registers).  In slot order the pieces of one (sequence
+  // head, tile set) are consecutive and form a group; every tile set has the same groups (its
+  // waves walked the same pieces).  Only a group's last piece can be a first piece (a first
   // piece that is not also the chunk's last ends its head), so after each wave takes its
   // parked piece back into registers and parks its last piece instead, every piece of a group
-  // but the last is in LDS, and the group is merged by the wave holding its last piece.
+  // but the last is in LDS.
   constexpr int NS = 2 * kWaves;
   static_assert(NS <= 64, "one slot per lane");
+  auto wave_of = [&](int x) { return ((x % (2 * KW)) >> 1) * RT + x / (2 * KW); };
   SplitMeta mt{-1, 0, 0, 0, 0, 0};
-  if (lane < NS) mt = sm_meta[lane >> 1][lane & 1];
+  const int my_rt = lane < NS ? lane / (2 * KW) : -1;
+  if (lane < NS) mt = sm_meta[wave_of(lane)][lane & 1];
   const bool used = lane < NS && mt.b >= 0;
   const uint64_t used_mask = __ballot(used);
   const uint64_t before_me = used_mask & ((1ull << lane) - 1ull);
   const int prev = before_me ? 63 - __clzll((long long)before_me) : lane;
   const int prev_b = __shfl(mt.b, prev), prev_kvh = __shfl(mt.kvh, prev);
-  const uint64_t start_mask =
-      __ballot(used && (prev == lane || prev_b != mt.b || prev_kvh != mt.kvh));
+  const int prev_rt = __shfl(my_rt, prev);
+  const uint64_t start_mask = __ballot(
+      used && (prev == lane || prev_b != mt.b || prev_kvh != mt.kvh || prev_rt != my_rt));
   const int ngroups = __popcll(start_mask);
   const int gid = __popcll(start_mask & ((2ull << lane) - 1ull)) - 1;
 
   struct Group {
     uint64_t slots;
-    int b, kvh, j0, j1, nblk, s0, last;
+    int b, kvh, j0, j1, nblk, s0, last, rt;
     bool whole;
   };
   auto group = [&](int g) {
@@ -437,6 +448,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
     r.nblk = __builtin_amdgcn_readlane(mt.nblk, f);
     r.s0 = __builtin_amdgcn_readlane(mt.s0, f);
     r.last = l;
+    r.rt = f / (2 * KW);
     r.whole = r.j0 == 0 && r.j1 == r.nblk;
     return r;
   };
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   }
   __syncthreads();
 
-  const int WGB = kWaves * Cw;                      // blocks per workgroup range
+  const int WGB = KW * Cw;                          // blocks per workgroup range
   for (int g = 0; g < ngroups; ++g) {
     const Group gr = group(g);
     // slot 1: the head starts strictly inside this workgroup's range; slot 0: at or before
@@ -482,19 +494,19 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
         float M_ = -INFINITY;
 #pragma unroll
         for (int k = 0; k < NS; ++k)
-          if ((gr.slots >> k) & 1) M_ = fmaxf(M_, sm_pm[k >> 1][u][col]);
+          if ((gr.slots >> k) & 1) M_ = fmaxf(M_, sm_pm[wave_of(k)][u][col]);
         const float Mr = M_ == -INFINITY ? 0.0f : M_;
         float gl = 0.0f;
         f32x4 go = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < NS; ++k)
           if ((gr.slots >> k) & 1) {
-            const float w = fast_exp2(sm_pm[k >> 1][u][col] - Mr);
-            gl += w * sm_pl[k >> 1][u][col];
-            go += w * sm_pacc[k >> 1][u][t][lane];
+            const float w = fast_exp2(sm_pm[wave_of(k)][u][col] - Mr);
+            gl += w * sm_pl[wave_of(k)][u][col];
+            go += w * sm_pacc[wave_of(k)][u][t][lane];
           }
         if (gr.whole) {
-          const TileRows tr(u, col, rows_of(gr.b), G, len_of(gr.b));
+          const TileRows tr(gr.rt * MT + u, col, rows_of(gr.b), G, len_of(gr.b));
           const long long n = (long long)a.query_start[gr.b] + tr.i;
           if (tr.real && n >= 0 && n < a.total_queries) {
             const float inv = gl > 0.0f ? 1.0f / gl : 0.0f;
@@ -504,7 +516,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
                                                       pack2<QT>(go[2] * inv, go[3] * inv));
           }
         } else {
-          const size_t ps = (((size_t)blockIdx.x * 2 + wslot) * MT + u) * 16 + col;
+          const size_t ps = (((size_t)blockIdx.x * 2 + wslot) * TT + gr.rt * MT + u) * 16 + col;
           store_coherent(a.ws_acc + ps * D + 16 * t + 4 * grp, go);
           if (t == 0 && grp == 0) {
             store_coherent(a.ws_ml + ps * 2, M_);
@@ -516,7 +528,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
     }
     // The group ends with a first piece, held in the registers of the wave that walked it:
     // that wave merges the group.
-    if ((gr.last >> 1) != wave) continue;
+    if (wave_of(gr.last) != wave) continue;
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
       float gm = -INFINITY, gl = 0.0f;
@@ -535,7 +547,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
 #pragma unroll
           for (int t = 0; t < NT; ++t) pa[t] = facc[u][t];
         } else {                                    // a last piece, parked
-          const int wk = k >> 1;
+          const int wk = wave_of(k);
           pm = sm_pm[wk][u][col];
           pl = sm_pl[wk][u][col];
 #pragma unroll
@@ -549,12 +561,12 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
         gm = M_;
       }
       if (gr.whole) {
-        const TileRows tr(u, col, rows_of(gr.b), G, len_of(gr.b));
+        const TileRows tr(gr.rt * MT + u, col, rows_of(gr.b), G, len_of(gr.b));
         const long long n = (long long)a.query_start[gr.b] + tr.i;
         if (tr.real && n >= 0 && n < a.total_queries)
           store_row<QT, NT>(a.out, (size_t)n * Hq + gr.kvh * G + tr.g, D, grp, gl, go);
       } else {
-        const size_t ps = (((size_t)blockIdx.x * 2 + wslot) * MT + u) * 16 + col;
+        const size_t ps = (((size_t)blockIdx.x * 2 + wslot) * TT + gr.rt * MT + u) * 16 + col;
 #pragma unroll
         for (int t = 0; t < NT; ++t) store_coherent(a.ws_acc + ps * D + 16 * t + 4 * grp, go[t]);
         if (grp == 0) {
@@ -565,13 +577,15 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
     }
   }
 
-  // the cut heads this workgroup publishes (at most two: its first and last group)
+  // the cut heads this workgroup publishes (at most two: the first and last group of a tile
+  // set; the other sets' groups are the same heads)
+  const int ngt = ngroups / RT;
   int npub = 0, pb_b[2] = {0, 0}, pb_kvh[2] = {0, 0}, pb_s0[2] = {0, 0};
   int pb_c0[2] = {0, 0}, pb_c1[2] = {0, 0};
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    if (x >= ngroups) break;
-    const Group gr = group(x == 0 ? 0 : ngroups - 1);
+    if (x >= ngt) break;
+    const Group gr = group(x == 0 ? 0 : ngt - 1);
     if (gr.whole) continue;
     const int c0 = gr.s0 / WGB, c1 = (gr.s0 + gr.nblk - 1) / WGB;
 #pragma unroll
@@ -599,7 +613,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   for (int x = 0; x < npub; ++x) {
     if (!sm_last[x]) continue;
     const int c1 = x == 0 ? pb_c1[0] : pb_c1[1];
-    merge_split_published<D, QT, MT>(a, x == 0 ? pb_b[0] : pb_b[1], x == 0 ? pb_kvh[0] : pb_kvh[1],
+    merge_split_published<D, QT, TT>(a, x == 0 ? pb_b[0] : pb_b[1], x == 0 ? pb_kvh[0] : pb_kvh[1],
                                      x == 0 ? pb_s0[0] : pb_s0[1], x == 0 ? pb_c0[0] : pb_c0[1],
                                      c1, WGB, sm_mw, sm_ml, sm_hm, sm_hl);
     if (tid == 0)                                   // ready for the next call
@@ -607,18 +621,26 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   }
 }
 
+// The instances: one tile per head (MT 1, RT 1); two tiles in one wave where its registers hold
+// them (fp8 or head_dim 64: MT 2); else two waves per chunk (RT 2).
+template <int D, int KVT>
+constexpr bool kTwoTilesOneWave = D == 64 || KVT == DT_FP8;
+
 template <int D, int QT, int KVT>
 static hipError_t launch_split_t(const MultiArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.total_lanes / kWaves)), block(64 * kWaves);
-  switch (a.split_rt) {
-    case 1: hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 1>), grid, block, 0, stream, a); break;
-    case 2:
-      if constexpr (D == 64 || KVT == DT_FP8) {
-        hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 2>), grid, block, 0, stream, a);
-        break;
-      }
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+  const dim3 block(64 * kWaves);
+  if (a.split_rt == 1) {
+    hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 1, 1>), dim3((unsigned)(a.total_lanes / kWaves)),
+                       block, 0, stream, a);
+  } else if (a.split_rt == 2) {
+    if constexpr (kTwoTilesOneWave<D, KVT>)
+      hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 2, 1>),
+                         dim3((unsigned)(a.total_lanes / kWaves)), block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 1, 2>),
+                         dim3((unsigned)(a.total_lanes / (kWaves / 2))), block, 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -627,12 +649,15 @@ template <int D, int QT, int KVT>
 static int split_occupancy_t(int rt) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
-  if (rt == 1)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 1>,
+  if (rt == 1) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 1, 1>,
                                                      64 * kWaves, 0);
-  else if constexpr (D == 64 || KVT == DT_FP8) {
-    if (rt == 2)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 2>,
+  } else if (rt == 2) {
+    if constexpr (kTwoTilesOneWave<D, KVT>)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 2, 1>,
+                                                       64 * kWaves, 0);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 1, 2>,
                                                        64 * kWaves, 0);
   }
   return e == hipSuccess ? n : 0;

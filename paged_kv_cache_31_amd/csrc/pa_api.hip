@@ -326,7 +326,7 @@ PA_EXPORT pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q,
     const pa::SplitLayout lay = pa::split_layout(p, desc->cache.head_dim);
     int64_t wgs = resident_split_wgs(desc, p.split_rt);
     if (wgs > p.split_wgs) wgs = p.split_wgs;
-    a.total_lanes = (int)(wgs * pa::kWaves);
+    a.total_lanes = (int)(wgs * (pa::kWaves / p.split_waves));
     a.ws_cnt = static_cast<int*>(workspace);
     a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.acc);
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml);

@@ -160,9 +160,9 @@ struct MultiArgs {
   long long total_items;
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
   int chunk_wide;              // chunk_kernel shape: 1 kChunkWide, 0 kChunkNarrow
-  // Balanced split (multi_split_kernel): split_rt > 0 row tiles per head, all in one wave.
+  // Balanced split (multi_split_kernel): split_rt > 0 row tiles per head.
   int split_rt;
-  int total_lanes;             // chunks of the flattened block space (= launched waves)
+  int total_lanes;             // chunks of the flattened block space
   int* ws_cnt;                 // [kMaxWorkgroups] arrival counters, zero between calls
   float qk_scale_log2;
 };
@@ -191,15 +191,19 @@ struct MultiPlan {
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
   int chunk_wide;              // chunk_kernel shape: 1 wide, 0 narrow
   int split_rt;                // > 0: multi_split_kernel with this many row tiles per head
+  int split_waves;             // multi_split_kernel: waves per chunk
   long long split_wgs;         // multi_split_kernel: most workgroups a launch may use
 };
 
-// multi_split_kernel takes heads of one row tile, and of two where a wave's registers hold both
-// tiles' accumulators and query operands next to the K/V steps in flight (fp8 caches or
-// head_dim 64: no spills; two tiles of 16-bit K/V at head_dim 128 would spill, so those heads
-// go to chunk_kernel).  It launches one workgroup per resident slot, at most
+// multi_split_kernel takes heads of one or two row tiles.  Two tiles go to one wave where its
+// registers hold both tiles' accumulators and query operands next to the K/V steps in flight
+// (fp8 caches or head_dim 64); two tiles of 16-bit K/V at head_dim 128 would spill there and
+// take two waves per chunk instead.  A launch is one workgroup per resident slot, at most
 // kMaxSplitWorkgroups (a workspace bound known without a GPU: twice the 256 CUs of an MI355X).
-inline int split_max_tiles(int head_dim, bool fp8_kv) { return fp8_kv || head_dim == 64 ? 2 : 1; }
+constexpr int kSplitMaxTiles = 2;
+inline int split_chunk_waves(int tiles, int head_dim, bool fp8_kv) {
+  return tiles == 2 && !fp8_kv && head_dim != 64 ? 2 : 1;
+}
 constexpr long kMaxSplitWorkgroups = 512;
 
 // Key partitions for `base` independent units so that about `target` units run, each at least
@@ -234,13 +238,16 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
   p.row_blocks = 0;
   p.chunk_wide = 0;
   p.split_rt = 0;
+  p.split_waves = 0;
   p.split_wgs = 0;
-  if (partition_tokens == 0 && p.tiles_per_head <= split_max_tiles(head_dim, fp8_kv)) {
-    // balanced split: one chunk per wave, all row tiles of a head in the wave; at least two
-    // blocks per chunk, so the space never needs more than half its blocks in chunks
+  if (partition_tokens == 0 && p.tiles_per_head <= kSplitMaxTiles) {
+    // balanced split: equal chunks of the block space, at least two blocks each, so the space
+    // never needs more than half its blocks in chunks
     p.split_rt = p.tiles_per_head;
+    p.split_waves = split_chunk_waves(p.tiles_per_head, head_dim, fp8_kv);
     const long long lanes_max = ((long long)batch * num_kv_heads * maxblk + 1) / 2;
-    long long wgs = (lanes_max + kWaves - 1) / kWaves;
+    const long long per_wg = kWaves / p.split_waves;
+    long long wgs = (lanes_max + per_wg - 1) / per_wg;
     if (wgs > kMaxSplitWorkgroups) wgs = kMaxSplitWorkgroups;
     p.split_wgs = wgs < 1 ? 1 : wgs;
     p.num_parts = 1;
@@ -327,7 +334,7 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, int q_dtype, int kv_
 // Enqueues multi_kernel and, with more than one partition, the merge.
 hipError_t launch_multi(const MultiArgs& a, int head_dim, int q_dtype, int kv_dtype,
                         hipStream_t stream);
-// Enqueues multi_split_kernel (a.split_rt row tiles per head, a.total_lanes chunks = waves).
+// Enqueues multi_split_kernel (a.split_rt row tiles per head, a.total_lanes chunks).
 hipError_t launch_multi_split(const MultiArgs& a, int head_dim, int q_dtype, int kv_dtype,
                               hipStream_t stream);
 // Resident multi_split_kernel workgroups per CU for this instance (0 if the query fails).

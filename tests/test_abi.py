@@ -200,9 +200,9 @@ def _mdesc(**kw):
 
 def test_multi_workspace_size():
     """Every layout starts with the 256 KiB of arrival counters.  Balanced split (automatic; one
-    row tile per head, or two with an fp8 cache or head_dim 64): then two parts per (workgroup,
-    row tile, column), an fp32 output row plus max and exp-sum, for one workgroup per 8 two-block
-    chunks of the largest flattened block space, at most 512 workgroups.  Fixed partitions: per
+    or two row tiles per head): then two parts per (workgroup, row tile, column), an fp32 output
+    row plus max and exp-sum, for one workgroup per 8 two-block chunks of the largest flattened
+    block space (4 with two waves per chunk), at most 512 workgroups.  Fixed partitions: per
     (row, head, partition) an output row plus max and exp-sum.  The chunk kernel with one
     partition needs none."""
     C = _r(65536 * 4)
@@ -214,11 +214,12 @@ def test_multi_workspace_size():
     size = pa.pa_decode_multi_workspace_size
     # 4 x 2 heads x 8 blocks = 64 blocks -> 32 chunks -> 4 workgroups; 16 rows: one tile
     assert size(_mdesc()) == split(4, 1)
-    # 32 rows: two tiles with head_dim 64 or an fp8 cache; 16-bit at head_dim 128: chunk kernel
+    # 32 rows: two tiles, in one wave with head_dim 64 or an fp8 cache, else in two waves per
+    # chunk (4 chunks a workgroup)
     assert size(_mdesc(max_query_len=8)) == split(4, 2)
     assert size(_mdesc(max_query_len=8, head_dim=128, kv_dtype=pa.PA_FP8_E4M3)) == \
         split(4, 2, 128)
-    assert size(_mdesc(max_query_len=8, head_dim=128)) == 0
+    assert size(_mdesc(max_query_len=8, head_dim=128)) == split(8, 2, 128)
     # a large space is capped at 512 workgroups
     assert size(_mdesc(batch=64, max_blocks_per_seq=512, head_dim=128)) == split(512, 1, 128)
     # more than 32 rows: the chunk kernel, here with one partition and no workspace

@@ -129,6 +129,8 @@ SPLIT = [
     ("bf16", "fp8_e4m3", 2, 8, 128, 4),      # two full tiles over fp8 codes
     ("f16", "fp8_e4m3", 2, 4, 128, 8),
     ("bf16", "bf16", 2, 8, 128, 2),          # one tile of 16-bit K/V
+    ("bf16", "bf16", 2, 8, 128, 4),          # two 16-bit tiles at head_dim 128: two waves a chunk
+    ("f16", "f16", 2, 3, 128, 8),            # the same with a partial second tile
     ("f16", "f16", 4, 1, 128, 8),            # one tile, several tokens in it
     ("f16", "f16", 2, 16, 64, 2),            # two tiles at head_dim 64
     ("bf16", "bf16", 2, 3, 64, 8),           # a partial second tile
@@ -202,7 +204,7 @@ def test_full_size_fp8_verification():
     _sampled(m, 2, rng)
 
 
-@pytest.mark.parametrize("kvd,T", [("fp8_e4m3", 4), ("bf16", 2)])
+@pytest.mark.parametrize("kvd,T", [("fp8_e4m3", 4), ("bf16", 2), ("bf16", 4)])
 def test_one_head_over_many_workgroups(kvd, T):
     """One KV head of 65536 tokens: two-block chunks, so its parts come from hundreds of
     workgroups and are merged in LDS-staged batches (sampled rows)."""
