@@ -175,10 +175,11 @@ constexpr long kMultiTargetWaves = 4096;   // waves the automatic partition aims
 constexpr long kChunkTargetWaves = 2048;
 constexpr int kMultiMinPartBlocks = 16;    // automatic partitions are at least 256 tokens
 
-// Heads with more than one MFMA tile of query rows go to chunk_kernel: a workgroup takes a block
-// of rows of one head and stages each K/V step once in LDS for all of them.  Two shapes:
-// kChunkWide (4 waves x 2 tiles = 128 rows, prefill chunks) and kChunkNarrow (2 waves x 1 tile
-// = 32 rows, a few tokens per sequence such as speculative verification).
+// Heads with more query rows than multi_split_kernel takes (more than two MFMA tiles) go to
+// chunk_kernel: a workgroup takes a block of rows of one head and stages each K/V step once in
+// LDS for all of them.  Two shapes: kChunkWide (4 waves x 2 tiles = 128 rows, prefill chunks)
+// and kChunkNarrow (2 waves x 1 tile = 32 rows, for 33..64 rows, e.g. 8 draft tokens of a group
+// of 8).
 struct ChunkShape {
   int waves, tiles;            // waves per workgroup, 16-column tiles per wave
 };
@@ -255,7 +256,7 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
     p.items = 0;
     return p;
   }
-  if (partition_tokens == 0 && rows > 16) {
+  if (partition_tokens == 0 && rows > 16) {   // (with split taken above: rows > 32)
     const ChunkShape c = rows > 64 ? kChunkWide : kChunkNarrow;
     const int block_rows = 16 * c.waves * c.tiles;
     p.chunk_wide = rows > 64 ? 1 : 0;
