@@ -31,6 +31,12 @@ struct VAppend {
   int off = 0;                     // its slot in the block
 };
 
+// Pacing hook of the walk, called with a step's first logical block before its loads are
+// issued (the default does nothing).
+struct NoPace {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 template <typename V8>
 __device__ __forceinline__ V8 zero_vec8() {
   return __builtin_bit_cast(V8, make_uint4(0u, 0u, 0u, 0u));
@@ -183,21 +189,22 @@ struct Stepper {
   // Several column tiles per wave: tile u's columns take qB[u] and their windows end_lane[u];
   // every K/V step is loaded once and multiplied into all MT tiles.  end_lo and end_v bound the
   // windows of all tiles.
-  template <int MT>
+  template <int MT, class Pace = NoPace>
   __device__ __forceinline__ void walk_tiles(const V8 (&qB)[MT][NC], const int32_t* trow,
                                              int kvh, int j0, int j1, const int (&end_lane)[MT],
                                              int end_lo, int end_v, float (&m_run)[MT],
-                                             float (&l_run)[MT], f32x4 (&acc)[MT][NT]) const {
+                                             float (&l_run)[MT], f32x4 (&acc)[MT][NT],
+                                             Pace pace = Pace()) const {
     walk<false, MT>(qB, trow, kvh, j0, j1, end_lane, end_lo, end_v, 0, 1, m_run, l_run, acc,
-                    false, VAppend());
+                    false, VAppend(), pace);
   }
 
-  template <bool APP, int MT>
+  template <bool APP, int MT, class Pace = NoPace>
   __device__ __forceinline__ void walk(const V8 (&qB)[MT][NC], const int32_t* trow, int kvh,
                                        int j0, int j1, const int (&end_tok)[MT], int end_lo,
                                        int end_v, int s_first, int stride, float (&m_run)[MT],
                                        float (&l_run)[MT], f32x4 (&acc)[MT][NT],
-                                       bool wait_stores, VAppend ap) const {
+                                       bool wait_stores, VAppend ap, Pace pace = Pace()) const {
     static_assert(!APP || MT == 1, "the append instance takes one tile");
     const int nsteps = (j1 - j0 + 1) >> 1;
     if (s_first >= nsteps) return;
@@ -232,6 +239,7 @@ struct Stepper {
     }
 
     auto issue = [&](StepRegs<D, FP8>& r, int s) {
+      pace(j0 + 2 * min(s, nsteps - 1));
       const int pb0 = nid0, pb1 = nid1;
       if constexpr (APP) {
         r.pb0 = pb0;
