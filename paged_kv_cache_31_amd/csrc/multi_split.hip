@@ -491,7 +491,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
     return r;
   };
 
-  // swap: the parked first piece into registers, the last piece into the slot
+  // swap: the parked first piece into registers, the last piece into the slot (a wave's own
+  // slot only, and one wave's LDS accesses stay in order, so no barrier between the two)
   const bool has_first = sm_meta[wave][0].b >= 0;
   float fm[MT], fl[MT];
   f32x4 facc[MT][NT];
@@ -504,7 +505,6 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
       for (int t = 0; t < NT; ++t) facc[u][t] = sm_pacc[wave][u][t][lane];
     }
   }
-  __syncthreads();
   if (keep) {
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
