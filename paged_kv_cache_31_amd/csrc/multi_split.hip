@@ -324,7 +324,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
     }
   }
   if (tid < 2 * kWaves) sm_meta[tid >> 1][tid & 1].b = -1;
-  if (tid < kWaves) sm_post[tid] = INT_MIN / 2;     // below every position: nobody waits yet
+  if (tid < kWaves) sm_post[tid] = INT_MIN / 2;     // not started: wait for a partner's first post
   __syncthreads();
 
   // ---- 2. This wave's chunk, piece by piece, all row tiles of a head at once.  A chunk's
