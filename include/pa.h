@@ -88,13 +88,19 @@ typedef struct pa_decode_desc {
                                  0 = chunks of equal length balanced over the GPU's resident
                                  waves (the default, best for ragged batches) */
   int32_t q_dtype;            /* PA_F16 or PA_BF16; the output has the same dtype */
-  int32_t shared_prefixes;    /* 0 or 1.  1: sequences whose block tables start with the same
+  int32_t shared_prefixes;    /* 0, 1 or 2.  1: sequences whose block tables start with the same
                                  physical blocks (a prefix cache shares blocks this way: youngju.dev
                                  LLM inference guide, PagedAttention "主な特性" and its prefix-
                                  caching example; Scaling Book note, "プレフィックスキャッシュ") read
                                  those blocks once per group of up to 16/group sequences instead of
                                  once each.  Taken when group <= 8 and batch <= 1024, else ignored.
-                                 The result is the same attention up to rounding order. */
+                                 The result is the same attention up to rounding order.
+                                 2: the same, reusing the grouping that the last call with 1 left in
+                                 this workspace instead of planning again: for the layers of one
+                                 step, whose calls read the same block_tables and context_lens.  The
+                                 caller guarantees those (and batch, max_blocks_per_seq,
+                                 max_context_len and the head counts) are unchanged since that call;
+                                 the results are then bitwise those of a call with 1. */
 } pa_decode_desc;
 
 typedef struct pa_multi_desc {

@@ -215,9 +215,11 @@ def pa_kv_append_quant(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_
 
 def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_tokens=0,
                 shared_prefixes=False) -> DecodeDesc:
+    # shared_prefixes: False/0 off, True/1 plan the groups, 2 reuse the plan of the last
+    # planning call on the same workspace (unchanged tables and lengths)
     B, Hq, D = q.shape
     return DecodeDesc(cache_desc(k_cache), B, Hq, block_tables.shape[1], int(max_context_len),
-                      int(partition_tokens), _dtype_code(q, False), int(bool(shared_prefixes)))
+                      int(partition_tokens), _dtype_code(q, False), int(shared_prefixes))
 
 
 def pa_decode_workspace_size(desc: DecodeDesc) -> int:
@@ -293,7 +295,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_sca
     """out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b through the block tables; returns out.
 
     shared_prefixes: read blocks that several sequences' tables start with once per group of
-    sequences (see pa_decode_desc.shared_prefixes)."""
+    sequences; 2 reuses the grouping planned by the previous call on this stream's workspace
+    (the layers of one step: unchanged block tables and lengths), see
+    pa_decode_desc.shared_prefixes."""
     DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                max_context_len, partition_tokens, workspace, stream, shared_prefixes)()
     return out

@@ -711,207 +711,239 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
   const int B = a.batch, MB = a.max_blocks_per_seq, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int G = a.group, S = 16 / G;
 
-  // ---- 1. Candidates: two or more whole blocks before the one with the last token, hashed by
-  // their first physical block.  A group's leader is its smallest sequence index.
+  // The plan (phases 1-3) depends only on the lengths and tables; a call that reuses the one a
+  // planning call saved goes straight to the units.
+  int U = 0;
+  if (a.plan_reuse) {
+    U = uniform(a.plan_units[0]);
+  } else {
+    // ---- 1. Candidates: two or more whole blocks before the one with the last token, hashed by
+    // their first physical block.  A group's leader is its smallest sequence index.
 #pragma unroll
-  for (int x = 0; x < SPT; ++x) {
-    h_key[tid * SPT + x] = -1;
-    h_lead[tid * SPT + x] = INT_MAX;
-    h_cnt[tid * SPT + x] = 0;
-    h_p[tid * SPT + x] = INT_MAX;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int b = tid * PER + q;
-    int slot = -1, full = 0;
-    if (b < B) {
-      const int L = clamp_len(a.context_lens[b], a.len_cap);
-      const int key = a.block_tables[(size_t)b * MB];
-      full = L > 0 ? min((L - 1) / kBlock, kMaxSharedBlocks) : 0;
-      if (full >= 2 && (unsigned)key < (unsigned)a.num_blocks) {
-        unsigned h = ((unsigned)key * 2654435761u) >> 21;
-        for (;;) {                                  // ends: fewer keys than slots
-          const int prev = atomicCAS(&h_key[h], -1, key);
-          if (prev == -1 || prev == key) break;
-          h = (h + 1) & (HS - 1);
-        }
-        slot = (int)h;
-        atomicMin(&h_lead[slot], b);
-        atomicAdd(&h_cnt[slot], 1);
-      }
+    for (int x = 0; x < SPT; ++x) {
+      h_key[tid * SPT + x] = -1;
+      h_lead[tid * SPT + x] = INT_MAX;
+      h_cnt[tid * SPT + x] = 0;
+      h_p[tid * SPT + x] = INT_MAX;
     }
-    s_full[b] = full;
-    s_slot[b] = slot;
-  }
-  __syncthreads();
-
-  // ---- 2. Shared length of a group: the first table entry where a member differs from the
-  // leader, at most the shorter of their whole-block counts.  A wave compares 8 members at a
-  // time, 64 consecutive entries of each row per round (one coalesced load per row), and stops
-  // at a member's first difference.
-  int cmpb[PER], csum = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int b = tid * PER + q, slot = s_slot[b];
-    cmpb[q] = 0;
-    if (slot >= 0 && h_cnt[slot] >= 2) {
-      const int lead = h_lead[slot];
-      const int cmp = min(s_full[b], s_full[lead]);
-      atomicMin(&h_p[slot], cmp);
-      if (b != lead && cmp > 1) cmpb[q] = cmp;
-    }
-    csum += cmpb[q] > 0;
-  }
-  int ncmp;
-  {
-    int pos = block_scan<NTH>(csum, s_scan, ncmp);
-#pragma unroll
-    for (int q = 0; q < PER; ++q)
-      if (cmpb[q] > 0) {
-        s_off[pos] = tid * PER + q;                 // members to compare, in sequence order
-        s_mseq[pos] = cmpb[q];                      // and their comparison lengths
-        ++pos;
-      }
-  }
-  __syncthreads();
-  for (int k0 = wave * 8; k0 < ncmp; k0 += kWaves * 8) {
-    int mb[8], len[8], first[8];
-    const int32_t* rm[8];
-    const int32_t* rl[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int k = k0 + v;
-      mb[v] = k < ncmp ? s_off[k] : -1;
-      len[v] = k < ncmp ? s_mseq[k] : 0;
-      first[v] = INT_MAX;
-      const int lead = mb[v] >= 0 ? h_lead[s_slot[mb[v]]] : 0;
-      rm[v] = a.block_tables + (size_t)(mb[v] >= 0 ? mb[v] : 0) * MB;
-      rl[v] = a.block_tables + (size_t)lead * MB;
-    }
-    for (int j0 = 1;; j0 += 64) {
-      const int j = j0 + lane;
-      int x[8], y[8];
-      bool live = false;
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        // unconditional loads (clamped into the row), so that they are all in flight at once
-        const int jc = min(j, max(len[v] - 1, 0));
-        x[v] = rm[v][jc];
-        y[v] = rl[v][jc];
-      }
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const bool act = first[v] == INT_MAX && j0 < len[v];
-        const unsigned long long diff = __ballot(act && j < len[v] && x[v] != y[v]);
-        if (diff) first[v] = j0 + __ffsll((long long)diff) - 1;
-        live |= first[v] == INT_MAX && j0 + 64 < len[v];
-      }
-      if (!live) break;
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int v = 0; v < 8; ++v)
-        if (first[v] != INT_MAX) atomicMin(&h_p[s_slot[mb[v]]], first[v]);
-    }
-  }
-  __syncthreads();
-
-  // ---- 3. Members (of groups of two or more sharing two or more blocks), listed in sequence
-  // order; a member's rank is the number of members of its group before it.
-  int mem[PER], msum = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int slot = s_slot[tid * PER + q];
-    mem[q] = slot >= 0 && h_cnt[slot] >= 2 && h_p[slot] >= 2;
-    msum += mem[q];
-  }
-  int nmem;
-  {
-    int pos = block_scan<NTH>(msum, s_scan, nmem);
-#pragma unroll
-    for (int q = 0; q < PER; ++q)
-      if (mem[q]) {
-        s_mslot[pos] = s_slot[tid * PER + q];
-        s_mseq[pos] = tid * PER + q;
-        ++pos;
-      }
-  }
-  // Groups are numbered in the order of their leaders (hash slots may differ between
-  // workgroups; leaders do not): each group's first member and first unit, by prefix sums over
-  // the sequences.
-  int mc[PER], uc[PER], ms = 0, us = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int b = tid * PER + q, slot = s_slot[b];
-    const bool leader = mem[q] && h_lead[slot] == b;
-    const int cnt = leader ? h_cnt[slot] : 0;
-    mc[q] = cnt;
-    uc[q] = leader ? (cnt + S - 1) / S * Hkv * prefix_parts(h_p[slot]) : 0;
-    ms += mc[q];
-    us += uc[q];
-  }
-  int U;
-  {
-    int mb = block_scan<NTH>(ms, s_scan, nmem);
-    int ub = block_scan<NTH>(us, s_scan, U);
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int b = tid * PER + q;
-      if (mc[q] > 0) {
-        h_mbase[s_slot[b]] = mb;
-        h_key[s_slot[b]] = 0;                       // rank counter of the member list below
+      int slot = -1, full = 0;
+      if (b < B) {
+        const int L = clamp_len(a.context_lens[b], a.len_cap);
+        const int key = a.block_tables[(size_t)b * MB];
+        full = L > 0 ? min((L - 1) / kBlock, kMaxSharedBlocks) : 0;
+        if (full >= 2 && (unsigned)key < (unsigned)a.num_blocks) {
+          unsigned h = ((unsigned)key * 2654435761u) >> 21;
+          for (;;) {                                  // ends: fewer keys than slots
+            const int prev = atomicCAS(&h_key[h], -1, key);
+            if (prev == -1 || prev == key) break;
+            h = (h + 1) & (HS - 1);
+          }
+          slot = (int)h;
+          atomicMin(&h_lead[slot], b);
+          atomicAdd(&h_cnt[slot], 1);
+        }
       }
-      s_ubase[b] = ub;
-      mb += mc[q];
-      ub += uc[q];
+      s_full[b] = full;
+      s_slot[b] = slot;
     }
-  }
-  __syncthreads();
-  // member ranks within their groups: the first wave walks the members in sequence order, 64
-  // at a time, one ballot per distinct group in the round
-  if (wave == 0) {
-    for (int i0 = 0; i0 < nmem; i0 += 64) {
-      const int i = i0 + lane;
-      const int slot = i < nmem ? s_mslot[i] : -1;
-      uint64_t todo = __ballot(slot >= 0);
-      while (todo) {
-        const int sl = __builtin_amdgcn_readlane(slot, __builtin_ctzll(todo));
-        const uint64_t same = __ballot(slot == sl);
-        const int base = h_key[sl];
-        if (slot == sl) s_mlist[h_mbase[sl] + base + __popcll(same & ((1ull << lane) - 1ull))] =
-            s_mseq[i];
-        if (lane == 0) h_key[sl] = base + __popcll(same);
-        todo &= ~same;
-      }
-    }
-  }
-  if (blockIdx.x == 0) {                            // shared blocks each sequence skips
+    __syncthreads();
+
+    // ---- 2. Shared length of a group: the first table entry where a member differs from the
+    // leader, at most the shorter of their whole-block counts.  A wave compares 8 members at a
+    // time, 64 consecutive entries of each row per round (one coalesced load per row), and stops
+    // at a member's first difference.
+    int cmpb[PER], csum = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int b = tid * PER + q, slot = s_slot[b];
-      if (b < B) a.ws_skip[b] = mem[q] ? h_p[slot] : 0;
+      cmpb[q] = 0;
+      if (slot >= 0 && h_cnt[slot] >= 2) {
+        const int lead = h_lead[slot];
+        const int cmp = min(s_full[b], s_full[lead]);
+        atomicMin(&h_p[slot], cmp);
+        if (b != lead && cmp > 1) cmpb[q] = cmp;
+      }
+      csum += cmpb[q] > 0;
     }
+    int ncmp;
+    {
+      int pos = block_scan<NTH>(csum, s_scan, ncmp);
+#pragma unroll
+      for (int q = 0; q < PER; ++q)
+        if (cmpb[q] > 0) {
+          s_off[pos] = tid * PER + q;                 // members to compare, in sequence order
+          s_mseq[pos] = cmpb[q];                      // and their comparison lengths
+          ++pos;
+        }
+    }
+    __syncthreads();
+    for (int k0 = wave * 8; k0 < ncmp; k0 += kWaves * 8) {
+      int mb[8], len[8], first[8];
+      const int32_t* rm[8];
+      const int32_t* rl[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int k = k0 + v;
+        mb[v] = k < ncmp ? s_off[k] : -1;
+        len[v] = k < ncmp ? s_mseq[k] : 0;
+        first[v] = INT_MAX;
+        const int lead = mb[v] >= 0 ? h_lead[s_slot[mb[v]]] : 0;
+        rm[v] = a.block_tables + (size_t)(mb[v] >= 0 ? mb[v] : 0) * MB;
+        rl[v] = a.block_tables + (size_t)lead * MB;
+      }
+      for (int j0 = 1;; j0 += 64) {
+        const int j = j0 + lane;
+        int x[8], y[8];
+        bool live = false;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          // unconditional loads (clamped into the row), so that they are all in flight at once
+          const int jc = min(j, max(len[v] - 1, 0));
+          x[v] = rm[v][jc];
+          y[v] = rl[v][jc];
+        }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const bool act = first[v] == INT_MAX && j0 < len[v];
+          const unsigned long long diff = __ballot(act && j < len[v] && x[v] != y[v]);
+          if (diff) first[v] = j0 + __ffsll((long long)diff) - 1;
+          live |= first[v] == INT_MAX && j0 + 64 < len[v];
+        }
+        if (!live) break;
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          if (first[v] != INT_MAX) atomicMin(&h_p[s_slot[mb[v]]], first[v]);
+      }
+    }
+    __syncthreads();
+
+    // ---- 3. Members (of groups of two or more sharing two or more blocks), listed in sequence
+    // order; a member's rank is the number of members of its group before it.
+    int mem[PER], msum = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int slot = s_slot[tid * PER + q];
+      mem[q] = slot >= 0 && h_cnt[slot] >= 2 && h_p[slot] >= 2;
+      msum += mem[q];
+    }
+    int nmem;
+    {
+      int pos = block_scan<NTH>(msum, s_scan, nmem);
+#pragma unroll
+      for (int q = 0; q < PER; ++q)
+        if (mem[q]) {
+          s_mslot[pos] = s_slot[tid * PER + q];
+          s_mseq[pos] = tid * PER + q;
+          ++pos;
+        }
+    }
+    // Groups are numbered in the order of their leaders (hash slots may differ between
+    // workgroups; leaders do not): each group's first member and first unit, by prefix sums over
+    // the sequences.
+    int mc[PER], uc[PER], ms = 0, us = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int b = tid * PER + q, slot = s_slot[b];
+      const bool leader = mem[q] && h_lead[slot] == b;
+      const int cnt = leader ? h_cnt[slot] : 0;
+      mc[q] = cnt;
+      uc[q] = leader ? (cnt + S - 1) / S * Hkv * prefix_parts(h_p[slot]) : 0;
+      ms += mc[q];
+      us += uc[q];
+    }
+    {
+      int mb = block_scan<NTH>(ms, s_scan, nmem);
+      int ub = block_scan<NTH>(us, s_scan, U);
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int b = tid * PER + q;
+        if (mc[q] > 0) {
+          h_mbase[s_slot[b]] = mb;
+          h_key[s_slot[b]] = 0;                       // rank counter of the member list below
+        }
+        s_ubase[b] = ub;
+        mb += mc[q];
+        ub += uc[q];
+      }
+    }
+    __syncthreads();
+    // member ranks within their groups: the first wave walks the members in sequence order, 64
+    // at a time, one ballot per distinct group in the round
+    if (wave == 0) {
+      for (int i0 = 0; i0 < nmem; i0 += 64) {
+        const int i = i0 + lane;
+        const int slot = i < nmem ? s_mslot[i] : -1;
+        uint64_t todo = __ballot(slot >= 0);
+        while (todo) {
+          const int sl = __builtin_amdgcn_readlane(slot, __builtin_ctzll(todo));
+          const uint64_t same = __ballot(slot == sl);
+          const int base = h_key[sl];
+          if (slot == sl) s_mlist[h_mbase[sl] + base + __popcll(same & ((1ull << lane) - 1ull))] =
+              s_mseq[i];
+          if (lane == 0) h_key[sl] = base + __popcll(same);
+          todo &= ~same;
+        }
+      }
+    }
+    if (blockIdx.x == 0) {                            // shared blocks each sequence skips
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int b = tid * PER + q, slot = s_slot[b];
+        if (b < B) a.ws_skip[b] = mem[q] ? h_p[slot] : 0;
+      }
+      if (tid == 0) a.plan_units[0] = U;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- 4. The units.
   const St st(a, lane);
   const int r = col / G, g = col - r * G;
   for (int u = blockIdx.x; u < U; u += gridDim.x) {
-    int lo = 0, hi = kPlanMaxBatch - 1;             // the leader whose group's units contain u
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_ubase[mid] <= u) lo = mid; else hi = mid - 1;
+    int* rec = a.plan_units + kUnitHead + (size_t)u * kUnitRec;
+    int lead, kvh, k, j0, j1, member;
+    if (a.plan_reuse) {
+      lead = uniform(rec[0]);
+      j0 = uniform(rec[1]);
+      j1 = uniform(rec[2]);
+      kvh = uniform(rec[3]);
+      k = uniform(rec[4]);
+      member = r < S ? rec[kUnitMembers + r] : -1;
+    } else {
+      int lo = 0, hi = kPlanMaxBatch - 1;           // the leader whose group's units contain u
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_ubase[mid] <= u) lo = mid; else hi = mid - 1;
+      }
+      const int s = s_slot[lo], p = h_p[s], cnt = h_cnt[s];
+      const int ks = prefix_parts(p);
+      const int uu = u - s_ubase[lo];
+      const int tile = uu / (Hkv * ks), rem = uu - tile * (Hkv * ks);
+      lead = lo;
+      kvh = rem / ks;
+      k = rem - kvh * ks;
+      j0 = k * kUnitBlocks;
+      j1 = min(p, j0 + kUnitBlocks);
+      const int mi = tile * S + r;                  // this column's member within the group
+      member = r < S && mi < cnt ? s_mlist[h_mbase[s] + mi] : -1;
+      if (wave == 0 && lane < 16) {                 // save the unit for calls that reuse the plan
+        const int ml = tile * S + lane;
+        rec[kUnitMembers + lane] = lane < S && ml < cnt ? s_mlist[h_mbase[s] + ml] : -1;
+        if (lane == 0) {
+          rec[0] = lead;
+          rec[1] = j0;
+          rec[2] = j1;
+          rec[3] = kvh;
+          rec[4] = k;
+        }
+      }
     }
-    const int s = s_slot[lo], p = h_p[s], lead = lo, cnt = h_cnt[s];
-    const int ks = prefix_parts(p);
-    const int uu = u - s_ubase[lo];
-    const int tile = uu / (Hkv * ks), rem = uu - tile * (Hkv * ks);
-    const int kvh = rem / ks, k = rem - kvh * ks;
-    const int j0 = k * kUnitBlocks, j1 = min(p, j0 + kUnitBlocks);
-    const int mi = tile * S + r;                    // this column's member within the group
-    const int member = r < S && mi < cnt ? s_mlist[h_mbase[s] + mi] : -1;
     const size_t row = (size_t)member * Hq + kvh * G + g;
 
     V8 qB[NC];

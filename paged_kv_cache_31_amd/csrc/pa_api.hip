@@ -53,7 +53,7 @@ pa_status check_decode_desc(const pa_decode_desc* d) {
     return PA_ERR_INVALID_ARG;
   if (blocks_upper(d) >= INT32_MAX) return PA_ERR_UNSUPPORTED;   // flattened index is 32-bit
   if (chunk_capacity(d) > pa::kMaxWorkgroups * pa::kWaves) return PA_ERR_UNSUPPORTED;
-  if (d->shared_prefixes != 0 && d->shared_prefixes != 1) return PA_ERR_INVALID_ARG;
+  if (d->shared_prefixes < 0 || d->shared_prefixes > 2) return PA_ERR_INVALID_ARG;
   if (d->q_dtype != PA_F16 && d->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   const int kv = d->cache.kv_dtype;
   if (kv != PA_FP8_E4M3 && kv != d->q_dtype) return PA_ERR_UNSUPPORTED;
@@ -130,7 +130,7 @@ int64_t chunk_capacity(const pa_decode_desc* d) {
 // Shared prefixes are planned when asked for, when a tile holds at least two members
 // (group <= 8) and when the batch fits one planning workgroup.
 bool sharing_active(const pa_decode_desc* d) {
-  return d->shared_prefixes == 1 && d->num_q_heads / d->cache.num_kv_heads <= 8 &&
+  return d->shared_prefixes != 0 && d->num_q_heads / d->cache.num_kv_heads <= 8 &&
          d->batch <= pa::kPlanMaxBatch;
 }
 
@@ -456,6 +456,8 @@ pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_n
   a.gp_acc = share ? reinterpret_cast<float*>(ws + lay.gp_acc) : nullptr;
   a.gp_ml = share ? reinterpret_cast<float*>(ws + lay.gp_ml) : nullptr;
   a.prefix_parts = share ? pa::prefix_parts_of(desc->max_blocks_per_seq) : 0;
+  a.plan_units = share ? reinterpret_cast<int*>(ws + lay.units) : nullptr;
+  a.plan_reuse = share && desc->shared_prefixes == 2 ? 1 : 0;
   a.batch = desc->batch;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->cache.num_kv_heads;

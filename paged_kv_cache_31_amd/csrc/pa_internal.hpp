@@ -73,6 +73,10 @@ struct DecodeArgs {
   float* gp_acc;        // [batch * num_q_heads][prefix_parts][head_dim]: unnormalised output
   float* gp_ml;         // [batch * num_q_heads][prefix_parts][2]: running max (log2), exp-sum
   int prefix_parts;     // partial results per query row: ceil(min(table width, 256) / 16)
+  // The plan's units, saved by a planning call for calls that reuse it (the layers of one step
+  // read the same tables): [0] the unit count, then kUnitRec ints per unit from kUnitHead on.
+  int* plan_units;
+  int plan_reuse;       // 1: take the saved units instead of planning (and keep ws_skip)
   int batch;
   int num_q_heads;
   int num_kv_heads;
@@ -96,6 +100,11 @@ constexpr int kMaxSharedBlocks = 256; // longest shared prefix taken (blocks)
 // Groups have at least two members and tiles at least two columns of members, so a batch of n
 // sequences makes at most floor(2n/3) tiles (groups of three, two tiles each, are the worst case).
 inline int plan_tiles_of(int batch) { return 2 * batch / 3 > 0 ? 2 * batch / 3 : 1; }
+// A saved unit: lead sequence, shared blocks [j0, j1), KV head, part index, then the member
+// sequence of each of the 16 tile slots (-1: none).
+constexpr int kUnitRec = 24;
+constexpr int kUnitMembers = 8;       // offset of the member slots in a record
+constexpr int kUnitHead = 64;         // ints before the first record (the count, padding)
 inline int prefix_parts_of(int max_blocks_per_seq) {
   const int m = max_blocks_per_seq < kMaxSharedBlocks ? max_blocks_per_seq : kMaxSharedBlocks;
   return (m + kUnitBlocks - 1) / kUnitBlocks;
@@ -103,11 +112,11 @@ inline int prefix_parts_of(int max_blocks_per_seq) {
 
 // Workspace: a fixed region of arrival counters (so that their place never depends on the
 // descriptor and a workspace zero-filled once stays valid for every call), then two published
-// partial results per workgroup; with shared prefixes, each sequence's skipped block count and
-// the prefix partial results follow.  Each part is 256-byte aligned.
+// partial results per workgroup; with shared prefixes, each sequence's skipped block count, the
+// prefix partial results and the saved units follow.  Each part is 256-byte aligned.
 constexpr long kMaxWorkgroups = 65536;
 struct WorkspaceLayout {
-  size_t acc, ml, plan, gp_acc, gp_ml, total;
+  size_t acc, ml, plan, gp_acc, gp_ml, units, total;
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline WorkspaceLayout workspace_layout(int group, int head_dim, long workgroups, int batch = 0,
@@ -116,12 +125,14 @@ inline WorkspaceLayout workspace_layout(int group, int head_dim, long workgroups
   w.acc = align256((size_t)kMaxWorkgroups * sizeof(int));
   w.ml = w.acc + align256((size_t)workgroups * 2 * group * head_dim * sizeof(float));
   w.plan = w.ml + align256((size_t)workgroups * 2 * group * 2 * sizeof(float));
-  w.gp_acc = w.gp_ml = w.total = w.plan;
+  w.gp_acc = w.gp_ml = w.units = w.total = w.plan;
   if (prefix_parts > 0) {
     const size_t rows = (size_t)batch * num_q_heads * prefix_parts;
+    const size_t units = (size_t)plan_tiles_of(batch) * (num_q_heads / group) * prefix_parts;
     w.gp_acc = w.plan + align256((size_t)batch * sizeof(int));
     w.gp_ml = w.gp_acc + align256(rows * head_dim * sizeof(float));
-    w.total = w.gp_ml + align256(rows * 2 * sizeof(float));
+    w.units = w.gp_ml + align256(rows * 2 * sizeof(float));
+    w.total = w.units + align256((kUnitHead + units * kUnitRec) * sizeof(int));
   }
   return w;
 }

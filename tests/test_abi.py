@@ -65,7 +65,8 @@ def _decode(desc, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, tab=FAKE, lens=FAKE,
     (dict(q_dtype=pa.PA_FP8_E4M3), pa.PA_ERR_UNSUPPORTED),
     (dict(kv_dtype=pa.PA_F16), pa.PA_ERR_UNSUPPORTED),     # bf16 q with f16 cache
     (dict(kv_dtype=7), pa.PA_ERR_INVALID_ARG),
-    (dict(shared_prefixes=2), pa.PA_ERR_INVALID_ARG),
+    (dict(shared_prefixes=3), pa.PA_ERR_INVALID_ARG),
+    (dict(shared_prefixes=-1), pa.PA_ERR_INVALID_ARG),
 ])
 def test_decode_rejects_descriptor(kw, status):
     d = _desc(**kw)
@@ -132,16 +133,21 @@ def test_append_rejects():
 
 
 def test_workspace_with_shared_prefixes():
-    """Shared prefixes add per-sequence skip counts and the prefix partial results when they are
-    taken (group <= 8, batch <= 1024) and nothing otherwise."""
+    """Shared prefixes add per-sequence skip counts, the prefix partial results and the saved
+    units of the plan (a 64-int head, then 24 ints for each of at most floor(2B/3) tiles x Hkv x
+    parts units) when they are taken (group <= 8, batch <= 1024), the same whether the call plans
+    (1) or reuses the plan (2), and nothing otherwise."""
     d = _desc(max_context_len=100)
     base = pa.pa_decode_workspace_size(d)
     s = _desc(max_context_len=100, shared_prefixes=1)
-    B, Hq, D, MB = 4, 8, 64, 7
+    B, Hq, Hkv, D, MB = 4, 8, 2, 64, 7
     P = -(-min(MB, 256) // 32)
     plan = _r(B * 4)
     parts = _r(B * Hq * P * D * 4) + _r(B * Hq * P * 2 * 4)
-    assert pa.pa_decode_workspace_size(s) == base + plan + parts
+    units = _r((64 + (2 * B // 3) * Hkv * P * 24) * 4)
+    assert pa.pa_decode_workspace_size(s) == base + plan + parts + units
+    assert pa.pa_decode_workspace_size(_desc(max_context_len=100, shared_prefixes=2)) == \
+        pa.pa_decode_workspace_size(s)
     # group 16 and batches over 1024 run without a plan
     g16 = dict(num_kv_heads=1, num_q_heads=16)
     assert (pa.pa_decode_workspace_size(_desc(shared_prefixes=1, **g16))

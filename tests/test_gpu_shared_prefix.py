@@ -137,3 +137,30 @@ def test_plan_not_taken_is_the_unshared_path(g, batch):
     on = _run(wl, k, v, t, f"g{g} b{batch} on", share=True)
     off = _run(wl, k, v, t, f"g{g} b{batch} off", share=False)
     assert np.array_equal(on, off)
+
+
+@pytest.mark.parametrize("kvd", ["bf16", "fp8_e4m3"])
+def test_layers_reuse_the_plan(kvd):
+    """The layers of one step read the same tables and lengths: the first call plans the groups
+    (shared_prefixes 1), the next ones reuse its saved units (2) with their own queries and K/V
+    (another layer's cache), and give bitwise what a planning call gives."""
+    import copy
+    wl0, k0, v0 = _setup("bf16", kvd, 2, 4, 128, LENS, seed=76)
+    # another layer over the same blocks: other queries, K with its sign bits flipped, V
+    # reversed along the head dimension (unused, poisoned blocks stay poisoned)
+    wl1 = copy.copy(wl0)
+    wl1.q = _setup("bf16", kvd, 2, 4, 128, LENS, seed=77)[0].q
+    sign = np.uint8(0x80) if kvd == "fp8_e4m3" else np.uint16(0x8000)
+    k1 = k0 ^ sign
+    v1 = np.ascontiguousarray(v0[:, :, ::-1, :])
+    t = wl0.block_tables.copy()
+    _share(t, 1, (2, 3, 5, 8, 11, 14), 40)
+    t[11, 33:40] = t[9, 33:40]
+    _share(t, 9, (10,), 40)
+    _share(t, 6, (7,), 3)
+    first = _run(wl0, k0, v0, t, f"layer 0 plans ({kvd})", share=1)
+    reused = _run(wl1, k1, v1, t, f"layer 1 reuses ({kvd})", share=2)
+    again = _run(wl0, k0, v0, t, f"layer 0 reuses ({kvd})", share=2)
+    assert np.array_equal(again, first)
+    planned = _run(wl1, k1, v1, t, f"layer 1 plans ({kvd})", share=1)
+    assert np.array_equal(reused, planned)
