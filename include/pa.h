@@ -98,9 +98,13 @@ typedef struct pa_decode_desc {
                                  2: the same, reusing the grouping that the last call with 1 left in
                                  this workspace instead of planning again: for the layers of one
                                  step, whose calls read the same block_tables and context_lens.  The
-                                 caller guarantees those (and batch, max_blocks_per_seq,
-                                 max_context_len and the head counts) are unchanged since that call;
-                                 the results are then bitwise those of a call with 1. */
+                                 caller guarantees those (and the whole descriptor apart from this
+                                 field) are unchanged since that call, and that the workspace saw
+                                 only such calls in between (another descriptor's or
+                                 pa_decode_multi's scratch may overlap the saved grouping); the
+                                 results are then bitwise those of a call with 1.  On a workspace
+                                 no planning call has written (all zero), 2 reads no shared
+                                 blocks and gives the unshared results. */
 } pa_decode_desc;
 
 typedef struct pa_multi_desc {

@@ -295,9 +295,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_sca
     """out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b through the block tables; returns out.
 
     shared_prefixes: read blocks that several sequences' tables start with once per group of
-    sequences; 2 reuses the grouping planned by the previous call on this stream's workspace
-    (the layers of one step: unchanged block tables and lengths), see
-    pa_decode_desc.shared_prefixes."""
+    sequences; 2 reuses the grouping planned by the previous call on the same workspace (the
+    layers of one step: unchanged block tables, lengths and descriptor, and no other kind of
+    call on that workspace in between), see pa_decode_desc.shared_prefixes."""
     DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                max_context_len, partition_tokens, workspace, stream, shared_prefixes)()
     return out
