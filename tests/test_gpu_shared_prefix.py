@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import Dev, assert_close, dev_bits
+from gpu_util import Dev, assert_close, dev_bits, host_bits
 from workloads.generate import Spec
 
 pytestmark = pytest.mark.gpu
@@ -164,3 +164,23 @@ def test_layers_reuse_the_plan(kvd):
     assert np.array_equal(again, first)
     planned = _run(wl1, k1, v1, t, f"layer 1 plans ({kvd})", share=1)
     assert np.array_equal(reused, planned)
+
+
+def test_reuse_on_a_fresh_workspace_is_the_unshared_path():
+    """shared_prefixes 2 on a zero-filled workspace that no planning call has written reads no
+    shared blocks: bitwise the output with shared prefixes off."""
+    import paged_kv_cache_31_amd as pa
+    wl, k, v = _setup("bf16", "bf16", 2, 4, 128, LENS, seed=78)
+    t = wl.block_tables.copy()
+    _share(t, 1, (2, 3, 5, 8, 11, 14), 40)
+    off = _run(wl, k, v, t, "off", share=False)
+    s = wl.spec
+    dev = Dev(wl)
+    dev.k_cache, dev.v_cache = dev_bits(k, s.kv_dtype), dev_bits(v, s.kv_dtype)
+    dev.tables = torch.from_numpy(np.ascontiguousarray(t)).cuda()
+    desc = pa.decode_desc(dev.q, dev.k_cache, dev.tables, 0, 0, 2)
+    ws = pa.new_workspace(pa.pa_decode_workspace_size(desc), dev.q.device)
+    pa.pa_decode(dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens, float(wl.scale), dev.out,
+                 workspace=ws, shared_prefixes=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dev.out), off)
