@@ -239,3 +239,29 @@ def test_one_workspace_serves_every_entry_point():
                 assert_close(host_bits(out), ref[last], s.q_dtype, f"decode after {order}")
             else:
                 m.check(m.run(partition_tokens=step), f"multi P{step} in {order}", ref)
+
+
+RANDOM = [
+    # (seed, q dtype, kv dtype, kv heads, group, head_dim, batch, longest context, most drafts)
+    (200, "bf16", "bf16", 2, 8, 128, 40, 3000, 2),
+    (201, "f16", "fp8_e4m3", 1, 4, 128, 60, 2500, 8),
+    (202, "bf16", "bf16", 3, 2, 64, 90, 1200, 8),
+    (203, "f16", "f16", 2, 1, 128, 30, 4000, 16),
+    (204, "bf16", "fp8_e4m3", 2, 16, 64, 25, 2000, 2),
+    (205, "bf16", "bf16", 1, 8, 128, 700, 120, 4),     # several sequences per scanning thread
+]
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=lambda c: f"seed{c[0]}")
+def test_random_split_batches(case):
+    """Random batches for the balanced split: lengths from 0 (no cached token) to the bound,
+    draft counts from 0 (no rows) to the bound, so heads of one or two tiles, empty sequences
+    and rows before the context all occur in one call."""
+    seed, qd, kvd, hkv, g, d, B, lmax, tmax = case
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, lmax + 1, size=B)
+    lens[rng.random(B) < 0.1] = 0
+    T = rng.integers(0, tmax + 1, size=B)
+    m = Multi(qd, kvd, hkv, g, d, [int(x) for x in lens], [int(x) for x in T], seed=seed,
+              spare_rows=2)
+    m.check(m.run(), f"random {case}")
