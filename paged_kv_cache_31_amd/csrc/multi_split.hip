@@ -246,7 +246,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   constexpr int NTH = 64 * kWaves;
   constexpr int KW = kWaves / RT;                   // chunks per workgroup
   constexpr int TT = MT * RT;                       // row tiles per head
-  static_assert(kWaves % RT == 0, "waves per chunk");
+  static_assert(RT == 1 || RT == 2, "waves per chunk");
 
   __shared__ int sm_wave_sum[kWaves];
   __shared__ int sm_start_b[KW], sm_start_off[KW];
@@ -660,7 +660,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
 }
 
 // The instances: one tile per head (MT 1, RT 1); two tiles in one wave where its registers hold
-// them (fp8 or head_dim 64: MT 2); else two waves per chunk (RT 2).
+// them (fp8 or head_dim 64: MT 2), else two waves per chunk (RT 2); four tiles (three laid out as
+// four) only where one wave holds two, in two waves per chunk (MT 2, RT 2).
 template <int D, int KVT>
 constexpr bool kTwoTilesOneWave = D == 64 || KVT == DT_FP8;
 
@@ -677,6 +678,12 @@ static hipError_t launch_split_t(const MultiArgs& a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 1, 2>),
                          dim3((unsigned)(a.total_lanes / (kWaves / 2))), block, 0, stream, a);
+  } else if (a.split_rt == 4) {
+    if constexpr (kTwoTilesOneWave<D, KVT>)
+      hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 2, 2>),
+                         dim3((unsigned)(a.total_lanes / (kWaves / 2))), block, 0, stream, a);
+    else
+      return hipErrorInvalidValue;                  // the plan gives these heads to chunk_kernel
   } else {
     return hipErrorInvalidValue;
   }
@@ -696,6 +703,10 @@ static int split_occupancy_t(int rt) {
                                                        64 * kWaves, 0);
     else
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 1, 2>,
+                                                       64 * kWaves, 0);
+  } else if (rt == 4) {
+    if constexpr (kTwoTilesOneWave<D, KVT>)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 2, 2>,
                                                        64 * kWaves, 0);
   }
   return e == hipSuccess ? n : 0;

@@ -207,14 +207,23 @@ struct MultiPlan {
   long long split_wgs;         // multi_split_kernel: most workgroups a launch may use
 };
 
-// multi_split_kernel takes heads of one or two row tiles.  Two tiles go to one wave where its
-// registers hold both tiles' accumulators and query operands next to the K/V steps in flight
-// (fp8 caches or head_dim 64); two tiles of 16-bit K/V at head_dim 128 would spill there and
-// take two waves per chunk instead.  A launch is one workgroup per resident slot, at most
-// kMaxSplitWorkgroups (a workspace bound known without a GPU: twice the 256 CUs of an MI355X).
-constexpr int kSplitMaxTiles = 2;
+// multi_split_kernel takes heads of up to two row tiles per wave of a pair.  Two tiles go to one
+// wave where its registers hold both tiles' accumulators and query operands next to the K/V
+// steps in flight (fp8 caches or head_dim 64); two tiles of 16-bit K/V at head_dim 128 would
+// spill there and take two waves per chunk instead.  Heads of three or four tiles go to two
+// waves of two tiles each where one wave holds two; at head_dim 128 over 16-bit K/V they stay
+// with chunk_kernel, whose LDS-staged blocks measured faster than four lockstep waves reading
+// one chunk.  A launch is one workgroup per resident slot, at most kMaxSplitWorkgroups (a
+// workspace bound known without a GPU: twice the 256 CUs of an MI355X).
+inline int split_tiles_per_wave(int head_dim, bool fp8_kv) {
+  return fp8_kv || head_dim == 64 ? 2 : 1;
+}
+inline int split_max_tiles(int head_dim, bool fp8_kv) {
+  return 2 * split_tiles_per_wave(head_dim, fp8_kv);
+}
 inline int split_chunk_waves(int tiles, int head_dim, bool fp8_kv) {
-  return tiles == 2 && !fp8_kv && head_dim != 64 ? 2 : 1;
+  const int per_wave = split_tiles_per_wave(head_dim, fp8_kv);
+  return tiles <= per_wave ? 1 : tiles / per_wave;
 }
 constexpr long kMaxSplitWorkgroups = 512;
 
@@ -252,11 +261,11 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
   p.split_rt = 0;
   p.split_waves = 0;
   p.split_wgs = 0;
-  if (partition_tokens == 0 && p.tiles_per_head <= kSplitMaxTiles) {
+  if (partition_tokens == 0 && p.tiles_per_head <= split_max_tiles(head_dim, fp8_kv)) {
     // balanced split: equal chunks of the block space, at least two blocks each, so the space
     // never needs more than half its blocks in chunks
-    p.split_rt = p.tiles_per_head;
-    p.split_waves = split_chunk_waves(p.tiles_per_head, head_dim, fp8_kv);
+    p.split_rt = p.tiles_per_head == 3 ? 4 : p.tiles_per_head;   // 1, 2 or 4 tiles
+    p.split_waves = split_chunk_waves(p.split_rt, head_dim, fp8_kv);
     const long long lanes_max = ((long long)batch * num_kv_heads * maxblk + 1) / 2;
     const long long per_wg = kWaves / p.split_waves;
     long long wgs = (lanes_max + per_wg - 1) / per_wg;
@@ -267,7 +276,7 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
     p.items = 0;
     return p;
   }
-  if (partition_tokens == 0 && rows > 16) {   // (with split taken above: rows > 32)
+  if (partition_tokens == 0 && rows > 16) {   // (with split taken above: rows > 32 or > 64)
     const ChunkShape c = rows > 64 ? kChunkWide : kChunkNarrow;
     const int block_rows = 16 * c.waves * c.tiles;
     p.chunk_wide = rows > 64 ? 1 : 0;

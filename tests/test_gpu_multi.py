@@ -124,8 +124,9 @@ def test_prefill_chunk_shapes(case, fp8):
 
 
 SPLIT = [
-    # (q dtype, kv dtype, kv heads, group, head_dim, most draft tokens): heads of at most two
-    # row tiles take the balanced split (one wave per chunk holding every tile of a head)
+    # (q dtype, kv dtype, kv heads, group, head_dim, most draft tokens): heads of two row tiles
+    # per wave of a pair at most take the balanced split (every tile of a head in one wave, or
+    # in two waves sharing a chunk)
     ("bf16", "fp8_e4m3", 2, 8, 128, 4),      # two full tiles over fp8 codes
     ("f16", "fp8_e4m3", 2, 4, 128, 8),
     ("bf16", "bf16", 2, 8, 128, 2),          # one tile of 16-bit K/V
@@ -134,6 +135,10 @@ SPLIT = [
     ("f16", "f16", 4, 1, 128, 8),            # one tile, several tokens in it
     ("f16", "f16", 2, 16, 64, 2),            # two tiles at head_dim 64
     ("bf16", "bf16", 2, 3, 64, 8),           # a partial second tile
+    ("bf16", "fp8_e4m3", 2, 8, 128, 8),      # four fp8 tiles: two waves of two tiles
+    ("f16", "f16", 2, 8, 64, 6),             # three tiles at head_dim 64 (the fourth empty)
+    ("bf16", "bf16", 2, 16, 64, 4),          # four tiles at head_dim 64
+    ("f16", "fp8_e4m3", 2, 5, 128, 8),       # three fp8 tiles, the last partial
 ]
 
 
@@ -204,7 +209,15 @@ def test_full_size_fp8_verification():
     _sampled(m, 2, rng)
 
 
-@pytest.mark.parametrize("kvd,T", [("fp8_e4m3", 4), ("bf16", 2), ("bf16", 4)])
+def test_full_size_wide_fp8_verification():
+    """4 sequences of 32768 fp8 tokens, GQA 64/8, 8 draft tokens each: four row tiles per head
+    in two waves a chunk (sampled rows)."""
+    rng = np.random.default_rng(108)
+    m = Multi("bf16", "fp8_e4m3", 8, 8, 128, [32768] * 4, [8] * 4, seed=108)
+    _sampled(m, 2, rng)
+
+
+@pytest.mark.parametrize("kvd,T", [("fp8_e4m3", 4), ("bf16", 2), ("bf16", 4), ("fp8_e4m3", 6)])
 def test_one_head_over_many_workgroups(kvd, T):
     """One KV head of 65536 tokens: two-block chunks, so its parts come from hundreds of
     workgroups and are merged in LDS-staged batches (sampled rows)."""
@@ -249,13 +262,16 @@ RANDOM = [
     (203, "f16", "f16", 2, 1, 128, 30, 4000, 16),
     (204, "bf16", "fp8_e4m3", 2, 16, 64, 25, 2000, 2),
     (205, "bf16", "bf16", 1, 8, 128, 700, 120, 4),     # several sequences per scanning thread
+    (206, "bf16", "bf16", 2, 16, 64, 50, 3000, 4),     # heads of one to four tiles
+    (207, "f16", "fp8_e4m3", 2, 8, 128, 50, 3000, 8),
 ]
 
 
 @pytest.mark.parametrize("case", RANDOM, ids=lambda c: f"seed{c[0]}")
 def test_random_split_batches(case):
     """Random batches for the balanced split: lengths from 0 (no cached token) to the bound,
-    draft counts from 0 (no rows) to the bound, so heads of one or two tiles, empty sequences
+    draft counts from 0 (no rows) to the bound, so heads of one to four tiles (two for 16-bit K/V at
+    head_dim 128), empty sequences
     and rows before the context all occur in one call."""
     seed, qd, kvd, hkv, g, d, B, lmax, tmax = case
     rng = np.random.default_rng(seed)
