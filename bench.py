@@ -224,9 +224,9 @@ def bench_multi(args, dev) -> int:
     log(f"{args.steps} back-to-back pa_decode_multi calls: {launch_s * 1e6:.1f} us each")
 
     # the library's choice (pa_internal.hpp multi_plan): without a fixed partition, heads of one
-    # or two row tiles (four where one wave holds two) take the balanced split kernel, larger ones the LDS-staged chunk kernel
+    # to four row tiles take the balanced split kernel, larger ones the LDS-staged chunk kernel
     tiles = (maxT * (Hq // Hkv) + 15) // 16
-    if P == 0 and tiles <= (4 if s.kv_dtype == "fp8_e4m3" or s.head_dim == 64 else 2):
+    if P == 0 and tiles <= 4:
         kernel = "multi_split_kernel"
     else:
         kernel = "chunk_kernel" if P == 0 and tiles > 1 else "multi_kernel"

@@ -231,10 +231,10 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
  * with p < 0 sees no token and is zero.  fp32 accumulation; within 2e-3 absolute + 2e-3 relative
  * of the exact result, and the same bits on every call with the same inputs.
  *
- * With partition_tokens 0, heads of at most 32 query rows (T_b * group) get the decode's
+ * With partition_tokens 0, heads of at most 64 query rows (T_b * group) get the decode's
  * balanced split-KV: equal chunks of the batch's (sequence, KV head, block) space, each walked
- * by one wave holding both 16-row tiles of a head (two waves, one tile each, for 16-bit caches
- * at head_dim 128), partial results merged by log-sum-exp inside the kernel.  Larger heads take a kernel that
+ * by one wave holding the head's 16-row tiles (two waves of two tiles for 33-64 rows), partial
+ * results merged by log-sum-exp inside the kernel.  Larger heads take a kernel that
  * stages K/V in LDS for blocks of rows; a fixed partition_tokens cuts every row tile's keys into
  * partitions merged by a second kernel.
  *

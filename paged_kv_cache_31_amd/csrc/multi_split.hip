@@ -1,6 +1,6 @@
 // Causal multi-query attention over the paged cache with a balanced split of the keys, for
 // gfx950: the speculative-verification shape (a few new tokens per sequence) whose query rows
-// per (sequence, KV head) fill one or two MFMA tiles.
+// per (sequence, KV head) fill one to four MFMA tiles.
 //
 // What is computed is pa_decode_multi's attention (row i of sequence b, at logical position
 // p = L_b - T_b + i, attends to tokens 0 .. p; youngju.dev guide, speculative-decoding figure;
@@ -12,7 +12,9 @@
 //  * A wave takes all MT row tiles (16 (token, group member) rows each) of a head at once: every
 //    K/V step is loaded once, with non-temporal loads, and multiplied into each tile.  Giving the
 //    tiles of a chunk to different waves instead (the second one reading the blocks from the
-//    cache) was measured 30% slower: a CU then keeps half as many independent HBM streams.
+//    cache) was measured 30% slower: a CU then keeps half as many independent HBM streams.  Two
+//    16-bit tiles at head_dim 128 fit a wave's registers with the stepper's rolling schedule;
+//    only heads of three or four tiles take two waves per chunk, two tiles each.
 //  * A wave walks its chunk piece by piece (a piece = the part of one sequence head inside the
 //    chunk), with each query column masked at its own causal end.  A piece that is a whole
 //    sequence head is normalised and written.  Cut pieces are merged by log-sum-exp in chunk
@@ -78,13 +80,13 @@ __device__ __forceinline__ void store_row(void* out, size_t row, int D, int grp,
                    pack2<QT>(acc[t][2] * inv, acc[t][3] * inv));
 }
 
-// Two waves walking one chunk (one tile each) read the same blocks; the second finds them in
+// Two waves walking one chunk (two tiles each) read the same blocks; the second finds them in
 // L2 only while the first is not far ahead.  Each wave posts the flattened position of the step
 // it is about to load in LDS and waits (bounded: pacing never decides a result) while its
 // partner is more than kPaceLag blocks behind; a wave that is done posts INT_MAX.  A wave only
 // waits for a partner behind it, which is then not waiting, so the pair always moves on.
-// Measured on the verification batch (64 x 128-8192 bf16 tokens, 4 drafts): unpaced 247 us,
-// lag 8 blocks 239, 4 239, 2 235, 0 (lockstep) 221.
+// Measured on the verification batch (64 x 128-8192 bf16 tokens, 4 drafts, then walked by two
+// waves of one tile each): unpaced 247 us, lag 8 blocks 239, 4 239, 2 235, 0 (lockstep) 221.
 constexpr int kPaceLag = 0;
 constexpr int kPaceSpins = 2048;
 struct PairPace {
@@ -386,13 +388,16 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
     for (int u = 0; u < MT; ++u) end_lane[u] = min(end_lane[u], tend);
     if (j0 < jt) {
       const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+      constexpr bool ROLL = KVT != DT_FP8 && D == 128 && MT == 2;
       if constexpr (RT == 2)
-        st.template walk_tiles<MT>(qB, trow, kvh, j0, jt, end_lane, min(end_lo, tend),
-                                   min(end_hi, tend), m_run, l_run, acc,
-                                   PairPace{sm_post, wave, wave ^ 1, pos - j0});
+        st.template walk_tiles<MT, PairPace, ROLL>(qB, trow, kvh, j0, jt, end_lane,
+                                                   min(end_lo, tend), min(end_hi, tend), m_run,
+                                                   l_run, acc,
+                                                   PairPace{sm_post, wave, wave ^ 1, pos - j0});
       else
-        st.template walk_tiles<MT>(qB, trow, kvh, j0, jt, end_lane, min(end_lo, tend),
-                                   min(end_hi, tend), m_run, l_run, acc);
+        st.template walk_tiles<MT, NoPace, ROLL>(qB, trow, kvh, j0, jt, end_lane,
+                                                 min(end_lo, tend), min(end_hi, tend), m_run,
+                                                 l_run, acc);
     }
 #pragma unroll
     for (int u = 0; u < MT; ++u) l_run[u] = sum_across_rows(l_run[u]);
@@ -659,34 +664,22 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void multi_split_kernel(Mu
   }
 }
 
-// The instances: one tile per head (MT 1, RT 1); two tiles in one wave where its registers hold
-// them (fp8 or head_dim 64: MT 2), else two waves per chunk (RT 2); four tiles (three laid out as
-// four) only where one wave holds two, in two waves per chunk (MT 2, RT 2).
-template <int D, int KVT>
-constexpr bool kTwoTilesOneWave = D == 64 || KVT == DT_FP8;
-
+// The instances: one tile per head (MT 1, RT 1); two tiles in one wave (MT 2); three or four
+// tiles (three laid out as four) in two paced waves of two (MT 2, RT 2).
 template <int D, int QT, int KVT>
 static hipError_t launch_split_t(const MultiArgs& a, hipStream_t stream) {
   const dim3 block(64 * kWaves);
-  if (a.split_rt == 1) {
-    hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 1, 1>), dim3((unsigned)(a.total_lanes / kWaves)),
-                       block, 0, stream, a);
-  } else if (a.split_rt == 2) {
-    if constexpr (kTwoTilesOneWave<D, KVT>)
-      hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 2, 1>),
-                         dim3((unsigned)(a.total_lanes / kWaves)), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 1, 2>),
-                         dim3((unsigned)(a.total_lanes / (kWaves / 2))), block, 0, stream, a);
-  } else if (a.split_rt == 4) {
-    if constexpr (kTwoTilesOneWave<D, KVT>)
-      hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 2, 2>),
-                         dim3((unsigned)(a.total_lanes / (kWaves / 2))), block, 0, stream, a);
-    else
-      return hipErrorInvalidValue;                  // the plan gives these heads to chunk_kernel
-  } else {
+  if (a.split_rt == 1)
+    hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 1, 1>),
+                       dim3((unsigned)(a.total_lanes / kWaves)), block, 0, stream, a);
+  else if (a.split_rt == 2)
+    hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 2, 1>),
+                       dim3((unsigned)(a.total_lanes / kWaves)), block, 0, stream, a);
+  else if (a.split_rt == 4)
+    hipLaunchKernelGGL((multi_split_kernel<D, QT, KVT, 2, 2>),
+                       dim3((unsigned)(a.total_lanes / (kWaves / 2))), block, 0, stream, a);
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 
@@ -694,21 +687,15 @@ template <int D, int QT, int KVT>
 static int split_occupancy_t(int rt) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
-  if (rt == 1) {
+  if (rt == 1)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 1, 1>,
                                                      64 * kWaves, 0);
-  } else if (rt == 2) {
-    if constexpr (kTwoTilesOneWave<D, KVT>)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 2, 1>,
-                                                       64 * kWaves, 0);
-    else
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 1, 2>,
-                                                       64 * kWaves, 0);
-  } else if (rt == 4) {
-    if constexpr (kTwoTilesOneWave<D, KVT>)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 2, 2>,
-                                                       64 * kWaves, 0);
-  }
+  else if (rt == 2)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 2, 1>,
+                                                     64 * kWaves, 0);
+  else if (rt == 4)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, multi_split_kernel<D, QT, KVT, 2, 2>,
+                                                     64 * kWaves, 0);
   return e == hipSuccess ? n : 0;
 }
 

@@ -170,7 +170,6 @@ struct MultiArgs {
   int part_blocks;             // even
   long long total_items;
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
-  int chunk_wide;              // chunk_kernel shape: 1 kChunkWide, 0 kChunkNarrow
   // Balanced split (multi_split_kernel): split_rt > 0 row tiles per head.
   int split_rt;
   int total_lanes;             // chunks of the flattened block space
@@ -180,51 +179,32 @@ struct MultiArgs {
 
 constexpr int kMultiWaves = 4;             // waves per multi_kernel workgroup
 constexpr long kMultiTargetWaves = 4096;   // waves the automatic partition aims for (multi_kernel)
-// chunk_kernel (narrow): one round of resident workgroups, 4 per CU of 2 waves on 256 CUs.
-// Measured on the two verification workloads with targets 512 ... 16384 waves: fewer leave CUs
-// idle (up to 2.3x slower), more add partitions and their partial results (5-50% slower).
-constexpr long kChunkTargetWaves = 2048;
 constexpr int kMultiMinPartBlocks = 16;    // automatic partitions are at least 256 tokens
 
-// Heads with more query rows than multi_split_kernel takes (more than two MFMA tiles) go to
-// chunk_kernel: a workgroup takes a block of rows of one head and stages each K/V step once in
-// LDS for all of them.  Two shapes: kChunkWide (4 waves x 2 tiles = 128 rows, prefill chunks)
-// and kChunkNarrow (2 waves x 1 tile = 32 rows, for 33..64 rows, e.g. 8 draft tokens of a group
-// of 8).
+// Heads with more query rows than multi_split_kernel takes (more than four MFMA tiles) go to
+// chunk_kernel: a workgroup takes a block of 128 rows of one head (4 waves x 2 tiles, prefill
+// chunks) and stages each K/V step once in LDS for all of them.
 struct ChunkShape {
   int waves, tiles;            // waves per workgroup, 16-column tiles per wave
 };
 constexpr ChunkShape kChunkWide = {4, 2};
-constexpr ChunkShape kChunkNarrow = {2, 1};
 
 struct MultiPlan {
   int tiles_per_head, num_parts, part_blocks;
   long long items;             // waves (multi_kernel) or workgroups (chunk_kernel)
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
-  int chunk_wide;              // chunk_kernel shape: 1 wide, 0 narrow
   int split_rt;                // > 0: multi_split_kernel with this many row tiles per head
   int split_waves;             // multi_split_kernel: waves per chunk
   long long split_wgs;         // multi_split_kernel: most workgroups a launch may use
 };
 
-// multi_split_kernel takes heads of up to two row tiles per wave of a pair.  Two tiles go to one
-// wave where its registers hold both tiles' accumulators and query operands next to the K/V
-// steps in flight (fp8 caches or head_dim 64); two tiles of 16-bit K/V at head_dim 128 would
-// spill there and take two waves per chunk instead.  Heads of three or four tiles go to two
-// waves of two tiles each where one wave holds two; at head_dim 128 over 16-bit K/V they stay
-// with chunk_kernel, whose LDS-staged blocks measured faster than four lockstep waves reading
-// one chunk.  A launch is one workgroup per resident slot, at most kMaxSplitWorkgroups (a
-// workspace bound known without a GPU: twice the 256 CUs of an MI355X).
-inline int split_tiles_per_wave(int head_dim, bool fp8_kv) {
-  return fp8_kv || head_dim == 64 ? 2 : 1;
-}
-inline int split_max_tiles(int head_dim, bool fp8_kv) {
-  return 2 * split_tiles_per_wave(head_dim, fp8_kv);
-}
-inline int split_chunk_waves(int tiles, int head_dim, bool fp8_kv) {
-  const int per_wave = split_tiles_per_wave(head_dim, fp8_kv);
-  return tiles <= per_wave ? 1 : tiles / per_wave;
-}
+// multi_split_kernel takes heads of up to four row tiles: one or two in one wave, three or
+// four (three laid out as four) in two paced waves of two.  Two 16-bit tiles at head_dim 128
+// fit a wave's registers only with the stepper's rolling schedule (one K/V register set).  A
+// launch is one workgroup per resident slot, at most kMaxSplitWorkgroups (a workspace bound
+// known without a GPU: twice the 256 CUs of an MI355X).
+constexpr int kSplitMaxTiles = 4;
+inline int split_chunk_waves(int tiles) { return tiles > 2 ? 2 : 1; }
 constexpr long kMaxSplitWorkgroups = 512;
 
 // Key partitions for `base` independent units so that about `target` units run, each at least
@@ -257,15 +237,14 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
   const long long maxblk = ((long long)len_cap + kBlock - 1) / kBlock;
   p.tiles_per_head = (int)((rows + 15) / 16);
   p.row_blocks = 0;
-  p.chunk_wide = 0;
   p.split_rt = 0;
   p.split_waves = 0;
   p.split_wgs = 0;
-  if (partition_tokens == 0 && p.tiles_per_head <= split_max_tiles(head_dim, fp8_kv)) {
+  if (partition_tokens == 0 && p.tiles_per_head <= kSplitMaxTiles) {
     // balanced split: equal chunks of the block space, at least two blocks each, so the space
     // never needs more than half its blocks in chunks
     p.split_rt = p.tiles_per_head == 3 ? 4 : p.tiles_per_head;   // 1, 2 or 4 tiles
-    p.split_waves = split_chunk_waves(p.split_rt, head_dim, fp8_kv);
+    p.split_waves = split_chunk_waves(p.split_rt);
     const long long lanes_max = ((long long)batch * num_kv_heads * maxblk + 1) / 2;
     const long long per_wg = kWaves / p.split_waves;
     long long wgs = (lanes_max + per_wg - 1) / per_wg;
@@ -276,19 +255,12 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
     p.items = 0;
     return p;
   }
-  if (partition_tokens == 0 && rows > 16) {   // (with split taken above: rows > 32 or > 64)
-    const ChunkShape c = rows > 64 ? kChunkWide : kChunkNarrow;
-    const int block_rows = 16 * c.waves * c.tiles;
-    p.chunk_wide = rows > 64 ? 1 : 0;
+  if (partition_tokens == 0) {   // more than 64 rows (fewer took the split above)
+    const int block_rows = 16 * kChunkWide.waves * kChunkWide.tiles;
     p.row_blocks = (int)((rows + block_rows - 1) / block_rows);
-    const long long base = (long long)batch * num_kv_heads * p.row_blocks;
-    if (p.chunk_wide) {
-      p.num_parts = 1;
-      p.part_blocks = (int)(maxblk + (maxblk & 1));
-    } else {
-      multi_parts(p, base, kChunkTargetWaves / c.waves, maxblk, 0);
-    }
-    p.items = base * p.num_parts;
+    p.num_parts = 1;
+    p.part_blocks = (int)(maxblk + (maxblk & 1));
+    p.items = (long long)batch * num_kv_heads * p.row_blocks;
     return p;
   }
   multi_parts(p, (long long)batch * num_kv_heads * (p.tiles_per_head > 0 ? p.tiles_per_head : 1),

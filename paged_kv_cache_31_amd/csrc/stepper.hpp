@@ -189,23 +189,26 @@ struct Stepper {
   // Several column tiles per wave: tile u's columns take qB[u] and their windows end_lane[u];
   // every K/V step is loaded once and multiplied into all MT tiles.  end_lo and end_v bound the
   // windows of all tiles.
-  template <int MT, class Pace = NoPace>
+  // ROLL: one register set instead of two; the next step's K is loaded as soon as this step's
+  // scores are taken, its V as soon as this step's P.V is done (16-bit K/V, no append).
+  template <int MT, class Pace = NoPace, bool ROLL = false>
   __device__ __forceinline__ void walk_tiles(const V8 (&qB)[MT][NC], const int32_t* trow,
                                              int kvh, int j0, int j1, const int (&end_lane)[MT],
                                              int end_lo, int end_v, float (&m_run)[MT],
                                              float (&l_run)[MT], f32x4 (&acc)[MT][NT],
                                              Pace pace = Pace()) const {
-    walk<false, MT>(qB, trow, kvh, j0, j1, end_lane, end_lo, end_v, 0, 1, m_run, l_run, acc,
-                    false, VAppend(), pace);
+    walk<false, MT, Pace, ROLL>(qB, trow, kvh, j0, j1, end_lane, end_lo, end_v, 0, 1, m_run,
+                                l_run, acc, false, VAppend(), pace);
   }
 
-  template <bool APP, int MT, class Pace = NoPace>
+  template <bool APP, int MT, class Pace = NoPace, bool ROLL = false>
   __device__ __forceinline__ void walk(const V8 (&qB)[MT][NC], const int32_t* trow, int kvh,
                                        int j0, int j1, const int (&end_tok)[MT], int end_lo,
                                        int end_v, int s_first, int stride, float (&m_run)[MT],
                                        float (&l_run)[MT], f32x4 (&acc)[MT][NT],
                                        bool wait_stores, VAppend ap, Pace pace = Pace()) const {
     static_assert(!APP || MT == 1, "the append instance takes one tile");
+    static_assert(!ROLL || (!APP && !FP8), "the rolling schedule takes 16-bit K/V, no append");
     const int nsteps = (j1 - j0 + 1) >> 1;
     if (s_first >= nsteps) return;
 
@@ -267,7 +270,33 @@ struct Stepper {
       }
     };
 
-    auto compute = [&](StepRegs<D, FP8>& r, int s) {
+    // the rolling schedule's halves of issue(): K with the pacing and the id prefetch, then V
+    const uint8_t* roll_vp = nullptr;
+    auto issue_k = [&](StepRegs<D, FP8>& r, int s) {
+      pace(j0 + 2 * min(s, nsteps - 1));
+      const int pb0 = nid0, pb1 = nid1;
+      ids_of(s + stride, nid0, nid1);
+      const int kb = k_hi ? pb1 : pb0;
+      const int vb = v_hi ? pb1 : pb0;
+      const uint8_t* kp = kc + ((size_t)kb * Hkv + kvh) * TILE + k_lane_off;
+      roll_vp = vc + ((size_t)vb * Hkv + kvh) * TILE + v_lane_off;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int cc = 0; cc < KL; ++cc) r.k[m][cc] = load16(kp + m * 4 * D * EB + cc * 64);
+    };
+    auto issue_v = [&](StepRegs<D, FP8>& r) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if constexpr (FP8)
+          r.v[i] = load8(roll_vp + i * 16 * kBlock * EB);
+        else
+          r.v[i] = load16(roll_vp + i * 16 * kBlock * EB);
+      }
+    };
+
+    // nxt >= 0 (rolling schedule only): the step whose loads go into r's registers as they free
+    auto compute = [&](StepRegs<D, FP8>& r, int s, int nxt) {
       const int t0 = kBlock * (j0 + 2 * s);
       const int tb = t0 + tb_lane;
       const bool partial = t0 + kStepTokens > (ROWS ? end_lo : end_tok[0]);   // wave-uniform
@@ -330,6 +359,9 @@ struct Stepper {
 #pragma unroll
           for (int u = 0; u < MT; ++u) S[u][m] = M::mma(kA, qB[u][cc], S[u][m]);
         }
+      }
+      if constexpr (ROLL) {
+        if (nxt >= 0) issue_k(r, nxt);
       }
       float qs = qk_scale_log2;
       if constexpr (FP8) qs *= r.ks;
@@ -413,26 +445,36 @@ struct Stepper {
           if constexpr (SPLIT_P) acc[u][i] = M::mma(vA, pLo[u], acc[u][i]);
         }
       }
+      if constexpr (ROLL) {
+        if (nxt >= 0) issue_v(r);
+      }
     };
 
 
     // The steady-state loop issues the next step's loads unconditionally (the tail is peeled),
     // so the loads of one step stay in flight while the previous step is computed.
+    if constexpr (ROLL) {
+      StepRegs<D, FP8> r;
+      issue(r, s_first);
+      for (int s = s_first; s < nsteps; s += stride)
+        compute(r, s, s + stride < nsteps ? s + stride : -1);
+      return;
+    }
     StepRegs<D, FP8> r0, r1;
     int s = s_first, rest = (nsteps - 1 - s_first) / stride;
     issue(r0, s);
     for (; rest >= 2; rest -= 2, s += 2 * stride) {
       issue(r1, s + stride);
-      compute(r0, s);
+      compute(r0, s, -1);
       issue(r0, s + 2 * stride);
-      compute(r1, s + stride);
+      compute(r1, s + stride, -1);
     }
     if (rest == 1) {
       issue(r1, s + stride);
-      compute(r0, s);
-      compute(r1, s + stride);
+      compute(r0, s, -1);
+      compute(r1, s + stride, -1);
     } else {
-      compute(r0, s);
+      compute(r0, s, -1);
     }
   }
 };

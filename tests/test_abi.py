@@ -206,7 +206,7 @@ def _mdesc(**kw):
 
 def test_multi_workspace_size():
     """Every layout starts with the 256 KiB of arrival counters.  Balanced split (automatic; one
-    or two row tiles per head, and three or four, laid out as four, where one wave holds two): then two parts per (workgroup, row
+    to four row tiles per head, three laid out as four): then two parts per (workgroup, row
     tile, column), an fp32 output row plus max and exp-sum, for one workgroup per 8 two-block
     chunks of the largest flattened block space (8 / waves per chunk), at most 512 workgroups.  Fixed partitions: per
     (row, head, partition) an output row plus max and exp-sum.  The chunk kernel with one
@@ -220,24 +220,23 @@ def test_multi_workspace_size():
     size = pa.pa_decode_multi_workspace_size
     # 4 x 2 heads x 8 blocks = 64 blocks -> 32 chunks -> 4 workgroups; 16 rows: one tile
     assert size(_mdesc()) == split(4, 1)
-    # 32 rows: two tiles, in one wave with head_dim 64 or an fp8 cache, else in two waves per
-    # chunk (4 chunks a workgroup)
+    # 32 rows: two tiles in one wave
     assert size(_mdesc(max_query_len=8)) == split(4, 2)
     assert size(_mdesc(max_query_len=8, head_dim=128, kv_dtype=pa.PA_FP8_E4M3)) == \
         split(4, 2, 128)
-    assert size(_mdesc(max_query_len=8, head_dim=128)) == split(8, 2, 128)
+    assert size(_mdesc(max_query_len=8, head_dim=128)) == split(4, 2, 128)
     # a large space is capped at 512 workgroups
     assert size(_mdesc(batch=64, max_blocks_per_seq=512, head_dim=128)) == split(512, 1, 128)
-    # 64 rows: four tiles, in two waves of two with head_dim 64 or an fp8 cache (4 chunks a
-    # workgroup); 48 rows take the four-tile layout too
+    # 64 rows: four tiles, in two waves of two (4 chunks a workgroup); 48 rows take the
+    # four-tile layout too
     assert size(_mdesc(max_query_len=16)) == split(8, 4)
     assert size(_mdesc(max_query_len=12)) == split(8, 4)
     assert size(_mdesc(max_query_len=16, head_dim=128, kv_dtype=pa.PA_FP8_E4M3)) == \
         split(8, 4, 128)
-    # the chunk kernel, here with one partition and no workspace: more than 64 rows, or more
-    # than 32 over 16-bit K/V at head_dim 128
+    assert size(_mdesc(max_query_len=9, head_dim=128)) == split(8, 4, 128)
+    # more than 64 rows: the chunk kernel, with one partition and no workspace
     assert size(_mdesc(max_query_len=17)) == 0
-    assert size(_mdesc(max_query_len=9, head_dim=128)) == 0
+    assert size(_mdesc(max_query_len=17, head_dim=128)) == 0
     d = _mdesc(partition_tokens=32, max_blocks_per_seq=10)          # 10 blocks -> 5 partitions
     rows = 16 * 8 * 5
     assert size(d) == C + _r(rows * 64 * 4) + _r(rows * 2 * 4)

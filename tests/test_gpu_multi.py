@@ -108,9 +108,7 @@ CHUNK = [
     ("f16", 2, 3, 128, (700, 77, 1025), (130, 77, 50)),
     ("bf16", 1, 8, 128, (40, 1000, 333), (40, 17, 300)),
     ("bf16", 2, 4, 64, (20, 600, 5), (64, 35, 32)),          # more queries than context
-    # 33-64 rows: the narrow shape with key partitions over 16-bit K/V at head_dim 128 (over
-    # fp8 codes the balanced split takes them)
-    ("f16", 2, 8, 128, (300, 45, 1000), (8, 3, 5)),
+    ("f16", 2, 16, 128, (300, 45, 1000), (9, 3, 5)),         # a partial second row block
 ]
 
 
@@ -126,18 +124,20 @@ def test_prefill_chunk_shapes(case, fp8):
 
 
 SPLIT = [
-    # (q dtype, kv dtype, kv heads, group, head_dim, most draft tokens): heads of two row tiles
-    # per wave of a pair at most take the balanced split (every tile of a head in one wave, or
-    # in two waves sharing a chunk)
+    # (q dtype, kv dtype, kv heads, group, head_dim, most draft tokens): heads of at most four
+    # row tiles take the balanced split (every tile of a head in one wave, or two tiles in each
+    # of two waves sharing a chunk)
     ("bf16", "fp8_e4m3", 2, 8, 128, 4),      # two full tiles over fp8 codes
     ("f16", "fp8_e4m3", 2, 4, 128, 8),
     ("bf16", "bf16", 2, 8, 128, 2),          # one tile of 16-bit K/V
-    ("bf16", "bf16", 2, 8, 128, 4),          # two 16-bit tiles at head_dim 128: two waves a chunk
+    ("bf16", "bf16", 2, 8, 128, 4),          # two 16-bit tiles at head_dim 128: rolling loads
     ("f16", "f16", 2, 3, 128, 8),            # the same with a partial second tile
     ("f16", "f16", 4, 1, 128, 8),            # one tile, several tokens in it
     ("f16", "f16", 2, 16, 64, 2),            # two tiles at head_dim 64
     ("bf16", "bf16", 2, 3, 64, 8),           # a partial second tile
     ("bf16", "fp8_e4m3", 2, 8, 128, 8),      # four fp8 tiles: two waves of two tiles
+    ("bf16", "bf16", 2, 8, 128, 8),          # four 16-bit tiles at head_dim 128
+    ("f16", "f16", 2, 6, 128, 8),            # three 16-bit tiles, the last partial
     ("f16", "f16", 2, 8, 64, 6),             # three tiles at head_dim 64 (the fourth empty)
     ("bf16", "bf16", 2, 16, 64, 4),          # four tiles at head_dim 64
     ("f16", "fp8_e4m3", 2, 5, 128, 8),       # three fp8 tiles, the last partial
@@ -211,15 +211,17 @@ def test_full_size_fp8_verification():
     _sampled(m, 2, rng)
 
 
-def test_full_size_wide_fp8_verification():
-    """4 sequences of 32768 fp8 tokens, GQA 64/8, 8 draft tokens each: four row tiles per head
-    in two waves a chunk (sampled rows)."""
+@pytest.mark.parametrize("kvd", ["bf16", "fp8_e4m3"])
+def test_full_size_wide_verification(kvd):
+    """4 sequences of 32768 tokens, GQA 64/8, 8 draft tokens each: four row tiles per head in
+    two waves a chunk (sampled rows)."""
     rng = np.random.default_rng(108)
-    m = Multi("bf16", "fp8_e4m3", 8, 8, 128, [32768] * 4, [8] * 4, seed=108)
+    m = Multi("bf16", kvd, 8, 8, 128, [32768] * 4, [8] * 4, seed=108)
     _sampled(m, 2, rng)
 
 
-@pytest.mark.parametrize("kvd,T", [("fp8_e4m3", 4), ("bf16", 2), ("bf16", 4), ("fp8_e4m3", 6)])
+@pytest.mark.parametrize("kvd,T", [("fp8_e4m3", 4), ("bf16", 2), ("bf16", 4), ("fp8_e4m3", 6),
+                                   ("bf16", 8)])
 def test_one_head_over_many_workgroups(kvd, T):
     """One KV head of 65536 tokens: two-block chunks, so its parts come from hundreds of
     workgroups and are merged in LDS-staged batches (sampled rows)."""
@@ -265,6 +267,7 @@ RANDOM = [
     (204, "bf16", "fp8_e4m3", 2, 16, 64, 25, 2000, 2),
     (205, "bf16", "bf16", 1, 8, 128, 700, 120, 4),     # several sequences per scanning thread
     (206, "bf16", "bf16", 2, 16, 64, 50, 3000, 4),     # heads of one to four tiles
+    (208, "bf16", "bf16", 2, 8, 128, 50, 3000, 8),
     (207, "f16", "fp8_e4m3", 2, 8, 128, 50, 3000, 8),
 ]
 
@@ -272,8 +275,7 @@ RANDOM = [
 @pytest.mark.parametrize("case", RANDOM, ids=lambda c: f"seed{c[0]}")
 def test_random_split_batches(case):
     """Random batches for the balanced split: lengths from 0 (no cached token) to the bound,
-    draft counts from 0 (no rows) to the bound, so heads of one to four tiles (two for 16-bit K/V at
-    head_dim 128), empty sequences
+    draft counts from 0 (no rows) to the bound, so heads of one to four tiles, empty sequences
     and rows before the context all occur in one call."""
     seed, qd, kvd, hkv, g, d, B, lmax, tmax = case
     rng = np.random.default_rng(seed)
