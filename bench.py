@@ -2,11 +2,13 @@
 """Benchmark of the paged decode-attention hot path on one MI355X.
 
 One step = pa_kv_append of every sequence's new token + pa_decode over the whole batch (one
-decode step of one attention layer).  The default workload is the 7B-style multi-head layer:
-16 sequences x 2048 tokens, 32 query heads = 32 KV heads, head_dim 128, fp16, 16-token blocks
-scattered over a pool twice the needed size.  Inputs are seeded synthetic data, resident in HBM
-before the timed region; the pool is replicated `rotations` times and the steps cycle through the
-copies so that no step finds its K/V in the 256 MB last-level cache.
+decode step of one attention layer).  The headline workload is the largest single-GPU one, the
+70B-style GQA layer: 64 sequences of 128..8192 tokens (uniform), 64 query / 8 KV heads,
+head_dim 128, bf16, 16-token blocks scattered over a pool twice the needed size (1.16 GB of
+K/V, tables, queries and outputs per call).  Every other decode workload is timed the same way
+in the same run and reported under "configs".  Inputs are seeded synthetic data, resident in
+HBM before the timed region; the pool is replicated `rotations` times and the steps cycle
+through the copies so that no step finds its K/V in the 256 MB last-level cache.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -14,6 +16,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -28,7 +31,12 @@ METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode token
 PEAK_GBS = 8000.0           # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA
 BLOCK_TOKENS = 16
-DEFAULT_WORKLOAD = "mha_b16_h32_d128_f16_l2048"
+DEFAULT_WORKLOAD = "gqa_b64_h64kv8_d128_bf16_l128to8192"
+# decode workloads timed beside the headline (reported under "configs"), smallest first
+CONFIG_WORKLOADS = ("tiny_b4_h8kv2_d64_bf16", "mha_b16_h32_d128_f16_l2048",
+                    "gqa_b64_h64kv8_d128_bf16_l128to8192",
+                    "mixed_b256_h32kv8_d128_bf16_lognorm600_prefix1024",
+                    "long_b4_h64kv8_d128_fp8_l32768_split512")
 
 
 def log(msg: str) -> None:
@@ -442,62 +450,22 @@ def bench_copy(args, dev) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="a single-query workload (default) or a multi-query one: "
-                         "verify_b64_h64kv8_d128_bf16_l128to8192_t4, "
-                         "verify_b4_h64kv8_d128_fp8_l32768_t4, "
-                         "prefill_b4_h32kv8_d128_bf16_l4608_chunk512")
-    ap.add_argument("--partition", type=int, default=None,
-                    help="key-partition tokens (default: the workload's, else the library's)")
-    ap.add_argument("--rotations", type=int, default=0, help="pool copies cycled (0: auto)")
-    ap.add_argument("--separate-append", action="store_true",
-                    help="time a step as pa_kv_append + pa_decode instead of pa_decode_append")
-    ap.add_argument("--no-shared-prefixes", action="store_true",
-                    help="decode a workload with a shared prefix without the prefix plan")
-    ap.add_argument("--graph-layers", type=int, default=0,
-                    help="also time a step of this many layers (one pool copy each) eagerly "
-                         "and as one HIP graph replay")
-    ap.add_argument("--cow-pairs", type=int, default=0,
-                    help="instead: time pa_copy_blocks of this many (source, target) block pairs "
-                         "on the workload's pool, and the host pool's slot bookkeeping")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: this library runs on one GPU; no multi-GPU path is built, so "
-              f"--gpus {args.gpus} is not supported (run with --gpus 1)", file=sys.stderr)
-        return 2
-
+def bench_decode(args, dev, name: str, headline: bool) -> dict:
+    """One decode workload: a step is pa_decode_append (the append of token L-1 fused into the
+    decode) unless --separate-append; the per-launch duration of the decode call alone is timed
+    back to back between HIP events on the launching stream.  headline=False: the compact record
+    reported under "configs" (no graph timing, no CPU baseline)."""
     import numpy as np
     import torch
 
     import paged_kv_cache_31_amd as pa
     import workloads
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    if args.copy_probe:
-        return copy_probe(dev)
-    pa.lib()
-    if args.workload in workloads.MULTI_SPECS:
-        return bench_multi(args, dev)
-    if args.cow_pairs:
-        return bench_copy(args, dev)
-
     t0 = time.perf_counter()
-    wl = workloads.make(args.workload, poison=False)
+    wl = workloads.make(name, poison=False)
     s = wl.spec
     B, Hq, Hkv, D = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim
-    log(f"workload {args.workload}: generated in {time.perf_counter() - t0:.1f} s")
+    log(f"workload {name}: generated in {time.perf_counter() - t0:.1f} s")
 
     def dbytes(lens, unique=None):
         return workloads.decode_bytes(lens, Hq, Hkv, D, s.q_dtype, s.kv_dtype, unique)
@@ -508,7 +476,7 @@ def main() -> int:
     pool_bytes = wl.k_cache.nbytes + wl.v_cache.nbytes
     R = args.rotations or max(2, math.ceil(2 * 2**30 / bytes_decode))
     R = max(1, min(R, 64, int(48 * 2**30 // pool_bytes)))
-    if args.graph_layers:
+    if headline and args.graph_layers:
         R = max(R, args.graph_layers)
 
     def to_dev(bits, dtype):
@@ -609,7 +577,7 @@ def main() -> int:
         "dtype": s.kv_dtype if s.kv_dtype == s.q_dtype else f"{s.q_dtype}+{s.kv_dtype}",
         "data": "synthetic",
         "config": {
-            "workload": args.workload, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "workload": name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": 16, "q_dtype": s.q_dtype, "kv_dtype": s.kv_dtype,
             "context_len_min": int(lens_np.min()), "context_len_max": int(lens_np.max()),
             "context_tokens": int(lens_np.sum()), "unique_tokens": int(wl.unique_tokens),
@@ -626,7 +594,7 @@ def main() -> int:
                            "append": bytes_append},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                     "traffic": traffic_record(args.workload),
+                     "traffic": traffic_record(name),
                      "kernel": kernel, "bytes_per_launch": bytes_decode,
                      "duration_us": round(launch_s * 1e6, 2)},
     }
@@ -656,12 +624,94 @@ def main() -> int:
             "us_per_decode_launch": round(reuse_s * 1e6, 2),
             "achieved": round(bytes_decode / reuse_s / 1e9, 2), "unit": "GB/s",
             "frac": round(bytes_decode / reuse_s / 1e9 / PEAK_GBS, 4)}
-    if args.graph_layers:
+    if headline and args.graph_layers:
         result["graph"] = graph_timing(args, rots, tables, lens, scale, k_scale, v_scale, mcl, P,
                                        share, ws_bytes, dev)
-    if not args.no_cpu_baseline:
+    if headline and not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(wl, dbytes, bytes_append)
+    record = {
+        "workload": name, "kernel": kernel, "bytes_per_launch": bytes_decode,
+        "us_per_decode_launch": round(launch_s * 1e6, 2),
+        "achieved_GBps": round(achieved, 2), "frac": round(achieved / PEAK_GBS, 4),
+        "decode_tokens_per_s": round(B / launch_s, 1),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "step": "pa_kv_append + pa_decode" if args.separate_append else "pa_decode_append",
+    }
+    if "reusing_the_plan" in result:
+        record["reusing_the_plan"] = {k: result["reusing_the_plan"][k] for k in
+                                      ("us_per_decode_launch", "achieved", "frac")}
+    if not headline:
+        return record
+    result["this_config"] = record
+    return result
+
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="a single-query workload (default) or a multi-query one: "
+                         "verify_b64_h64kv8_d128_bf16_l128to8192_t4, "
+                         "verify_b4_h64kv8_d128_fp8_l32768_t4, "
+                         "prefill_b4_h32kv8_d128_bf16_l4608_chunk512")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="key-partition tokens (default: the workload's, else the library's)")
+    ap.add_argument("--rotations", type=int, default=0, help="pool copies cycled (0: auto)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="time a step as pa_kv_append + pa_decode instead of pa_decode_append")
+    ap.add_argument("--no-shared-prefixes", action="store_true",
+                    help="decode a workload with a shared prefix without the prefix plan")
+    ap.add_argument("--graph-layers", type=int, default=0,
+                    help="also time a step of this many layers (one pool copy each) eagerly "
+                         "and as one HIP graph replay")
+    ap.add_argument("--cow-pairs", type=int, default=0,
+                    help="instead: time pa_copy_blocks of this many (source, target) block pairs "
+                         "on the workload's pool, and the host pool's slot bookkeeping")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the chosen workload, not every decode workload beside it")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; no multi-GPU path is built, so "
+              f"--gpus {args.gpus} is not supported (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_31_amd as pa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    if args.copy_probe:
+        return copy_probe(dev)
+    pa.lib()
+    if args.workload in workloads.MULTI_SPECS:
+        return bench_multi(args, dev)
+    if args.cow_pairs:
+        return bench_copy(args, dev)
+
+    result = bench_decode(args, dev, args.workload, headline=True)
+    if not args.no_configs:
+        # every decode workload, timed the same way in this run (the headline's own included)
+        result["configs"] = []
+        for name in CONFIG_WORKLOADS:
+            gc.collect()
+            torch.cuda.empty_cache()                  # the previous workload's pool copies
+            if name == args.workload:
+                result["configs"].append(result["this_config"])
+            else:
+                result["configs"].append(bench_decode(args, dev, name, headline=False))
+    result.pop("this_config", None)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -36,8 +36,9 @@
  *
  * Errors: conditions the host can see (null pointers, non-positive sizes, unsupported shapes or
  * dtype pairs, misaligned pointers, a short workspace) return a status before anything is
- * launched.  Device-resident values are a caller contract that is not checked on the host; the
- * kernels clamp them so that nothing is ever read or written outside the described arrays:
+ * launched.  Device-resident values are a caller contract that is not checked on the host (the
+ * Python binding's check=True validates it on host copies, for tests); the kernels clamp them
+ * so that nothing is ever read or written outside the described arrays:
  *   - a slot outside [0, num_blocks*16) is skipped by pa_kv_append;
  *   - a context length is clamped to [0, min(max_context_len, max_blocks_per_seq*16)];
  *   - a block-table entry outside [0, num_blocks) reads physical block 0 instead
@@ -84,9 +85,9 @@ typedef struct pa_decode_desc {
   int32_t max_blocks_per_seq; /* row length (stride) of block_tables, > 0 */
   int32_t max_context_len;    /* host-side upper bound on context_lens; sizes the launch without
                                  reading device memory.  0 = max_blocks_per_seq * 16. */
-  int32_t partition_tokens;   /* split-KV chunk length in tokens, a multiple of 32 in [32, 65536];
-                                 0 = chunks of equal length balanced over the GPU's resident
-                                 waves (the default, best for ragged batches) */
+  int32_t partition_tokens;   /* split-KV chunk length in tokens, a multiple of the 16-token
+                                 block in [16, 65536]; 0 = chunks of equal length balanced over
+                                 the GPU's resident waves (the default, best for ragged batches) */
   int32_t q_dtype;            /* PA_F16 or PA_BF16; the output has the same dtype */
   int32_t shared_prefixes;    /* 0, 1 or 2.  1: sequences whose block tables start with the same
                                  physical blocks (a prefix cache shares blocks this way: youngju.dev
@@ -98,13 +99,16 @@ typedef struct pa_decode_desc {
                                  2: the same, reusing the grouping that the last call with 1 left in
                                  this workspace instead of planning again: for the layers of one
                                  step, whose calls read the same block_tables and context_lens.  The
-                                 caller guarantees those (and the whole descriptor apart from this
-                                 field) are unchanged since that call, and that the workspace saw
-                                 only such calls in between (another descriptor's or
-                                 pa_decode_multi's scratch may overlap the saved grouping); the
-                                 results are then bitwise those of a call with 1.  On a workspace
-                                 no planning call has written (all zero), 2 reads no shared
-                                 blocks and gives the unshared results. */
+                                 caller guarantees those are unchanged since that call, and that
+                                 the workspace saw only such calls in between; the results are
+                                 then bitwise those of a call with 1.  The planning call saves a
+                                 signature of its descriptor and workspace layout with the plan;
+                                 a reusing call that finds another signature there (a workspace
+                                 no planning call has written, another descriptor, or scratch of
+                                 another call written over it) reads no shared blocks and gives
+                                 the unshared results.  Saved plan entries are clamped into range
+                                 before use, so even a workspace overwritten in a way the
+                                 signature misses is never read or written out of bounds. */
 } pa_decode_desc;
 
 typedef struct pa_multi_desc {
@@ -115,8 +119,8 @@ typedef struct pa_multi_desc {
   int32_t max_context_len;    /* host-side bound on context_lens, as in pa_decode_desc (0: table) */
   int32_t total_queries;      /* rows of q and out, >= 0 */
   int32_t max_query_len;      /* host-side bound on query_start[b+1] - query_start[b], > 0 */
-  int32_t partition_tokens;   /* key partition per row tile, a multiple of 32 in [32, 65536];
-                                 0 = chosen from the shape (see pa_decode_multi) */
+  int32_t partition_tokens;   /* key partition per row tile, a multiple of the 16-token block in
+                                 [16, 65536]; 0 = chosen from the shape (see pa_decode_multi) */
   int32_t q_dtype;            /* PA_F16 or PA_BF16; the output has the same dtype */
 } pa_multi_desc;
 

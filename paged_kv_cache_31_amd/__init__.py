@@ -18,6 +18,8 @@ import threading
 
 import torch
 
+from . import contract
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
@@ -188,8 +190,17 @@ class AppendCall:
             _check("pa_kv_append", st)
 
 
-def pa_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
-    """Scatter k_new/v_new [T][Hkv][D] into their slots (int64 [T], <0 skips)."""
+def _host(t):
+    return t.detach().cpu().numpy()
+
+
+def pa_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None,
+                 check=False) -> None:
+    """Scatter k_new/v_new [T][Hkv][D] into their slots (int64 [T], <0 skips).
+
+    check=True (tests): first copy slot_mapping to the host and validate it (contract.py)."""
+    if check:
+        contract.check_slots(_host(slot_mapping), k_cache.shape[0])
     AppendCall(k_new, v_new, slot_mapping, k_cache, v_cache, stream)()
 
 
@@ -227,6 +238,12 @@ def pa_decode_workspace_size(desc: DecodeDesc) -> int:
 
 
 _workspaces: dict = {}
+
+# Which call last left a shared-prefix plan in a workspace (keyed by its device address): the
+# key of a planning call with the same descriptor, tables and lengths lets a later call reuse
+# the plan (shared_prefixes 2); any other call on the workspace overwrites its scratch, so it
+# forgets the entry and the next reusing call plans again.
+_plan_owner: dict = {}
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
@@ -277,27 +294,55 @@ class DecodeCall:
                 ctypes.c_float(scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(wbytes), st)
         if fused:
             self._name, self._fn = "pa_decode_append", lib().pa_decode_append
-            self._args = (ctypes.byref(self._desc), _ptr(q), _ptr(k_new), _ptr(v_new),
-                          _ptr(k_cache), _ptr(v_cache)) + tail
+            head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache))
         else:
             self._name, self._fn = "pa_decode", lib().pa_decode
-            self._args = (ctypes.byref(self._desc), _ptr(q), _ptr(k_cache), _ptr(v_cache)) + tail
+            head = (_ptr(q), _ptr(k_cache), _ptr(v_cache))
+        self._args = (ctypes.byref(self._desc),) + head + tail
+        # shared-prefix plan bookkeeping (see _plan_owner)
+        self._ws = workspace.data_ptr()
+        self._mode = int(shared_prefixes)
+        d = self._desc
+        self._plan_key = (d.cache.num_blocks, d.cache.num_kv_heads, d.cache.head_dim,
+                          d.cache.kv_dtype, d.batch, d.num_q_heads, d.max_blocks_per_seq,
+                          d.max_context_len, d.partition_tokens, d.q_dtype,
+                          block_tables.data_ptr(), context_lens.data_ptr(), wbytes)
+        if self._mode == 2:                  # the planning form, for when the plan is gone
+            self._plan_desc = decode_desc(q, k_cache, block_tables, max_context_len,
+                                          partition_tokens, 1)
+            self._plan_args = (ctypes.byref(self._plan_desc),) + head + tail
 
     def __call__(self) -> None:
-        st = self._fn(*self._args)
+        args = self._args
+        self.reused = False           # whether this call took a saved plan (shared_prefixes 2)
+        if self._mode == 0:
+            _plan_owner.pop(self._ws, None)
+        else:
+            if self._mode == 2:
+                if _plan_owner.get(self._ws) == self._plan_key:
+                    self.reused = True
+                else:
+                    args = self._plan_args
+            _plan_owner[self._ws] = self._plan_key
+        st = self._fn(*args)
         if st != PA_OK:
             _check(self._name, st)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
               v_scale=None, max_context_len=0, partition_tokens=0, workspace=None,
-              stream=None, shared_prefixes=False) -> torch.Tensor:
+              stream=None, shared_prefixes=False, check=False) -> torch.Tensor:
     """out[b][h] = softmax(scale * q[b][h] . K_b^T) . V_b through the block tables; returns out.
 
     shared_prefixes: read blocks that several sequences' tables start with once per group of
     sequences; 2 reuses the grouping planned by the previous call on the same workspace (the
-    layers of one step: unchanged block tables, lengths and descriptor, and no other kind of
-    call on that workspace in between), see pa_decode_desc.shared_prefixes."""
+    layers of one step: unchanged block tables, lengths and descriptor), see
+    pa_decode_desc.shared_prefixes.  The binding tracks which call last used each workspace and
+    plans again when another call has used it since the planning call.
+    check=True (tests): first copy the tables and lengths to the host and validate them."""
+    if check:
+        contract.check_tables(_host(block_tables), _host(context_lens), k_cache.shape[0],
+                              max_context_len)
     DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                max_context_len, partition_tokens, workspace, stream, shared_prefixes)()
     return out
@@ -305,9 +350,14 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_sca
 
 def pa_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
                      k_scale=None, v_scale=None, max_context_len=0, partition_tokens=0,
-                     workspace=None, stream=None, shared_prefixes=False) -> torch.Tensor:
+                     workspace=None, stream=None, shared_prefixes=False,
+                     check=False) -> torch.Tensor:
     """Store k_new/v_new [B][Hkv][D] as token context_lens[b]-1 of every sequence, then decode
-    (pa_kv_append + pa_decode in one launch); returns out."""
+    (pa_kv_append + pa_decode in one launch); returns out.
+    check=True (tests): first validate the tables, lengths and appended blocks on the host."""
+    if check:
+        contract.check_decode_append(_host(block_tables), _host(context_lens), k_cache.shape[0],
+                                     max_context_len)
     DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                max_context_len, partition_tokens, workspace, stream, shared_prefixes, k_new,
                v_new)()
@@ -353,6 +403,7 @@ class MultiCall:
         wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         self._keep = (q, query_start, k_cache, v_cache, block_tables, context_lens, out, k_scale,
                       v_scale, workspace)
+        self._ws = None if workspace is None else workspace.data_ptr()
         self._fn = lib().pa_decode_multi
         self._args = (ctypes.byref(self._desc), _ptr(q), _ptr(query_start), _ptr(k_cache),
                       _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
@@ -360,6 +411,8 @@ class MultiCall:
                       ctypes.c_size_t(wbytes), st)
 
     def __call__(self) -> None:
+        if self._ws is not None:
+            _plan_owner.pop(self._ws, None)          # its scratch overwrites a saved plan
         st = self._fn(*self._args)
         if st != PA_OK:
             _check("pa_decode_multi", st)
@@ -367,9 +420,14 @@ class MultiCall:
 
 def pa_decode_multi(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, out,
                     max_query_len, k_scale=None, v_scale=None, max_context_len=0,
-                    partition_tokens=0, workspace=None, stream=None) -> torch.Tensor:
+                    partition_tokens=0, workspace=None, stream=None,
+                    check=False) -> torch.Tensor:
     """Causal attention of several query tokens per sequence (speculative verification, prefill
-    chunks) over the paged cache; returns out."""
+    chunks) over the paged cache; returns out.
+    check=True (tests): first validate query_start, tables and lengths on the host."""
+    if check:
+        contract.check_multi(_host(query_start), _host(block_tables), _host(context_lens),
+                             k_cache.shape[0], q.shape[0], max_query_len, max_context_len)
     MultiCall(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, out,
               max_query_len, k_scale, v_scale, max_context_len, partition_tokens, workspace,
               stream)()
@@ -471,12 +529,15 @@ class BlockPool:
         return int(slot.value), (None if src.value < 0 else (int(src.value), int(dst.value)))
 
 
-def pa_copy_blocks(pairs, k_cache, v_cache, k_scale=None, v_scale=None, stream=None) -> None:
+def pa_copy_blocks(pairs, k_cache, v_cache, k_scale=None, v_scale=None, stream=None,
+                   check=False) -> None:
     """Copy whole blocks (every KV head, K and V, fp8 scales) for int32 pairs [n][2] on the
-    device: (source, target)."""
+    device: (source, target).  check=True (tests): first validate the pairs on the host."""
     for t in (pairs, k_cache, v_cache):
         assert t.is_cuda and t.is_contiguous()
     assert pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2
+    if check:
+        contract.check_copy_pairs(_host(pairs), k_cache.shape[0])
     st = lib().pa_copy_blocks(ctypes.byref(cache_desc(k_cache)), pairs.shape[0], _ptr(pairs),
                               _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                               _stream(stream))

@@ -65,12 +65,13 @@
 namespace pa {
 
 // Leading blocks of sequence b that prefix_kernel covers (0 when shared prefixes are off).  The
-// plan never takes the block holding a sequence's last token, so at least one block is left;
-// the clamp only keeps indexing in range.
+// plan never takes the block holding a sequence's last token and never more than
+// kMaxSharedBlocks, so at least one block is left; the clamp only keeps indexing in range
+// (the prefix parts read for a sequence then stay within its prefix_parts).
 __device__ __forceinline__ int skip_of(const DecodeArgs& a, int b, int nblk) {
   if (!a.ws_skip) return 0;
   const int s = a.ws_skip[b];
-  return max(0, min(s, nblk - 1));
+  return max(0, min(min(s, nblk - 1), kMaxSharedBlocks));
 }
 
 // A cut piece parked in LDS for the workgroup-level merge.
@@ -715,7 +716,16 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
   // planning call saved goes straight to the units.
   int U = 0;
   if (a.plan_reuse) {
-    U = uniform(a.plan_units[0]);
+    // The saved plan is taken only if the header carries this call's signature (descriptor and
+    // workspace layout) and a unit count the layout can hold; otherwise (another kind of call
+    // wrote over it, or none planned) the call runs with no shared blocks: no units, and
+    // workgroup 0 sets every skip count to 0 before decode_kernel reads them.
+    const int u0 = a.plan_units[0], s1 = a.plan_units[1], s2 = a.plan_units[2];
+    const int umax = plan_tiles_of(B) * Hkv * a.prefix_parts;
+    const bool valid = s1 == a.plan_sig && s2 == ~a.plan_sig && u0 >= 0 && u0 <= umax;
+    U = valid ? uniform(u0) : 0;
+    if (!valid && blockIdx.x == 0)
+      for (int b = tid; b < B; b += NTH) a.ws_skip[b] = 0;
   } else {
     // ---- 1. Candidates: two or more whole blocks before the one with the last token, hashed by
     // their first physical block.  A group's leader is its smallest sequence index.
@@ -897,7 +907,11 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
         const int b = tid * PER + q, slot = s_slot[b];
         if (b < B) a.ws_skip[b] = mem[q] ? h_p[slot] : 0;
       }
-      if (tid == 0) a.plan_units[0] = U;
+      if (tid == 0) {
+        a.plan_units[0] = U;
+        a.plan_units[1] = a.plan_sig;
+        a.plan_units[2] = ~a.plan_sig;
+      }
     }
     __syncthreads();
   }
@@ -909,12 +923,14 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
     int* rec = a.plan_units + kUnitHead + (size_t)u * kUnitRec;
     int lead, kvh, k, j0, j1, member;
     if (a.plan_reuse) {
-      lead = uniform(rec[0]);
-      j0 = uniform(rec[1]);
-      j1 = uniform(rec[2]);
-      kvh = uniform(rec[3]);
-      k = uniform(rec[4]);
+      // clamped into range: the records are workspace contents this call did not write
+      lead = min(max(uniform(rec[0]), 0), B - 1);
+      j1 = min(max(uniform(rec[2]), 0), min(MB, kMaxSharedBlocks));
+      j0 = min(max(uniform(rec[1]), 0), j1);
+      kvh = min(max(uniform(rec[3]), 0), Hkv - 1);
+      k = min(max(uniform(rec[4]), 0), a.prefix_parts - 1);
       member = r < S ? rec[kUnitMembers + r] : -1;
+      if (member >= B) member = -1;
     } else {
       int lo = 0, hi = kPlanMaxBatch - 1;           // the leader whose group's units contain u
       while (lo < hi) {
@@ -963,14 +979,16 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
 #pragma unroll
     for (int i = 0; i < NT; ++i) sm_acc[wave][i][lane] = acc[i];
     __syncthreads();
-    // wave 0 always has a step, so the maximum is finite; waves without steps weigh 0
+    // wave 0 has a step whenever the unit has blocks, so the maximum is finite; waves without
+    // steps weigh 0 (an empty unit, possible only from a clamped record, gives zeros)
     float M_ = sm_m[0][col];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M_ = fmaxf(M_, sm_m[w][col]);
+    const float M_ref = M_ == -INFINITY ? 0.0f : M_;
     float wt[kWaves], L_ = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      wt[w] = fast_exp2(sm_m[w][col] - M_);
+      wt[w] = fast_exp2(sm_m[w][col] - M_ref);
       L_ += wt[w] * sm_l[w][col];
     }
     if (member >= 0) {

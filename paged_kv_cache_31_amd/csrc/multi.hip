@@ -70,6 +70,9 @@ __global__ __launch_bounds__(64 * kMultiWaves, 2) void multi_kernel(MultiArgs a)
   const int nblk = blocks_of(end_hi);
   const int j0 = part * a.part_blocks;
   const int j1 = min(j0 + a.part_blocks, nblk);
+  // keys from 16 * j1 on belong to later partitions; a partition of an odd number of blocks
+  // ends with a step whose second block repeats its first, and those slots must be masked too
+  const int cap = kBlock * j1;
   const long long n = (long long)q0 + i;               // query row of q and out
   const bool row_ok = real && n >= 0 && n < a.total_queries;
   const size_t row = (size_t)n * a.num_q_heads + kvh * G + g;
@@ -82,8 +85,8 @@ __global__ __launch_bounds__(64 * kMultiWaves, 2) void multi_kernel(MultiArgs a)
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (j0 < j1)
-    st.walk_rows(qB, a.block_tables + (size_t)b * a.max_blocks_per_seq, kvh, j0, j1, end_lane,
-                 end_lo, end_hi, m_run, l_run, acc);
+    st.walk_rows(qB, a.block_tables + (size_t)b * a.max_blocks_per_seq, kvh, j0, j1,
+                 min(end_lane, cap), min(end_lo, cap), min(end_hi, cap), m_run, l_run, acc);
   l_run = sum_across_rows(l_run);
   if (!row_ok) return;
 

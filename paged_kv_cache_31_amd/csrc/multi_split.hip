@@ -85,8 +85,10 @@ __device__ __forceinline__ void store_row(void* out, size_t row, int D, int grp,
 // it is about to load in LDS and waits (bounded: pacing never decides a result) while its
 // partner is more than kPaceLag blocks behind; a wave that is done posts INT_MAX.  A wave only
 // waits for a partner behind it, which is then not waiting, so the pair always moves on.
-// Measured on the verification batch (64 x 128-8192 bf16 tokens, 4 drafts, then walked by two
-// waves of one tile each): unpaced 247 us, lag 8 blocks 239, 4 239, 2 235, 0 (lockstep) 221.
+// The pairs are two waves of two tiles each (heads of three or four row tiles).  For them
+// lockstep and allowed lags of 2 and 8 blocks measured the same within noise (64 x 128-8192
+// bf16 tokens with 8 drafts: 262.4-263.8 us; 4 x 32768 bf16 tokens with 8 drafts:
+// 125.9-126.6 us), so the pair walks in lockstep.
 constexpr int kPaceLag = 0;
 constexpr int kPaceSpins = 2048;
 struct PairPace {

@@ -49,7 +49,7 @@ pa_status check_decode_desc(const pa_decode_desc* d) {
   const int group = d->num_q_heads / d->cache.num_kv_heads;
   if (group > 16) return PA_ERR_UNSUPPORTED;
   if (d->partition_tokens != 0 &&
-      (d->partition_tokens % pa::kStepTokens != 0 || d->partition_tokens > pa::kMaxPartition))
+      (d->partition_tokens % pa::kBlock != 0 || d->partition_tokens > pa::kMaxPartition))
     return PA_ERR_INVALID_ARG;
   if (blocks_upper(d) >= INT32_MAX) return PA_ERR_UNSUPPORTED;   // flattened index is 32-bit
   if (chunk_capacity(d) > pa::kMaxWorkgroups * pa::kWaves) return PA_ERR_UNSUPPORTED;
@@ -142,6 +142,25 @@ pa::WorkspaceLayout layout_of(const pa_decode_desc* d) {
 }
 
 size_t workspace_bytes_of(const pa_decode_desc* d) { return layout_of(d).total; }
+
+// Signature of a shared-prefix plan: the descriptor fields and the workspace layout it was made
+// for (FNV-1a over them).  A call reusing a plan takes it only if it finds its own signature.
+int32_t plan_signature(const pa_decode_desc* d, const pa::WorkspaceLayout& w) {
+  const uint64_t fields[] = {(uint64_t)d->batch, (uint64_t)d->num_q_heads,
+                             (uint64_t)d->cache.num_kv_heads, (uint64_t)d->cache.head_dim,
+                             (uint64_t)d->cache.kv_dtype, (uint64_t)d->q_dtype,
+                             (uint64_t)d->cache.num_blocks, (uint64_t)d->max_blocks_per_seq,
+                             (uint64_t)len_cap(d), (uint64_t)d->partition_tokens,
+                             (uint64_t)w.plan, (uint64_t)w.gp_acc, (uint64_t)w.units,
+                             (uint64_t)w.total};
+  uint32_t h = 2166136261u;
+  for (uint64_t f : fields)
+    for (int i = 0; i < 8; ++i) {
+      h ^= (uint32_t)((f >> (8 * i)) & 0xFF);
+      h *= 16777619u;
+    }
+  return (int32_t)h;
+}
 
 // Resident decode waves on the current device for this kernel instance, cached per device.
 int64_t resident_waves(const pa_decode_desc* d) {
@@ -262,13 +281,16 @@ pa_status check_multi_desc(const pa_multi_desc* d) {
     return PA_ERR_INVALID_ARG;
   if (d->num_q_heads % d->cache.num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (d->partition_tokens != 0 &&
-      (d->partition_tokens % pa::kStepTokens != 0 || d->partition_tokens > pa::kMaxPartition))
+      (d->partition_tokens % pa::kBlock != 0 || d->partition_tokens > pa::kMaxPartition))
     return PA_ERR_INVALID_ARG;
   if (d->q_dtype != PA_F16 && d->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   const int kv = d->cache.kv_dtype;
   if (kv != PA_FP8_E4M3 && kv != d->q_dtype) return PA_ERR_UNSUPPORTED;
   // grid sizes: items of the attention kernel and rows of the merge, 4 waves per workgroup
   const pa::MultiPlan p = multi_plan_of(d);
+  if (p.split_rt > 0 && (int64_t)d->batch * d->cache.num_kv_heads *
+                                ((multi_len_cap(d) + pa::kBlock - 1) / pa::kBlock) >= INT32_MAX)
+    return PA_ERR_UNSUPPORTED;   // the balanced split indexes the flattened block space in 32 bits
   if (p.items > (1LL << 32) || (long long)d->batch * d->max_query_len * d->num_q_heads > (1LL << 32))
     return PA_ERR_UNSUPPORTED;
   if (p.row_blocks > 0 && p.items > (1LL << 31) - 8) return PA_ERR_UNSUPPORTED;  // one per workgroup
@@ -457,6 +479,7 @@ pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_n
   a.prefix_parts = share ? pa::prefix_parts_of(desc->max_blocks_per_seq) : 0;
   a.plan_units = share ? reinterpret_cast<int*>(ws + lay.units) : nullptr;
   a.plan_reuse = share && desc->shared_prefixes == 2 ? 1 : 0;
+  a.plan_sig = share ? plan_signature(desc, lay) : 0;
   a.batch = desc->batch;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->cache.num_kv_heads;

@@ -77,6 +77,9 @@ struct DecodeArgs {
   // read the same tables): [0] the unit count, then kUnitRec ints per unit from kUnitHead on.
   int* plan_units;
   int plan_reuse;       // 1: take the saved units instead of planning (and keep ws_skip)
+  int plan_sig;         // signature of the descriptor and workspace layout: a planning call
+                        // saves it beside the unit count, a reusing call takes the saved plan
+                        // only if it finds its own there (else it runs without shared blocks)
   int batch;
   int num_q_heads;
   int num_kv_heads;
@@ -84,8 +87,8 @@ struct DecodeArgs {
   int num_blocks;
   int max_blocks_per_seq;
   int len_cap;          // context lengths are clamped to [0, len_cap]
-  int chunk_blocks;     // fixed chunk length in blocks (even), or 0: balanced over total_waves
-  int total_waves;      // waves launched (4 per workgroup); chunk c is wave c's
+  int chunk_blocks;     // fixed chunk length in blocks, or 0: balanced over total_waves
+  int total_waves;      // waves launched (kWaves per workgroup); chunk c is wave c's
   float qk_scale_log2;  // scale * log2(e)
 };
 
@@ -99,12 +102,15 @@ constexpr int kMaxSharedBlocks = 256; // longest shared prefix taken (blocks)
 
 // Groups have at least two members and tiles at least two columns of members, so a batch of n
 // sequences makes at most floor(2n/3) tiles (groups of three, two tiles each, are the worst case).
-inline int plan_tiles_of(int batch) { return 2 * batch / 3 > 0 ? 2 * batch / 3 : 1; }
+__host__ __device__ inline int plan_tiles_of(int batch) {
+  return 2 * batch / 3 > 0 ? 2 * batch / 3 : 1;
+}
 // A saved unit: lead sequence, shared blocks [j0, j1), KV head, part index, then the member
 // sequence of each of the 16 tile slots (-1: none).
 constexpr int kUnitRec = 24;
 constexpr int kUnitMembers = 8;       // offset of the member slots in a record
-constexpr int kUnitHead = 64;         // ints before the first record (the count, padding)
+constexpr int kUnitHead = 64;         // ints before the first record: the count, the signature
+                                      // and its complement, padding
 inline int prefix_parts_of(int max_blocks_per_seq) {
   const int m = max_blocks_per_seq < kMaxSharedBlocks ? max_blocks_per_seq : kMaxSharedBlocks;
   return (m + kUnitBlocks - 1) / kUnitBlocks;
@@ -167,7 +173,7 @@ struct MultiArgs {
   int max_query_len;           // query counts are clamped to [0, max_query_len]
   int tiles_per_head;          // ceil(max_query_len * group / 16)
   int num_parts;
-  int part_blocks;             // even
+  int part_blocks;             // blocks per key partition (even unless partition_tokens fixes it)
   long long total_items;
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
   // Balanced split (multi_split_kernel): split_rt > 0 row tiles per head.
@@ -208,7 +214,7 @@ inline int split_chunk_waves(int tiles) { return tiles > 2 ? 2 : 1; }
 constexpr long kMaxSplitWorkgroups = 512;
 
 // Key partitions for `base` independent units so that about `target` units run, each at least
-// kMultiMinPartBlocks blocks long; part_blocks is even.
+// kMultiMinPartBlocks blocks long; part_blocks is even unless partition_tokens fixes it.
 inline void multi_parts(MultiPlan& p, long long base, long long target, long long maxblk,
                         int partition_tokens) {
   long long pb;

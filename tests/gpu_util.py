@@ -3,6 +3,7 @@ C ABI binding, and compare with the fp64 oracle under the stated tolerance."""
 
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -71,26 +72,52 @@ def oracle_after_append(wl):
 
 
 def half_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Half the spacing of the output format's values at |ref| (normal range)."""
+    mant = 7 if dtype == "bf16" else 10
+    _, ex = np.frexp(np.abs(ref))                  # |ref| = m * 2^ex, m in [0.5, 1)
+    return np.where(ref != 0, np.ldexp(1.0, ex - 1 - mant - 1), 0.0)
+
+
+def nearest_gap(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """|ref - RNE(ref)|: how far the closest value of the output format lies from ref.  The
+    scaling by a power of two is exact, so this is exact in float64 (normal range)."""
     mant = 7 if dtype == "bf16" else 10
     a = np.abs(ref)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    return np.where(a > 0, 2.0 ** (e - mant - 1), 0.0)
+    _, ex = np.frexp(a)
+    spacing = np.ldexp(1.0, ex - 1 - mant)
+    return np.where(a > 0, np.abs(a - np.round(a / spacing) * spacing), 0.0)
 
 
-def assert_close(out_bits: np.ndarray, ref: np.ndarray, dtype: str, label: str = ""):
-    """|gpu - ref| <= 2e-3 + 2e-3 |ref| against the unrounded fp64 reference.  An element that
-    misses that bound only because the output format cannot hold ref more closely (within half
-    an output ulp, plus fp32 slack) is counted as rounding-limited instead of failing."""
+# Every comparison made in this session: one record per assert_close call, reported in the
+# pytest terminal summary (tests/conftest.py).
+RECORDS: list = []
+
+
+def assert_close(out_bits: np.ndarray, ref: np.ndarray, dtype: str, label: str = "",
+                 relief: bool = False):
+    """Every element must satisfy |gpu - ref| <= 2e-3 + 2e-3 |ref| against the unrounded fp64
+    reference.
+
+    relief=True is for named short-context edge cases only: with a window of a few keys an
+    output can land where the output format itself cannot meet that bound (bf16 half-spacing
+    exceeds it for |ref| in about [2, 2.9) and [4, 6.8)).  Such an element passes, and is counted
+    as rounding-limited, only if the value of the format closest to ref is itself outside the
+    bound and the GPU result is within half a spacing of ref (plus fp32 slack).  Without relief
+    the count must be zero."""
     got = oracle.to_f64(out_bits, dtype)
     assert got.shape == ref.shape
     err = np.abs(got - ref)
     bound = ATOL + RTOL * np.abs(ref)
     ok = err <= bound
-    rounding = ~ok & (err <= half_ulp(ref, dtype) + 1e-5 * np.abs(ref) + 1e-7)
-    bad = ~(ok | rounding)
+    unattainable = nearest_gap(ref, dtype) > bound
+    rounding = ~ok & unattainable & (err <= half_ulp(ref, dtype) + 1e-5 * np.abs(ref) + 1e-7)
+    bad = ~ok if not relief else ~(ok | rounding)
     rel = err / np.maximum(np.abs(ref), 1e-3)
     stats = dict(max_abs=float(err.max(initial=0)), max_rel=float(rel.max(initial=0)),
-                 rounding_limited=int(rounding.sum()), n=int(err.size))
+                 rounding_limited=int(rounding.sum()), unattainable=int(unattainable.sum()),
+                 n=int(err.size), relief=relief)
+    RECORDS.append(dict(stats, label=label,
+                        test=os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]))
     print(f"[parity] {label} {stats}", file=sys.stderr, flush=True)
     if bad.any():
         idx = np.argwhere(bad)[:5]

@@ -60,8 +60,9 @@ def _decode(desc, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, tab=FAKE, lens=FAKE,
     (dict(num_q_heads=7), pa.PA_ERR_INVALID_ARG),          # not a multiple of kv heads
     (dict(num_q_heads=34), pa.PA_ERR_UNSUPPORTED),         # group of 17
     (dict(batch=0), pa.PA_ERR_INVALID_ARG),
-    (dict(partition_tokens=48), pa.PA_ERR_INVALID_ARG),    # not a multiple of 32
-    (dict(partition_tokens=65568), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=40), pa.PA_ERR_INVALID_ARG),    # not a multiple of 16
+    (dict(partition_tokens=8), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=65552), pa.PA_ERR_INVALID_ARG),
     (dict(q_dtype=pa.PA_FP8_E4M3), pa.PA_ERR_UNSUPPORTED),
     (dict(kv_dtype=pa.PA_F16), pa.PA_ERR_UNSUPPORTED),     # bf16 q with f16 cache
     (dict(kv_dtype=7), pa.PA_ERR_INVALID_ARG),
@@ -89,6 +90,25 @@ def _r(x):
 
 
 COUNTERS = 65536 * 4
+
+
+def test_partitions_are_whole_blocks():
+    """partition_tokens may be any multiple of the 16-token block: 48 tokens (3 blocks) gives
+    ceil(56 / 3) = 19 chunks of the 56-block space -> 24 chunk slots (3 workgroups of 8)."""
+    d = _desc(max_context_len=100, partition_tokens=48)
+    wgs = 3
+    assert pa.pa_decode_workspace_size(d) == \
+        COUNTERS + _r(wgs * 2 * 4 * 64 * 4) + _r(wgs * 2 * 4 * 2 * 4)
+    for P in (16, 48, 80, 65536):
+        assert pa.pa_decode_workspace_size(_desc(partition_tokens=P)) > 0
+    for P in (16, 48, 80):
+        assert pa.pa_decode_multi_workspace_size(_mdesc(partition_tokens=P)) > 0
+    # one partition covers every head: nothing to merge, no workspace
+    assert pa.pa_decode_multi_workspace_size(_mdesc(partition_tokens=65536)) == 0
+    # 16-token partitions of 8 blocks per sequence: 8 partitions per row
+    rows = 16 * 8 * 8
+    assert pa.pa_decode_multi_workspace_size(_mdesc(partition_tokens=16)) == \
+        _r(65536 * 4) + _r(rows * 64 * 4) + _r(rows * 2 * 4)
 
 
 def test_workspace_size_and_check():
@@ -248,8 +268,11 @@ def test_multi_workspace_size():
     (dict(total_queries=-1), pa.PA_ERR_INVALID_ARG),
     (dict(batch=0), pa.PA_ERR_INVALID_ARG),
     (dict(num_q_heads=7), pa.PA_ERR_INVALID_ARG),
-    (dict(partition_tokens=48), pa.PA_ERR_INVALID_ARG),
-    (dict(partition_tokens=65536 + 32), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=40), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=65536 + 16), pa.PA_ERR_INVALID_ARG),
+    # the balanced split indexes the flattened (sequence, KV head, block) space in 32 bits
+    (dict(batch=65536, num_kv_heads=16, num_q_heads=64, max_blocks_per_seq=2048),
+     pa.PA_ERR_UNSUPPORTED),
     (dict(q_dtype=pa.PA_FP8_E4M3), pa.PA_ERR_UNSUPPORTED),
     (dict(head_dim=80), pa.PA_ERR_UNSUPPORTED),
     (dict(kv_dtype=pa.PA_F16), pa.PA_ERR_UNSUPPORTED),

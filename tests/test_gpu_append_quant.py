@@ -167,4 +167,5 @@ def test_decode_after_quantised_append(src, first):
     torch.cuda.synchronize()
     ref = oracle.decode(wl.q, rk, rv, wl.block_tables, wl.context_lens, wl.scale, spec.q_dtype,
                         spec.kv_dtype, rks, rvs)
-    assert_close(host_bits(out), ref, spec.q_dtype, f"decode {src} first={first}")
+    # contexts of 1 and 16 tokens: outputs of one or a few rows (counted rounding-limited relief)
+    assert_close(host_bits(out), ref, spec.q_dtype, f"decode {src} first={first}", relief=True)

@@ -57,7 +57,8 @@ def test_fused_equals_append_then_decode(case):
     split.append()
     out_split = split.decode(partition_tokens=P, shared_prefixes=share)
     assert np.array_equal(out_fused, out_split)
-    assert_close(out_fused, ref, qd, label=f"fused {case}")
+    # the edge lengths start at 0 and 1 (counted rounding-limited relief)
+    assert_close(out_fused, ref, qd, label=f"fused {case}", relief=True)
 
 
 @pytest.mark.parametrize("kvd", ["bf16", "fp8_e4m3"])
@@ -78,7 +79,8 @@ def test_dense_appends(kvd):
     split = Dev(wl)
     split.append()
     assert np.array_equal(out_fused, split.decode())
-    assert_close(out_fused, ref, "bf16", label=f"dense appends {kvd}")
+    # contexts of 1 to 39 tokens (counted rounding-limited relief)
+    assert_close(out_fused, ref, "bf16", label=f"dense appends {kvd}", relief=True)
 
 
 def test_block_outside_the_pool_is_not_written():

@@ -73,7 +73,8 @@ def test_multi_layer_step_replays_bitwise():
         s = ly.wl.spec
         ref = oracle.decode(ly.wl.q, k, v, ly.wl.block_tables, ly.wl.context_lens, ly.wl.scale,
                             s.q_dtype, s.kv_dtype, ly.wl.k_scale, ly.wl.v_scale)
-        assert_close(o, ref, s.q_dtype, f"eager {s.name}")
+        # the layers hold contexts of 1, 2 and 5 tokens (counted rounding-limited relief)
+        assert_close(o, ref, s.q_dtype, f"eager {s.name}", relief=True)
 
     graph = pa.StepGraph(calls, stream)
     for rep in range(3):

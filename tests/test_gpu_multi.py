@@ -59,14 +59,19 @@ class Multi:
                                    wl.context_lens, wl.scale, s.q_dtype, s.kv_dtype, wl.k_scale,
                                    wl.v_scale)
 
-    def check(self, got, label, ref=None):
+    def check(self, got, label, ref=None, relief=False):
         n = int(self.qs[-1])
         ref = self.reference() if ref is None else ref
-        assert_close(got[:n], ref, self.spec.q_dtype, label)
+        assert_close(got[:n], ref, self.spec.q_dtype, label, relief=relief)
         assert np.all(got[n:] == SENTINEL[self.spec.q_dtype]), f"{label}: unowned rows written"
 
 
 LENS = (1, 2, 5, 16, 17, 33, 64, 100, 257, 700, 1023, 2049)
+# The small shapes put query rows at the very start of a context, where a row sees one to a few
+# keys and its output is an average of that many N(0,1) values: bf16 cannot then always hold the
+# result within 2e-3 + 2e-3 |ref|, so those comparisons allow the counted rounding-limited
+# elements (see gpu_util.assert_close).  Full-size batches are compared without it.
+SHORT_WINDOWS = True
 DRAFT = (1, 2, 5, 4, 8, 3, 0, 8, 7, 4, 6, 5)       # 2 queries with a 1-token context; one empty
 
 VERIFY = [
@@ -84,21 +89,22 @@ VERIFY = [
 
 
 @pytest.mark.parametrize("case", VERIFY, ids=lambda c: f"{c[0]}-{c[1]}-kv{c[2]}g{c[3]}d{c[4]}")
-@pytest.mark.parametrize("P", [0, 32, 256])
+@pytest.mark.parametrize("P", [0, 32, 48, 256])
 def test_speculative_verification(case, P):
     qd, kvd, hkv, g, d = case
     m = Multi(qd, kvd, hkv, g, d, LENS, DRAFT, seed=90 + VERIFY.index(case), spare_rows=3)
-    m.check(m.run(partition_tokens=P), f"verify {case} P{P}")
+    m.check(m.run(partition_tokens=P), f"verify {case} P{P}", relief=SHORT_WINDOWS)
 
 
 @pytest.mark.parametrize("qd,kvd,g,P", [("bf16", "bf16", 4, 0), ("bf16", "bf16", 4, 512),
-                                        ("f16", "f16", 1, 0), ("bf16", "fp8_e4m3", 8, 0)])
+                                        ("f16", "f16", 1, 0), ("bf16", "fp8_e4m3", 8, 0),
+                                        ("bf16", "bf16", 4, 80)])
 def test_prefill_chunks_of_512(qd, kvd, g, P):
     """Chunks of 512 tokens: the first chunk of a prompt (the chunk is the whole context), later
     chunks of long prompts, and a short last chunk."""
     lens, T = (512, 1100, 2048, 1700), (512, 512, 512, 188)
     m = Multi(qd, kvd, 2, g, 128, lens, T, seed=100)
-    m.check(m.run(partition_tokens=P), f"prefill g{g} P{P}")
+    m.check(m.run(partition_tokens=P), f"prefill g{g} P{P}", relief=SHORT_WINDOWS)
 
 
 CHUNK = [
@@ -120,7 +126,7 @@ def test_prefill_chunk_shapes(case, fp8):
     qd, hkv, g, d, lens, T = case
     kv = "fp8_e4m3" if fp8 else qd
     m = Multi(qd, kv, hkv, g, d, lens, T, seed=110 + CHUNK.index(case), spare_rows=2)
-    m.check(m.run(), f"chunk {case} {kv}")
+    m.check(m.run(), f"chunk {case} {kv}", relief=SHORT_WINDOWS)
 
 
 SPLIT = [
@@ -152,7 +158,7 @@ def test_balanced_split_shapes(case):
     qd, kvd, hkv, g, d, tmax = case
     T = tuple(min(t, tmax) for t in DRAFT)
     m = Multi(qd, kvd, hkv, g, d, LENS, T, seed=120 + SPLIT.index(case), spare_rows=3)
-    m.check(m.run(), f"split {case}")
+    m.check(m.run(), f"split {case}", relief=SHORT_WINDOWS)
 
 
 def test_more_queries_than_context_and_loose_bounds():
@@ -160,8 +166,9 @@ def test_more_queries_than_context_and_loose_bounds():
     m = Multi("bf16", "bf16", 2, 4, 128, (3, 1, 40), (6, 4, 2), seed=101, spare_rows=2)
     ref = m.reference()
     assert np.all(ref[0:3] == 0) and np.all(ref[6:9] == 0)
-    m.check(m.run(), "tight", ref)
-    m.check(m.run(max_query_len=64, max_context_len=4096), "loose", ref)
+    m.check(m.run(), "tight", ref, relief=SHORT_WINDOWS)
+    m.check(m.run(max_query_len=64, max_context_len=4096), "loose", ref,
+            relief=SHORT_WINDOWS)
 
 
 def test_repeat_runs_bitwise_identical():
@@ -171,63 +178,42 @@ def test_repeat_runs_bitwise_identical():
         assert np.array_equal(m.run(partition_tokens=64), first)
 
 
-def _sampled(m, rows_per_seq, rng):
-    """Sampled rows against the single-query oracle decode at each row's position (the pinned
-    equivalence of the two), for sizes where the full oracle would be slow."""
-    wl, s = m.wl, m.spec
-    got = m.run()
-    for b in range(s.batch):
-        T, L = int(m.T[b]), int(wl.context_lens[b])
-        if T == 0:
-            continue
-        for i in sorted(set(rng.integers(0, T, size=rows_per_seq).tolist()) | {0, T - 1}):
-            n = int(m.qs[b]) + i
-            ctx = np.array([min(max(L - T + i + 1, 0), L)], dtype=np.int32)
-            ref = oracle.decode(m.q[n][None], m.k, m.v, wl.block_tables[b:b + 1], ctx, wl.scale,
-                                s.q_dtype, s.kv_dtype, wl.k_scale, wl.v_scale)
-            assert_close(got[n][None], ref, s.q_dtype, f"seq {b} row {i}")
-
-
 def test_full_size_verification_batch():
-    """64 sequences of 128..8192 tokens, GQA 64/8, 4 draft tokens each (sampled rows)."""
+    """64 sequences of 128..8192 tokens, GQA 64/8, 4 draft tokens each: every row."""
     rng = np.random.default_rng(103)
     lens = rng.integers(128, 8192, size=64, endpoint=True)
     m = Multi("bf16", "bf16", 8, 8, 128, lens, [4] * 64, seed=103)
-    _sampled(m, 2, rng)
+    m.check(m.run(), "full-size verification")
 
 
 def test_full_size_prefill_chunk():
-    """4 prompts whose last 512-token chunk runs against 4096 cached tokens (sampled rows)."""
-    rng = np.random.default_rng(104)
+    """4 prompts whose last 512-token chunk runs against 4096 cached tokens: every row."""
     m = Multi("bf16", "bf16", 8, 4, 128, [4608] * 4, [512] * 4, seed=104)
-    _sampled(m, 6, rng)
+    m.check(m.run(), "full-size prefill chunk")
 
 
 def test_full_size_fp8_verification():
     """4 sequences of 32768 fp8 tokens, GQA 64/8, 4 draft tokens each: two row tiles per head in
-    one wave (sampled rows)."""
-    rng = np.random.default_rng(105)
+    one wave; every row."""
     m = Multi("bf16", "fp8_e4m3", 8, 8, 128, [32768] * 4, [4] * 4, seed=105)
-    _sampled(m, 2, rng)
+    m.check(m.run(), "full-size fp8 verification")
 
 
 @pytest.mark.parametrize("kvd", ["bf16", "fp8_e4m3"])
 def test_full_size_wide_verification(kvd):
     """4 sequences of 32768 tokens, GQA 64/8, 8 draft tokens each: four row tiles per head in
-    two waves a chunk (sampled rows)."""
-    rng = np.random.default_rng(108)
+    two waves a chunk; every row."""
     m = Multi("bf16", kvd, 8, 8, 128, [32768] * 4, [8] * 4, seed=108)
-    _sampled(m, 2, rng)
+    m.check(m.run(), f"full-size wide verification {kvd}")
 
 
 @pytest.mark.parametrize("kvd,T", [("fp8_e4m3", 4), ("bf16", 2), ("bf16", 4), ("fp8_e4m3", 6),
                                    ("bf16", 8)])
-def test_one_head_over_many_workgroups(kvd, T):
+def test_full_size_one_head_over_many_workgroups(kvd, T):
     """One KV head of 65536 tokens: two-block chunks, so its parts come from hundreds of
-    workgroups and are merged in LDS-staged batches (sampled rows)."""
-    rng = np.random.default_rng(106)
+    workgroups and are merged in LDS-staged batches; every row."""
     m = Multi("bf16", kvd, 1, 8, 128, [65536], [T], seed=106)
-    _sampled(m, 2, rng)
+    m.check(m.run(), f"one head {kvd} T{T}")
 
 
 def test_one_workspace_serves_every_entry_point():
@@ -253,9 +239,11 @@ def test_one_workspace_serves_every_entry_point():
                 pa.pa_decode(qd, kd, vd, tables, lens, float(wl.scale), out, k_scale=ks,
                              v_scale=vs)
                 torch.cuda.synchronize()
-                assert_close(host_bits(out), ref[last], s.q_dtype, f"decode after {order}")
+                assert_close(host_bits(out), ref[last], s.q_dtype, f"decode after {order}",
+                             relief=SHORT_WINDOWS)
             else:
-                m.check(m.run(partition_tokens=step), f"multi P{step} in {order}", ref)
+                m.check(m.run(partition_tokens=step), f"multi P{step} in {order}", ref,
+                        relief=SHORT_WINDOWS)
 
 
 RANDOM = [
@@ -284,4 +272,4 @@ def test_random_split_batches(case):
     T = rng.integers(0, tmax + 1, size=B)
     m = Multi(qd, kvd, hkv, g, d, [int(x) for x in lens], [int(x) for x in T], seed=seed,
               spare_rows=2)
-    m.check(m.run(), f"random {case}")
+    m.check(m.run(), f"random {case}", relief=SHORT_WINDOWS)

@@ -97,7 +97,8 @@ def test_continuous_batching_with_forks(dt):
         k, v = oracle.kv_append(k, v, kn, vn, np.array(slots))
         assert np.array_equal(host_bits(kd), k) and np.array_equal(host_bits(vd), v), step
         ref = oracle.decode(qb, k, v, tab, lens, scale, dt, dt)
-        assert_close(host_bits(out), ref, dt, f"step {step} ({B} sequences)")
+        # a request arrives with a 1-token prompt (counted rounding-limited relief)
+        assert_close(host_bits(out), ref, dt, f"step {step} ({B} sequences)", relief=True)
 
         # finished requests give their blocks back
         for seq in [s for s in live if s[2] == 1]:

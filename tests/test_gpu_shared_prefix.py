@@ -139,11 +139,57 @@ def test_plan_not_taken_is_the_unshared_path(g, batch):
     assert np.array_equal(on, off)
 
 
+def _abi_decode(dev, mode, ws, partition=0):
+    """pa_decode through the C ABI itself (none of the binding's bookkeeping), with
+    shared_prefixes = mode and the given workspace."""
+    import ctypes
+
+    import paged_kv_cache_31_amd as pa
+
+    def ptr(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    desc = pa.decode_desc(dev.q, dev.k_cache, dev.tables, 0, partition, mode)
+    st = pa.lib().pa_decode(ctypes.byref(desc), ptr(dev.q), ptr(dev.k_cache), ptr(dev.v_cache),
+                            ptr(dev.k_scale), ptr(dev.v_scale), ptr(dev.tables), ptr(dev.lens),
+                            ctypes.c_float(float(dev.wl.scale)), ptr(dev.out), ptr(ws),
+                            ctypes.c_size_t(ws.numel()),
+                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == pa.PA_OK, pa.status_string(st)
+    torch.cuda.synchronize()
+    return host_bits(dev.out)
+
+
+def _layer(wl, k, v, tables):
+    s = wl.spec
+    dev = Dev(wl)
+    dev.k_cache, dev.v_cache = dev_bits(k, s.kv_dtype), dev_bits(v, s.kv_dtype)
+    dev.tables = torch.from_numpy(np.ascontiguousarray(tables)).cuda()
+    return dev
+
+
+def _grouped_tables(wl):
+    t = wl.block_tables.copy()
+    _share(t, 1, (2, 3, 5, 8, 11, 14), 40)
+    t[11, 33:40] = t[9, 33:40]
+    _share(t, 9, (10,), 40)
+    _share(t, 6, (7,), 3)
+    return t
+
+
+def _workspace(dev, extra=0):
+    import paged_kv_cache_31_amd as pa
+    need = max(pa.pa_decode_workspace_size(pa.decode_desc(dev.q, dev.k_cache, dev.tables, 0, P, 1))
+               for P in (0, 128))
+    return pa.new_workspace(max(need, extra), dev.q.device)
+
+
 @pytest.mark.parametrize("kvd", ["bf16", "fp8_e4m3"])
 def test_layers_reuse_the_plan(kvd):
     """The layers of one step read the same tables and lengths: the first call plans the groups
     (shared_prefixes 1), the next ones reuse its saved units (2) with their own queries and K/V
-    (another layer's cache), and give bitwise what a planning call gives."""
+    (another layer's cache), and give bitwise what a planning call gives.  Through the C ABI, so
+    that the reusing calls really take the saved plan."""
     import copy
     wl0, k0, v0 = _setup("bf16", kvd, 2, 4, 128, LENS, seed=76)
     # another layer over the same blocks: other queries, K with its sign bits flipped, V
@@ -153,34 +199,118 @@ def test_layers_reuse_the_plan(kvd):
     sign = np.uint8(0x80) if kvd == "fp8_e4m3" else np.uint16(0x8000)
     k1 = k0 ^ sign
     v1 = np.ascontiguousarray(v0[:, :, ::-1, :])
-    t = wl0.block_tables.copy()
-    _share(t, 1, (2, 3, 5, 8, 11, 14), 40)
-    t[11, 33:40] = t[9, 33:40]
-    _share(t, 9, (10,), 40)
-    _share(t, 6, (7,), 3)
-    first = _run(wl0, k0, v0, t, f"layer 0 plans ({kvd})", share=1)
-    reused = _run(wl1, k1, v1, t, f"layer 1 reuses ({kvd})", share=2)
-    again = _run(wl0, k0, v0, t, f"layer 0 reuses ({kvd})", share=2)
+    t = _grouped_tables(wl0)
+    dev0, dev1 = _layer(wl0, k0, v0, t), _layer(wl1, k1, v1, t)
+    ws = _workspace(dev0)
+    first = _abi_decode(dev0, 1, ws)
+    reused = _abi_decode(dev1, 2, ws)
+    again = _abi_decode(dev0, 2, ws)
     assert np.array_equal(again, first)
-    planned = _run(wl1, k1, v1, t, f"layer 1 plans ({kvd})", share=1)
+    planned = _abi_decode(dev1, 1, ws)
     assert np.array_equal(reused, planned)
+    s = wl1.spec
+    ref = oracle.decode(wl1.q, k1, v1, t, wl1.context_lens, wl1.scale, s.q_dtype, s.kv_dtype,
+                        wl1.k_scale, wl1.v_scale)
+    assert_close(reused, ref, s.q_dtype, f"layer 1 reuses ({kvd})")
+    # with sharing on, the plan is really taken: the result differs from the unshared path
+    off = _abi_decode(dev1, 0, _workspace(dev1))
+    assert not np.array_equal(reused, off)
 
 
 def test_reuse_on_a_fresh_workspace_is_the_unshared_path():
     """shared_prefixes 2 on a zero-filled workspace that no planning call has written reads no
     shared blocks: bitwise the output with shared prefixes off."""
-    import paged_kv_cache_31_amd as pa
     wl, k, v = _setup("bf16", "bf16", 2, 4, 128, LENS, seed=78)
     t = wl.block_tables.copy()
     _share(t, 1, (2, 3, 5, 8, 11, 14), 40)
-    off = _run(wl, k, v, t, "off", share=False)
+    dev = _layer(wl, k, v, t)
+    off = _abi_decode(dev, 0, _workspace(dev))
+    assert np.array_equal(_abi_decode(dev, 2, _workspace(dev)), off)
+
+
+def test_reuse_after_the_workspace_was_overwritten():
+    """A reusing call whose workspace another call has written since the planning call (here:
+    pa_decode_multi, whose scratch overlaps the saved plan, and then random bytes over all of
+    the workspace but its arrival counters) finds a foreign signature and runs unshared; a
+    changed descriptor (another max_context_len) is refused the same way.  Through the C ABI:
+    the kernels alone must keep every access in bounds and the result right."""
+    import ctypes
+
+    import paged_kv_cache_31_amd as pa
+    wl, k, v = _setup("bf16", "bf16", 2, 4, 128, LENS, seed=79)
+    t = _grouped_tables(wl)
+    dev = _layer(wl, k, v, t)
     s = wl.spec
-    dev = Dev(wl)
-    dev.k_cache, dev.v_cache = dev_bits(k, s.kv_dtype), dev_bits(v, s.kv_dtype)
-    dev.tables = torch.from_numpy(np.ascontiguousarray(t)).cuda()
-    desc = pa.decode_desc(dev.q, dev.k_cache, dev.tables, 0, 0, 2)
-    ws = pa.new_workspace(pa.pa_decode_workspace_size(desc), dev.q.device)
-    pa.pa_decode(dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens, float(wl.scale), dev.out,
-                 workspace=ws, shared_prefixes=2)
+    ref = oracle.decode(wl.q, k, v, t, wl.context_lens, wl.scale, s.q_dtype, s.kv_dtype)
+    # a multi-query problem over the same cache: 4 rows per sequence, fixed partitions of 32
+    T = np.minimum(4, wl.context_lens).astype(np.int64)
+    qs = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    N = int(qs[-1])
+    qm = dev_bits(workloads.storage_bits(np.random.default_rng(5).standard_normal(
+        (N, s.num_q_heads, s.head_dim)), "bf16"), "bf16")
+    om = torch.empty_like(qm)
+    mdesc = pa.multi_desc(qm, dev.k_cache, dev.tables, 4, 0, 32)
+    need_m = pa.pa_decode_multi_workspace_size(mdesc)
+    ws = _workspace(dev, need_m)
+    planned = _abi_decode(dev, 1, ws)
+    off = _abi_decode(dev, 0, _workspace(dev))
+    assert not np.array_equal(planned, off)
+    qsd = torch.from_numpy(qs).cuda()
+
+    def p(x):
+        return ctypes.c_void_p(x.data_ptr())
+    st = pa.lib().pa_decode_multi(ctypes.byref(mdesc), p(qm), p(qsd), p(dev.k_cache),
+                                  p(dev.v_cache), None, None, p(dev.tables), p(dev.lens),
+                                  ctypes.c_float(float(wl.scale)), p(om), p(ws),
+                                  ctypes.c_size_t(ws.numel()),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == pa.PA_OK
     torch.cuda.synchronize()
-    assert np.array_equal(host_bits(dev.out), off)
+    got = _abi_decode(dev, 2, ws)
+    assert np.array_equal(got, off) or np.array_equal(got, planned)
+    assert_close(got, ref, s.q_dtype, "reuse after pa_decode_multi")
+    # random bytes over everything after the counters: the signature is foreign
+    _abi_decode(dev, 1, ws)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    ws[65536 * 4:] = torch.randint(0, 256, (ws.numel() - 65536 * 4,), dtype=torch.uint8,
+                                   device="cuda", generator=g)
+    assert np.array_equal(_abi_decode(dev, 2, ws), off)
+    # a planning call, then a reuse with another descriptor (fixed partitions of 128 tokens):
+    # the signature differs, so the call runs unshared
+    _abi_decode(dev, 1, ws)
+    assert np.array_equal(_abi_decode(dev, 2, ws, partition=128),
+                          _abi_decode(dev, 0, _workspace(dev), partition=128))
+
+
+def test_binding_plans_again_after_another_call():
+    """The binding's prepared calls keep the plan only while nothing else used the workspace:
+    planning call, reusing call (takes the plan), a multi-query call on the same workspace,
+    then the reusing call plans again (bitwise the planning output)."""
+    import paged_kv_cache_31_amd as pa
+    wl, k, v = _setup("bf16", "bf16", 2, 4, 128, LENS, seed=80)
+    t = _grouped_tables(wl)
+    dev = _layer(wl, k, v, t)
+    s = wl.spec
+    T = np.minimum(2, wl.context_lens).astype(np.int64)
+    qs = torch.from_numpy(np.concatenate([[0], np.cumsum(T)]).astype(np.int32)).cuda()
+    qm = dev.q[:0].new_empty((int(T.sum()), s.num_q_heads, s.head_dim)).fill_(0.5)
+    om = torch.empty_like(qm)
+    mdesc = pa.multi_desc(qm, dev.k_cache, dev.tables, 2, 0, 32)
+    ws = _workspace(dev, pa.pa_decode_multi_workspace_size(mdesc))
+    outs = [torch.empty_like(dev.out) for _ in range(3)]
+
+    def call(mode, out):
+        return pa.DecodeCall(dev.q, dev.k_cache, dev.v_cache, dev.tables, dev.lens,
+                             float(wl.scale), out, workspace=ws, shared_prefixes=mode)
+    plan, reuse_a, reuse_b = call(1, outs[0]), call(2, outs[1]), call(2, outs[2])
+    multi = pa.MultiCall(qm, qs, dev.k_cache, dev.v_cache, dev.tables, dev.lens, float(wl.scale),
+                         om, 2, partition_tokens=32, workspace=ws)
+    plan()
+    reuse_a()
+    multi()
+    reuse_b()
+    torch.cuda.synchronize()
+    assert reuse_a.reused and not reuse_b.reused
+    first = host_bits(outs[0])
+    assert np.array_equal(host_bits(outs[1]), first)
+    assert np.array_equal(host_bits(outs[2]), first)
