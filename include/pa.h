@@ -282,6 +282,26 @@ pa_status pa_decode_append(const pa_decode_desc* desc, const void* q, const void
                            const int32_t* block_tables, const int32_t* context_lens, float scale,
                            void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_noalloc -- pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The library keeps its own scratch, a static device array of 64 MiB
+ * (PA_NOALLOC_SCRATCH_BYTES) on every GPU it runs on, held until the process ends; it calls no
+ * hipMalloc, hipFree or other allocating routine.  Arguments, results and errors are those of
+ * pa_decode, plus: a descriptor whose workspace (pa_decode_workspace_size) exceeds 64 MiB returns
+ * PA_ERR_UNSUPPORTED before anything is launched (every decode descriptor without shared prefixes
+ * needs at most about 17 MiB; shared prefixes add batch * num_q_heads * P * (head_dim + 2) * 4
+ * bytes).  The first call on a device also enqueues on `stream` a small kernel that clears the
+ * scratch's arrival counters.  Every call on one GPU shares that GPU's scratch, which keeps the
+ * last call's contents: calls that overlap on one GPU (other streams, other threads) race, so the
+ * caller serialises them.  shared_prefixes 2 reuses a plan that the last pa_decode_noalloc call
+ * with 1 left in the scratch, under the rules of pa_decode_desc.
+ */
+pa_status pa_decode_noalloc(const pa_decode_desc* desc, const void* q, const void* k_cache,
+                            const void* v_cache, const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, void* out, void* stream);
+
 /* Bytes of workspace pa_decode needs for this descriptor, or 0 if the descriptor is invalid
  * (pa_decode reports why).  It depends only on the descriptor, not on the GPU:
  * 262144 + workgroups * 2 * group * (head_dim + 2) * 4 bytes (each part rounded up to 256),

@@ -64,6 +64,7 @@ _lib = None
 _lock = threading.Lock()
 
 EXPORTS = ("pa_kv_append", "pa_kv_append_quant", "pa_decode", "pa_decode_append",
+           "pa_decode_noalloc",
            "pa_decode_workspace_size", "pa_decode_multi", "pa_decode_multi_workspace_size",
            "pa_graph_begin", "pa_graph_end", "pa_graph_launch", "pa_graph_destroy",
            "pa_pool_create", "pa_pool_destroy", "pa_pool_free_blocks", "pa_pool_refcount",
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
             L.pa_decode_append.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp,
                                            vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
             L.pa_decode_append.restype = i32
+            L.pa_decode_noalloc.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp,
+                                            vp, ctypes.c_float, vp, vp]
+            L.pa_decode_noalloc.restype = i32
             L.pa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc)]
             L.pa_decode_workspace_size.restype = sz
             L.pa_decode_multi.argtypes = [ctypes.POINTER(MultiDesc), vp, vp, vp, vp, vp, vp, vp,
@@ -361,6 +365,29 @@ def pa_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_le
     DecodeCall(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                max_context_len, partition_tokens, workspace, stream, shared_prefixes, k_new,
                v_new)()
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale=None,
+                      v_scale=None, max_context_len=0, partition_tokens=0, stream=None,
+                      shared_prefixes=False) -> torch.Tensor:
+    """pa_decode with the library's own static scratch (no workspace, no allocation anywhere):
+    for code that must not allocate, e.g. under graph capture.  Calls on one GPU share that
+    scratch, so they must not overlap.  Returns out."""
+    for t in (q, k_cache, v_cache, block_tables, context_lens, out):
+        assert t.is_cuda and t.is_contiguous()
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert out.shape == q.shape and out.dtype == q.dtype
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_tokens,
+                       shared_prefixes)
+    st = lib().pa_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                 _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
+                                 _stream(stream))
+    _check("pa_decode_noalloc", st)
     return out
 
 

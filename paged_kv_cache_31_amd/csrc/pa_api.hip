@@ -12,6 +12,11 @@
 
 #define PA_EXPORT extern "C" __attribute__((visibility("default")))
 
+// Bytes of the static scratch behind pa_decode_noalloc, per GPU (see include/pa.h).
+#ifndef PA_NOALLOC_SCRATCH_BYTES
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#endif
+
 // Balanced mode launches this many waves per resident wave slot.
 #ifndef PA_WAVE_ROUNDS
 #define PA_WAVE_ROUNDS 1
@@ -428,11 +433,11 @@ PA_EXPORT size_t pa_decode_workspace_size(const pa_decode_desc* desc) {
 namespace {
 
 // pa_decode, and with k_new/v_new set, pa_decode_append.
-pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_new,
-                      const void* v_new, const void* k_cache, const void* v_cache,
-                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
-                      const int32_t* context_lens, float scale, void* out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+// Host-visible checks of a decode call's descriptor and pointers (the workspace aside).
+pa_status check_decode_args(const pa_decode_desc* desc, const void* q, const void* k_cache,
+                            const void* v_cache, const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const void* out) {
   pa_status s = check_decode_desc(desc);
   if (s != PA_OK) return s;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
@@ -444,6 +449,18 @@ pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_n
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
     return PA_ERR_INVALID_ARG;
   if (!fp8 && (k_scale || v_scale)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_new,
+                      const void* v_new, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  pa_status s = check_decode_args(desc, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                  context_lens, out);
+  if (s != PA_OK) return s;
+  const bool fp8 = desc->cache.kv_dtype == PA_FP8_E4M3;
 
   const size_t need = workspace_bytes_of(desc);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return PA_ERR_WORKSPACE;
@@ -552,6 +569,77 @@ PA_EXPORT pa_status pa_decode_append(const pa_decode_desc* desc, const void* q,
   if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return PA_ERR_INVALID_ARG;
   return decode_impl(desc, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
                      context_lens, scale, out, workspace, workspace_bytes, stream);
+}
+
+// ---- pa_decode_noalloc: pa_decode with the library's own scratch, for callers that cannot
+// allocate device memory.  The scratch is a static device array; each GPU the library runs on
+// holds its own copy (PA_NOALLOC_SCRATCH_BYTES) until the process ends.  In host code its name
+// stands for a host-side symbol, so its device address on each GPU is taken once with
+// hipGetSymbolAddress and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Zero-fills n 32-bit words (the arrival counters of a fresh scratch).
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;   // device -> the device address of `scratch` there
+
+// The scratch of the current device; its first use on a device also enqueues, on `stream`, the
+// clearing of the arrival counters (the decode kernels leave them at zero after every call).
+pa_status scratch_of_current_device(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) {
+    *ptr = it->second;
+    return PA_OK;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr) {
+    g_last_hip_error = (int32_t)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    return PA_ERR_HIP;
+  }
+  const int words = (int)(pa::kMaxWorkgroups * sizeof(int) / sizeof(uint32_t));
+  hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(p), words);
+  e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+  }
+  g_scratch[dev] = p;
+  *ptr = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_decode_noalloc(const pa_decode_desc* desc, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      float scale, void* out, void* stream) {
+  pa_status s = check_decode_args(desc, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                  context_lens, out);
+  if (s != PA_OK) return s;
+  if (workspace_bytes_of(desc) > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  s = scratch_of_current_device(static_cast<hipStream_t>(stream), &ws);
+  if (s != PA_OK) return s;
+  return decode_impl(desc, q, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
+                     block_tables, context_lens, scale, out, ws, PA_NOALLOC_SCRATCH_BYTES,
+                     stream);
 }
 
 // ---- HIP graphs of whole steps.  The entry points above enqueue kernels only (no allocation,

@@ -376,3 +376,23 @@ def test_pool_rejects_bad_arguments_from_c():
     finally:
         assert lib.pa_pool_destroy(p) == pa.PA_OK
     assert lib.pa_pool_destroy(None) == pa.PA_OK
+
+
+def test_noalloc_rejects_before_touching_the_gpu():
+    """pa_decode_noalloc validates like pa_decode and refuses a descriptor whose scratch needs
+    more than its 64 MiB, all before any HIP call (so on the CPU too)."""
+    lib = pa.lib()
+
+    def call(d, q=FAKE, ks=None):
+        return lib.pa_decode_noalloc(ctypes.byref(d) if d is not None else None, q, FAKE, FAKE,
+                                     ks, ks, FAKE, FAKE, 0.125, FAKE, None)
+
+    assert call(None) == pa.PA_ERR_INVALID_ARG
+    assert call(_desc(), q=None) == pa.PA_ERR_INVALID_ARG
+    assert call(_desc(head_dim=96)) == pa.PA_ERR_UNSUPPORTED
+    assert call(_desc(kv_dtype=pa.PA_FP8_E4M3)) == pa.PA_ERR_INVALID_ARG     # fp8 w/o scales
+    # shared prefixes for 1024 sequences x 128 query heads: ~545 MB of prefix partial results
+    big = _desc(batch=1024, num_q_heads=128, num_kv_heads=16, head_dim=128, num_blocks=1 << 20,
+                max_blocks_per_seq=256, shared_prefixes=1)
+    assert pa.pa_decode_workspace_size(big) > pa.NOALLOC_SCRATCH_BYTES
+    assert call(big) == pa.PA_ERR_UNSUPPORTED
