@@ -292,6 +292,98 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
   const int B = a.batch, Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = a.group;
   const int cap = a.len_cap;
 
+  if (a.head_mode > 0) {
+    // ---- Short heads (at most 2 * WPH blocks each): WPH waves per sequence head, wave k of a
+    // head taking its blocks [skip + 2k, skip + 2k + 2) as one step; the pieces of a head meet
+    // in LDS and its waves write it, each a share of the 16-dim tiles.  No scan of the lengths,
+    // nothing crosses workgroups.
+    const int WPH = a.head_mode;
+    const int hl = wave / WPH, k = wave - hl * WPH;
+    const int h = uniform(blockIdx.x * (kWaves / WPH) + hl);
+    int b = 0, kvh = 0, L = 0, nblk = 0, sk = 0;
+    if (h < B * Hkv) {
+      b = h / Hkv;
+      kvh = h - b * Hkv;
+      L = clamp_len(a.context_lens[b], cap);
+      nblk = blocks_of(L);
+      sk = skip_of(a, b, nblk);
+    }
+    const int j0 = min(sk + 2 * k, nblk), j1 = min(nblk, j0 + 2);
+    const int h0 = kvh * G;
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (j0 < j1) {
+      const St st(a, lane);
+      const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+      const int end_tok = j1 == nblk ? L : kBlock * j1;
+      const bool append = a.k_new != nullptr && j1 == nblk;
+      if (append) append_token<D, KVT>(a, b, kvh, trow[(L - 1) / kBlock], (L - 1) % kBlock, lane);
+      V8 qB[NC];
+      st.load_q(qB, col < G ? reinterpret_cast<const E*>(a.q) + ((size_t)b * Hq + h0 + col) * D
+                            : nullptr);
+      if (append && (unsigned)trow[(L - 1) / kBlock] < (unsigned)a.num_blocks) {
+        constexpr int EB = KVT == DT_FP8 ? 1 : 2;
+        VAppend ap;
+        ap.vnew = a.v_new + ((size_t)b * Hkv + kvh) * D * EB;
+        ap.blk = (L - 1) / kBlock;
+        ap.off = (L - 1) % kBlock;
+        st.run_append(qB, trow, kvh, j0, j1, end_tok, m_run, l_run, acc, true, ap);
+      } else {
+        st.run(qB, trow, kvh, j0, j1, end_tok, 0, 1, m_run, l_run, acc);
+      }
+      l_run = sum_across_rows(l_run);
+    }
+    const size_t row = (size_t)b * Hq + h0 + col;
+    E* out = reinterpret_cast<E*>(a.out) + row * D + 4 * grp;
+    if (WPH == 1) {
+      if (h < B * Hkv && col < G) {
+        if (nblk == 0) {
+#pragma unroll
+          for (int i = 0; i < NT; ++i) *reinterpret_cast<uint2*>(out + 16 * i) = make_uint2(0u, 0u);
+        } else {
+          if (sk > 0) fold_prefix<D>(a, row, prefix_parts(sk), grp, 0, 1, m_run, l_run, acc);
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+            *reinterpret_cast<uint2*>(out + 16 * i) =
+                make_uint2(pack2<QT>(acc[i][0] / l_run, acc[i][1] / l_run),
+                           pack2<QT>(acc[i][2] / l_run, acc[i][3] / l_run));
+        }
+      }
+      return;
+    }
+    if (grp == 0) {
+      sm_pm[wave][0][col] = m_run;
+      sm_pl[wave][0][col] = l_run;
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) sm_pacc[wave][0][i][lane] = acc[i];
+    __syncthreads();
+    if (h >= B * Hkv || col >= G) return;
+    const int w0 = hl * WPH;
+    for (int t = k; t < NT; t += WPH) {
+      if (nblk == 0) {
+        *reinterpret_cast<uint2*>(out + 16 * t) = make_uint2(0u, 0u);
+        continue;
+      }
+      // piece 0 has tokens (skip_of leaves at least one block), so the maximum is finite
+      float M_ = sm_pm[w0][0][col];
+      for (int i = 1; i < WPH; ++i) M_ = fmaxf(M_, sm_pm[w0 + i][0][col]);
+      float gl = 0.0f;
+      f32x4 go[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+      for (int i = 0; i < WPH; ++i) {
+        const float w = fast_exp2(sm_pm[w0 + i][0][col] - M_);
+        gl += w * sm_pl[w0 + i][0][col];
+        go[0] += w * sm_pacc[w0 + i][0][t][lane];
+      }
+      if (sk > 0) fold_prefix<D>(a, row, prefix_parts(sk), grp, t, 1, M_, gl, go);
+      *reinterpret_cast<uint2*>(out + 16 * t) =
+          make_uint2(pack2<QT>(go[0][0] / gl, go[0][1] / gl), pack2<QT>(go[0][2] / gl, go[0][3] / gl));
+    }
+    return;
+  }
+
   // ---- 1. Flattened block space and this workgroup's chunk starts.  A sequence head (b, kvh)
   // takes its blocks [skip_b, blocks(L_b)) there.  Thread t owns sequences [t*per, t*per + per);
   // W = sum_b Hkv * (blocks(L_b) - skip_b).

@@ -467,7 +467,17 @@ pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_n
 
   const int64_t cap_chunks = chunk_capacity(desc);
   int64_t waves = cap_chunks;
-  if (desc->partition_tokens == 0) {
+  // Short heads: WPH waves per head, one step each, when every head fits the resident waves.
+  const int64_t heads = (int64_t)desc->batch * desc->cache.num_kv_heads;
+  const int max_blocks = (len_cap(desc) + pa::kBlock - 1) / pa::kBlock;
+  int wph = 1;
+  while (2 * wph < max_blocks) wph *= 2;
+  const bool head_mode = desc->partition_tokens == 0 && max_blocks <= pa::kHeadModeBlocks &&
+                         heads * wph <= resident_waves(desc);
+  if (head_mode) {
+    waves = (heads * wph + pa::kWaves - 1) / pa::kWaves * pa::kWaves;
+    if (waves < pa::kWaves) waves = pa::kWaves;
+  } else if (desc->partition_tokens == 0) {
     const int64_t resident = resident_waves(desc) * PA_WAVE_ROUNDS;
     if (resident > 0 && resident < waves) waves = resident / pa::kWaves * pa::kWaves;
     if (waves < pa::kWaves) waves = pa::kWaves;
@@ -506,6 +516,7 @@ pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_n
   a.len_cap = len_cap(desc);
   a.chunk_blocks = desc->partition_tokens / pa::kBlock;
   a.total_waves = (int)waves;
+  a.head_mode = head_mode ? wph : 0;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
 
   // prefix workgroups: one per resident slot, never more than the plan can have units
@@ -523,7 +534,7 @@ pa_status decode_impl(const pa_decode_desc* desc, const void* q, const void* k_n
   // own costs (measured: 256 sequences x 8 KV heads on 2048 waves, 232.7 us fused against
   // 224.2 us with the separate append; 512 appends on 2048 waves, fused equal or faster).
   hipError_t e = hipSuccess;
-  if (k_new && (int64_t)desc->batch * desc->cache.num_kv_heads >= waves) {
+  if (k_new && !head_mode && heads >= waves) {
     pa::LastAppendArgs ap;
     ap.k_new = a.k_new;
     ap.v_new = a.v_new;

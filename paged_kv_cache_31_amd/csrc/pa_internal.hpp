@@ -89,8 +89,15 @@ struct DecodeArgs {
   int len_cap;          // context lengths are clamped to [0, len_cap]
   int chunk_blocks;     // fixed chunk length in blocks, or 0: balanced over total_waves
   int total_waves;      // waves launched (kWaves per workgroup); chunk c is wave c's
+  int head_mode;        // 0, or WPH (1, 2, 4 or 8): short heads, WPH waves per sequence head
+                        // in head order, each wave one step of its head (no scan, nothing
+                        // crosses workgroups)
   float qk_scale_log2;  // scale * log2(e)
 };
+
+// Head mode: with no fixed partition and every head at most 2 * kWaves blocks, when the heads
+// fit the resident waves at WPH = (blocks / 2 rounded up to a power of two) waves each.
+constexpr int kHeadModeBlocks = 2 * kWaves;
 
 // Shared prefixes.  Sequences whose block tables start with the same physical blocks are
 // grouped; each group is cut into tiles of up to 16/group members (one MFMA column per query

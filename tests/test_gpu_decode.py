@@ -160,6 +160,82 @@ def test_length_zero_gives_zeros():
     assert_close(out, ref, "bf16", "zero-length batch")
 
 
+# Heads of at most 16 blocks that fit the resident waves take the head mode: 1, 2, 4 or 8
+# waves per sequence head (blocks / 2 rounded up to a power of two), one 32-token step each,
+# the pieces of a head merged in LDS.  Lengths by waves per head, each set with an empty
+# sequence, single tokens and block edges.
+SHORT_LENS = {1: (1, 0, 32, 20, 17), 2: (33, 64, 0, 1, 50), 4: (100, 7, 128, 0, 65, 16),
+              8: (256, 1, 0, 129, 200, 17, 240, 255)}
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype,hkv,g,d", [("bf16", "bf16", 2, 8, 128),
+                                                      ("f16", "f16", 4, 1, 64),
+                                                      ("bf16", "fp8_e4m3", 2, 4, 128),
+                                                      ("f16", "fp8_e4m3", 1, 16, 64)])
+@pytest.mark.parametrize("wph", [1, 2, 4, 8])
+def test_short_heads(q_dtype, kv_dtype, hkv, g, d, wph):
+    """Short heads: decode and the fused step against the oracle; rows of an empty sequence are
+    zeros; the fused append leaves the caches of the separate append and the same output."""
+    lens = SHORT_LENS[wph]
+    spec = Spec("short", len(lens), hkv * g, hkv, d, q_dtype, kv_dtype, ("list", lens),
+                pool=("times", 2), seed=50 + wph)
+    wl = workloads.make(spec)
+    assert wl.max_context_len <= 16 * 2 * wph
+    dev = Dev(wl)
+    dev.out.fill_(float("nan"))
+    dev.append()
+    out = dev.decode(partition_tokens=0)
+    ref, k_ref, v_ref = oracle_after_append(wl)
+    assert_close(out, ref, q_dtype, f"short heads wph={wph}", relief=kv_dtype == "fp8_e4m3")
+    for b in np.flatnonzero(wl.context_lens == 0):
+        assert (out[b] == 0).all()
+    fused = Dev(wl)
+    fused.out.fill_(float("nan"))
+    pa.pa_decode_append(fused.q, fused.k_new, fused.v_new, fused.k_cache, fused.v_cache,
+                        fused.tables, fused.lens, float(wl.scale), fused.out,
+                        k_scale=fused.k_scale, v_scale=fused.v_scale,
+                        max_context_len=wl.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(fused.k_cache), k_ref)
+    assert np.array_equal(host_bits(fused.v_cache), v_ref)
+    assert np.array_equal(host_bits(fused.out), out)
+
+
+@pytest.mark.parametrize("kv_dtype,q_dtype", [("bf16", "bf16"), ("fp8_e4m3", "bf16")])
+def test_short_heads_needle_bit_exact(kv_dtype, q_dtype):
+    """The needle through the head mode's LDS merge (8 waves per head)."""
+    L = 250
+    t_stars = (0, 15, 16, 31, 32, 33, 100, 127, 128, 200, L - 1)
+    wl, q, k, v, ks, vs, expect = _needle_setup(kv_dtype, q_dtype, t_stars, L)
+    dev = Dev(wl)
+    dev.q = dev_bits(q, q_dtype)
+    dev.k_cache = dev_bits(k, kv_dtype)
+    dev.v_cache = dev_bits(v, kv_dtype)
+    if ks is not None:
+        dev.k_scale = torch.from_numpy(ks).cuda()
+        dev.v_scale = torch.from_numpy(vs).cuda()
+    out = oracle.to_f64(dev.decode(partition_tokens=0), q_dtype)
+    mism = np.argwhere(out != expect)
+    assert len(mism) == 0, f"{len(mism)} mismatches, first {mism[:4].tolist()}"
+
+
+def test_short_heads_with_shared_prefix():
+    """Head mode with shared prefixes: members skip the shared blocks and fold the prefix parts
+    in; the same call without sharing reads the prefix per sequence."""
+    spec = Spec("short_prefix", 10, 16, 2, 128, "bf16", "bf16",
+                ("list", (40, 3, 120, 0, 77, 17, 150, 96, 1, 60)), prefix=(5, 64),
+                pool=("times", 2), seed=58)
+    wl = workloads.make(spec)
+    assert wl.max_context_len <= 256 and len(wl.sharing) == 5
+    dev = Dev(wl)
+    dev.append()
+    ref, _, _ = oracle_after_append(wl)
+    planned = dev.decode(partition_tokens=0, shared_prefixes=True)
+    assert_close(planned, ref, "bf16", "short heads, shared prefix")
+    unshared = dev.decode(partition_tokens=0)
+    assert_close(unshared, ref, "bf16", "short heads, prefix read per sequence")
+
+
 def _relocate(wl, seed):
     """Same logical K/V, every used block moved to a fresh random physical block."""
     rng = np.random.default_rng(seed)
