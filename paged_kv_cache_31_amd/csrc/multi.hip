@@ -462,6 +462,7 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
     }
     const bool partial = t0 + kStepTokens > end_lo;          // wave-uniform
     const int tb = t0 + 8 * grp;
+
     // Scores stay unscaled until the exponent: the largest scaled score is the scaled largest
     // (or smallest, for a negative scale) raw one, and exp2(fma(s, scale, -m)) saves a pass.
     V8 pHi[TPW], pLo[TPW];
@@ -494,12 +495,12 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
       const float m_new = fmaxf(m_run[u], mx * qs);
       const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
       const float alpha = fast_exp2(m_run[u] - m_ref);
-      float pr[8], psum = 0.0f;
+      float pr[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        pr[jj] = fast_exp2(__builtin_fmaf(sc[jj], qs, -m_ref));
-        psum += pr[jj];
-      }
+      for (int jj = 0; jj < 8; ++jj) pr[jj] = fast_exp2(__builtin_fmaf(sc[jj], qs, -m_ref));
+      float psum = pr[0];
+#pragma unroll
+      for (int jj = 1; jj < 8; ++jj) psum += pr[jj];
       l_run[u] = l_run[u] * alpha + psum;
       m_run[u] = m_new;
       // once the running maxima settle, most steps leave them unchanged (alpha = 1 exactly)
@@ -515,10 +516,7 @@ __global__ __launch_bounds__(64 * W, 2) void chunk_kernel(MultiArgs a) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         h[w] = pack2<QT>(pr[2 * w], pr[2 * w + 1]);
-        if constexpr (SPLIT_P) {
-          const V8 hv = as_vec8<V8>(make_uint4(h[w], 0u, 0u, 0u));
-          lo[w] = pack2<QT>(pr[2 * w] - (float)hv[0], pr[2 * w + 1] - (float)hv[1]);
-        }
+        if constexpr (SPLIT_P) lo[w] = bf16_lo2(pr[2 * w], pr[2 * w + 1], h[w]);
       }
       pHi[u] = as_vec8<V8>(make_uint4(h[0], h[1], h[2], h[3]));
       if constexpr (SPLIT_P) pLo[u] = as_vec8<V8>(make_uint4(lo[0], lo[1], lo[2], lo[3]));

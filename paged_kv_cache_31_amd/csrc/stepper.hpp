@@ -42,14 +42,20 @@ __device__ __forceinline__ V8 zero_vec8() {
   return __builtin_bit_cast(V8, make_uint4(0u, 0u, 0u, 0u));
 }
 
+// Two floats rounded (to nearest even) to the 16-bit element type, x in the low half: one
+// packed conversion (two scalar ones and the packing cost five instructions).
 template <int QT>
 __device__ __forceinline__ uint32_t pack2(float x, float y) {
   typedef typename Mfma<QT>::elem E;
-  E a = (E)x, b = (E)y;
-  uint16_t ua, ub;
-  __builtin_memcpy(&ua, &a, 2);
-  __builtin_memcpy(&ub, &b, 2);
-  return (uint32_t)ua | ((uint32_t)ub << 16);
+  typedef E E2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, E2));
+}
+
+// The low part of a bf16 hi/lo pair: hi = pack2(x, y), and x - hi, y - hi rounded again, so
+// that hi + lo carries about 16 significant bits of each weight.
+__device__ __forceinline__ uint32_t bf16_lo2(float x, float y, uint32_t hi) {
+  return pack2<DT_BF16>(x - __builtin_bit_cast(float, hi << 16),
+                        y - __builtin_bit_cast(float, hi & 0xFFFF0000u));
 }
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
@@ -388,12 +394,12 @@ struct Stepper {
         // a column that has seen no key yet keeps m = -inf; its weights and rescale are then 0
         const float m_ref = ROWS && m_new == -INFINITY ? 0.0f : m_new;
         const float alpha = fast_exp2(m_run[u] - m_ref);
-        float pr[8], psum = 0.0f;
+        float pr[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          pr[jj] = fast_exp2(sc[jj] - m_ref);
-          psum += pr[jj];
-        }
+        for (int jj = 0; jj < 8; ++jj) pr[jj] = fast_exp2(sc[jj] - m_ref);
+        float psum = pr[0];
+#pragma unroll
+        for (int jj = 1; jj < 8; ++jj) psum += pr[jj];
         l_run[u] = l_run[u] * alpha + psum;
         m_run[u] = m_new;
 #pragma unroll
@@ -406,10 +412,7 @@ struct Stepper {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           h[w] = pack2<QT>(pr[2 * w], pr[2 * w + 1]);
-          if constexpr (SPLIT_P) {
-            const V8 hv = as_vec8<V8>(make_uint4(h[w], 0u, 0u, 0u));
-            l[w] = pack2<QT>(pr[2 * w] - (float)hv[0], pr[2 * w + 1] - (float)hv[1]);
-          }
+          if constexpr (SPLIT_P) l[w] = bf16_lo2(pr[2 * w], pr[2 * w + 1], h[w]);
         }
         pHi[u] = as_vec8<V8>(make_uint4(h[0], h[1], h[2], h[3]));
         if constexpr (SPLIT_P) pLo[u] = as_vec8<V8>(make_uint4(l[0], l[1], l[2], l[3]));
