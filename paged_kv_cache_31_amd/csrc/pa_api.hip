@@ -379,6 +379,7 @@ PA_EXPORT pa_status pa_decode_multi(const pa_multi_desc* desc, const void* q,
   a.part_blocks = p.part_blocks;
   a.total_items = p.items;
   a.row_blocks = p.row_blocks;
+  a.chunk_waves = p.chunk_waves;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   hipError_t e =
       p.split_rt > 0

@@ -183,6 +183,7 @@ struct MultiArgs {
   int part_blocks;             // blocks per key partition (even unless partition_tokens fixes it)
   long long total_items;
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
+  int chunk_waves;             // chunk_kernel: waves per workgroup (kChunkWide or kChunkPingPong)
   // Balanced split (multi_split_kernel): split_rt > 0 row tiles per head.
   int split_rt;
   int total_lanes;             // chunks of the flattened block space
@@ -195,17 +196,20 @@ constexpr long kMultiTargetWaves = 4096;   // waves the automatic partition aims
 constexpr int kMultiMinPartBlocks = 16;    // automatic partitions are at least 256 tokens
 
 // Heads with more query rows than multi_split_kernel takes (more than four MFMA tiles) go to
-// chunk_kernel: a workgroup takes a block of 128 rows of one head (4 waves x 2 tiles, prefill
-// chunks) and stages each K/V step once in LDS for all of them.
+// chunk_kernel: a workgroup takes a block of rows of one head and stages each K/V step once in
+// LDS for all of them: 128 rows (4 waves x 2 tiles), or for heads of at least 256 rows (prefill
+// chunks) 256 rows in 8 waves whose two halves ping-pong between softmax and matrix products.
 struct ChunkShape {
   int waves, tiles;            // waves per workgroup, 16-column tiles per wave
 };
 constexpr ChunkShape kChunkWide = {4, 2};
+constexpr ChunkShape kChunkPingPong = {8, 2};
 
 struct MultiPlan {
   int tiles_per_head, num_parts, part_blocks;
   long long items;             // waves (multi_kernel) or workgroups (chunk_kernel)
   int row_blocks;              // > 0: chunk_kernel, this many row blocks per head
+  int chunk_waves;             // chunk_kernel: waves per workgroup
   int split_rt;                // > 0: multi_split_kernel with this many row tiles per head
   int split_waves;             // multi_split_kernel: waves per chunk
   long long split_wgs;         // multi_split_kernel: most workgroups a launch may use
@@ -250,6 +254,7 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
   const long long maxblk = ((long long)len_cap + kBlock - 1) / kBlock;
   p.tiles_per_head = (int)((rows + 15) / 16);
   p.row_blocks = 0;
+  p.chunk_waves = 0;
   p.split_rt = 0;
   p.split_waves = 0;
   p.split_wgs = 0;
@@ -269,7 +274,10 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
     return p;
   }
   if (partition_tokens == 0) {   // more than 64 rows (fewer took the split above)
-    const int block_rows = 16 * kChunkWide.waves * kChunkWide.tiles;
+    const ChunkShape sh =
+        rows >= 16 * kChunkPingPong.waves * kChunkPingPong.tiles ? kChunkPingPong : kChunkWide;
+    const int block_rows = 16 * sh.waves * sh.tiles;
+    p.chunk_waves = sh.waves;
     p.row_blocks = (int)((rows + block_rows - 1) / block_rows);
     p.num_parts = 1;
     p.part_blocks = (int)(maxblk + (maxblk & 1));
