@@ -268,7 +268,7 @@ __device__ __forceinline__ void merge_published(const DecodeArgs& a, int b, int 
   }
 }
 
-template <int D, int QT, int KVT>
+template <int D, int QT, int KVT, bool HEADS>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeArgs a) {
   typedef Stepper<D, QT, KVT> St;
   typedef typename St::V8 V8;
@@ -292,11 +292,14 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
   const int B = a.batch, Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = a.group;
   const int cap = a.len_cap;
 
-  if (a.head_mode > 0) {
+  if constexpr (HEADS) {
     // ---- Short heads (at most 2 * WPH blocks each): WPH waves per sequence head, wave k of a
     // head taking its blocks [skip + 2k, skip + 2k + 2) as one step; the pieces of a head meet
     // in LDS and its waves write it, each a share of the 16-dim tiles.  No scan of the lengths,
-    // nothing crosses workgroups.
+    // nothing crosses workgroups.  A launch of its own instance, whose LDS is one piece per
+    // wave (a launch costs more the more LDS its workgroups take).
+    __shared__ float hm_pm[kWaves][16], hm_pl[kWaves][16];
+    __shared__ f32x4 hm_pacc[kWaves][NT][64];
     const int WPH = a.head_mode;
     const int hl = wave / WPH, k = wave - hl * WPH;
     const int h = uniform(blockIdx.x * (kWaves / WPH) + hl);
@@ -354,11 +357,11 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
       return;
     }
     if (grp == 0) {
-      sm_pm[wave][0][col] = m_run;
-      sm_pl[wave][0][col] = l_run;
+      hm_pm[wave][col] = m_run;
+      hm_pl[wave][col] = l_run;
     }
 #pragma unroll
-    for (int i = 0; i < NT; ++i) sm_pacc[wave][0][i][lane] = acc[i];
+    for (int i = 0; i < NT; ++i) hm_pacc[wave][i][lane] = acc[i];
     __syncthreads();
     if (h >= B * Hkv || col >= G) return;
     const int w0 = hl * WPH;
@@ -368,14 +371,14 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void decode_kernel(DecodeA
         continue;
       }
       // piece 0 has tokens (skip_of leaves at least one block), so the maximum is finite
-      float M_ = sm_pm[w0][0][col];
-      for (int i = 1; i < WPH; ++i) M_ = fmaxf(M_, sm_pm[w0 + i][0][col]);
+      float M_ = hm_pm[w0][col];
+      for (int i = 1; i < WPH; ++i) M_ = fmaxf(M_, hm_pm[w0 + i][col]);
       float gl = 0.0f;
       f32x4 go[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
       for (int i = 0; i < WPH; ++i) {
-        const float w = fast_exp2(sm_pm[w0 + i][0][col] - M_);
-        gl += w * sm_pl[w0 + i][0][col];
-        go[0] += w * sm_pacc[w0 + i][0][t][lane];
+        const float w = fast_exp2(hm_pm[w0 + i][col] - M_);
+        gl += w * hm_pl[w0 + i][col];
+        go[0] += w * hm_pacc[w0 + i][t][lane];
       }
       if (sk > 0) fold_prefix<D>(a, row, prefix_parts(sk), grp, t, 1, M_, gl, go);
       *reinterpret_cast<uint2*>(out + 16 * t) =
@@ -1111,15 +1114,20 @@ static hipError_t launch_t(const DecodeArgs& a, int prefix_wgs, hipStream_t stre
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_kernel<D, QT, KVT>), dim3(a.total_waves / kWaves), dim3(64 * kWaves),
-                     0, stream, a);
+  if (a.head_mode > 0)
+    hipLaunchKernelGGL((decode_kernel<D, QT, KVT, true>), dim3(a.total_waves / kWaves),
+                       dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, QT, KVT, false>), dim3(a.total_waves / kWaves),
+                       dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int QT, int KVT>
 static int occupancy_t() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, QT, KVT>, 64 * kWaves, 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, QT, KVT, false>, 64 * kWaves,
+                                                   0)
       != hipSuccess)
     return 0;
   return n;
