@@ -98,17 +98,22 @@ typedef struct pa_decode_desc {
                                  The result is the same attention up to rounding order.
                                  2: the same, reusing the grouping that the last call with 1 left in
                                  this workspace instead of planning again: for the layers of one
-                                 step, whose calls read the same block_tables and context_lens.  The
-                                 caller guarantees those are unchanged since that call, and that
-                                 the workspace saw only such calls in between; the results are
-                                 then bitwise those of a call with 1.  The planning call saves a
-                                 signature of its descriptor and workspace layout with the plan;
-                                 a reusing call that finds another signature there (a workspace
-                                 no planning call has written, another descriptor, or scratch of
-                                 another call written over it) reads no shared blocks and gives
-                                 the unshared results.  Saved plan entries are clamped into range
-                                 before use, so even a workspace overwritten in a way the
-                                 signature misses is never read or written out of bounds. */
+                                 step, and for later steps while the batch keeps its sequences.
+                                 The reusing call checks the saved grouping against its own
+                                 block_tables and context_lens: a member whose shared entries
+                                 now differ from its leader's, or whose length no longer leaves
+                                 it a block past the shared ones, reads its whole head instead
+                                 (sequences that came to share blocks since the plan are read
+                                 unshared until a call with 1 plans again).  With tables and
+                                 lengths unchanged the results are bitwise those of a call with
+                                 1.  The planning call saves a signature of its descriptor and
+                                 workspace layout with the plan; a reusing call that finds
+                                 another signature there (a workspace no planning call has
+                                 written, another descriptor, or scratch of another call written
+                                 over it) reads no shared blocks and gives the unshared results.
+                                 Saved plan entries are clamped into range before use, so even a
+                                 workspace overwritten in a way the signature misses is never
+                                 read or written out of bounds. */
 } pa_decode_desc;
 
 typedef struct pa_multi_desc {

@@ -340,7 +340,8 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_sca
 
     shared_prefixes: read blocks that several sequences' tables start with once per group of
     sequences; 2 reuses the grouping planned by the previous call on the same workspace (the
-    layers of one step: unchanged block tables, lengths and descriptor), see
+    layers of one step, and later steps while the batch keeps its sequences: the kernel drops
+    members whose tables or lengths no longer fit the saved grouping), see
     pa_decode_desc.shared_prefixes.  The binding tracks which call last used each workspace and
     plans again when another call has used it since the planning call.
     check=True (tests): first copy the tables and lengths to the host and validate them."""

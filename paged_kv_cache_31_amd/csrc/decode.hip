@@ -799,6 +799,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
   __shared__ int s_ubase[kPlanMaxBatch];            // per leader: the group's first unit
   __shared__ int s_scan[NTH / 64];
   __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
+  __shared__ uint32_t sm_bad;                       // members a reused unit record drops
   __shared__ f32x4 sm_acc[kWaves][NT][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1026,6 +1027,32 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
       k = min(max(uniform(rec[4]), 0), a.prefix_parts - 1);
       member = r < S ? rec[kUnitMembers + r] : -1;
       if (member >= B) member = -1;
+      // The saved plan is checked against this call's tables and lengths: a member whose table
+      // entries over [j0, j1) differ from the leader's, or whose length no longer leaves it a
+      // block past j1, is dropped (bit r of sm_bad): its skip count goes to 0, so that
+      // decode_kernel reads its whole head, and its parts are not written.  Every unit of a
+      // member checks its own range, and the unit ending at the member's skip count checks the
+      // length, so a member keeps its skip count only if every shared block still matches.
+      // The loads are issued here and used after the unit's steps.
+      if (wave == 0) {
+        uint32_t bad = 0;
+        const int32_t* tl = a.block_tables + (size_t)lead * MB;
+        for (int e = lane; e < S * kUnitBlocks; e += 64) {
+          const int rr = e / kUnitBlocks, j = j0 + (e - rr * kUnitBlocks);
+          const int mb = rec[kUnitMembers + rr];
+          if (mb < 0 || mb >= B) continue;
+          bool ok = j >= j1 || a.block_tables[(size_t)mb * MB + j] == tl[j];
+          if (e == rr * kUnitBlocks) ok = ok && clamp_len(a.context_lens[mb], a.len_cap) > kBlock * j1;
+          if (!ok) bad |= 1u << rr;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) bad |= __shfl_xor(bad, o);
+        if (lane == 0) sm_bad = bad;
+        if (lane < S && ((bad >> lane) & 1)) {
+          const int mb = rec[kUnitMembers + lane];
+          if (mb >= 0 && mb < B) a.ws_skip[mb] = 0;
+        }
+      }
     } else {
       int lo = 0, hi = kPlanMaxBatch - 1;           // the leader whose group's units contain u
       while (lo < hi) {
@@ -1086,7 +1113,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
       wt[w] = fast_exp2(sm_m[w][col] - M_ref);
       L_ += wt[w] * sm_l[w][col];
     }
-    if (member >= 0) {
+    if (member >= 0 && !(a.plan_reuse && ((sm_bad >> r) & 1))) {
       const size_t part = row * a.prefix_parts + k;
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) {

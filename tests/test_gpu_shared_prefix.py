@@ -314,3 +314,35 @@ def test_binding_plans_again_after_another_call():
     first = host_bits(outs[0])
     assert np.array_equal(host_bits(outs[1]), first)
     assert np.array_equal(host_bits(outs[2]), first)
+
+
+@pytest.mark.parametrize("change", ["member_block", "member_length", "leader_row", "none"])
+def test_reuse_checks_the_saved_plan(change):
+    """A reusing call (shared_prefixes 2) checks the saved plan against its own tables and
+    lengths: a member whose shared entries now differ from its leader's, or whose length no
+    longer leaves it a block past the shared ones, reads its whole head instead.  After each
+    change the result is the attention over the changed tables (oracle), and with no change it
+    is bitwise the planning call's.  Through the C ABI."""
+    wl, k, v = _setup("bf16", "bf16", 2, 4, 128, LENS, seed=79)
+    t = _grouped_tables(wl)
+    dev = _layer(wl, k, v, t)
+    ws = _workspace(dev)
+    planned = _abi_decode(dev, 1, ws)
+    t2, lens2 = t.copy(), wl.context_lens.copy()
+    if change == "member_block":          # member 3 now holds another sequence's block at 10
+        t2[3, 10] = t[0, 10]
+    elif change == "member_length":       # member 8 (2000 tokens) shrinks inside the shared part
+        lens2[8] = 100
+    elif change == "leader_row":          # the leader's slot now holds another request's blocks
+        t2[1, :40] = t[0, :40]
+    dev.tables = torch.from_numpy(np.ascontiguousarray(t2)).cuda()
+    dev.lens = torch.from_numpy(lens2).cuda()
+    reused = _abi_decode(dev, 2, ws)
+    s = wl.spec
+    ref = oracle.decode(wl.q, k, v, t2, lens2, wl.scale, s.q_dtype, s.kv_dtype)
+    assert_close(reused, ref, s.q_dtype, f"reuse after {change}")
+    if change == "none":
+        assert np.array_equal(reused, planned)
+    else:                                 # and a fresh plan of the changed tables agrees
+        fresh = _abi_decode(dev, 1, _workspace(dev))
+        assert_close(fresh, ref, s.q_dtype, f"planning after {change}")
