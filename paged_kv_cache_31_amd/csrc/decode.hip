@@ -777,7 +777,9 @@ __device__ __forceinline__ int block_scan(int v, int* sm, int& total) {
   return before + incl - v;
 }
 
-template <int D, int QT, int KVT>
+// REUSE: the instance for calls that reuse a saved plan (shared_prefixes 2), which declares
+// none of the planning arrays: a launch costs more the more LDS its workgroups take.
+template <int D, int QT, int KVT, bool REUSE>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeArgs a) {
   typedef Stepper<D, QT, KVT, false> St;
   typedef typename St::V8 V8;
@@ -811,7 +813,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
   // The plan (phases 1-3) depends only on the lengths and tables; a call that reuses the one a
   // planning call saved goes straight to the units.
   int U = 0;
-  if (a.plan_reuse) {
+  if constexpr (REUSE) {
     // The saved plan is taken only if the header carries this call's signature (descriptor and
     // workspace layout) and a unit count the layout can hold; otherwise (another kind of call
     // wrote over it, or none planned) the call runs with no shared blocks: no units, and
@@ -1018,7 +1020,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
   for (int u = blockIdx.x; u < U; u += gridDim.x) {
     int* rec = a.plan_units + kUnitHead + (size_t)u * kUnitRec;
     int lead, kvh, k, j0, j1, member;
-    if (a.plan_reuse) {
+    if constexpr (REUSE) {
       // clamped into range: the records are workspace contents this call did not write
       lead = min(max(uniform(rec[0]), 0), B - 1);
       j1 = min(max(uniform(rec[2]), 0), min(MB, kMaxSharedBlocks));
@@ -1113,7 +1115,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
       wt[w] = fast_exp2(sm_m[w][col] - M_ref);
       L_ += wt[w] * sm_l[w][col];
     }
-    if (member >= 0 && !(a.plan_reuse && ((sm_bad >> r) & 1))) {
+    if (member >= 0 && !(REUSE && ((sm_bad >> r) & 1))) {
       const size_t part = row * a.prefix_parts + k;
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) {
@@ -1136,8 +1138,12 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void prefix_kernel(DecodeA
 template <int D, int QT, int KVT>
 static hipError_t launch_t(const DecodeArgs& a, int prefix_wgs, hipStream_t stream) {
   if (a.ws_skip) {
-    hipLaunchKernelGGL((prefix_kernel<D, QT, KVT>), dim3(prefix_wgs), dim3(64 * kWaves), 0,
-                       stream, a);
+    if (a.plan_reuse)
+      hipLaunchKernelGGL((prefix_kernel<D, QT, KVT, true>), dim3(prefix_wgs), dim3(64 * kWaves),
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL((prefix_kernel<D, QT, KVT, false>), dim3(prefix_wgs), dim3(64 * kWaves),
+                         0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
