@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
   constexpr int PT = Lay::PER_THREAD;
   constexpr int ROWS_W = 16 * TPW;                           // rows per wave
   constexpr int ROWS_G = ROWS_W * W;                         // rows per workgroup
-  static_assert(BUFS == 2 || BUFS == 3, "two or three LDS step buffers");
+  static_assert(BUFS == 2 || BUFS == 3 || (BUFS == 4 && W == 8), "LDS step buffers");
   __shared__ __attribute__((aligned(16))) uint8_t lds[BUFS * Lay::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -573,60 +573,69 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
   const int se = s0 + nsteps;
   auto active = [&](int s) { return has_rows && kStepTokens * s < end_hi; };
   if constexpr (W == 8) {
-    // Ping-pong (three buffers, step s in buffer (s - s0) % 3).  Waves w and w + 4 share a
+    // Ping-pong (four buffers, step s in buffer (s - s0) % 4).  Waves w and w + 4 share a
     // SIMD; the second group (waves 4-7) runs half a step behind the first, so that on every
     // SIMD one wave is in its softmax (vector ALU) while the other issues matrix products.
     // Iteration s, phase 1 -- first group: softmax(s); second: P.V(s - 1), scores(s).  Phase 2
-    // -- first: P.V(s), scores(s + 1); second: softmax(s); all: store step s + 2 into the buffer
-    // of s - 1 (its last reader, the second group's P.V(s - 1), ran in phase 1) and load step
-    // s + 4.  A barrier ends each phase.
-    static_assert(BUFS == 3, "the ping-pong schedule takes three buffers");
+    // -- first: P.V(s), scores(s + 1); second: softmax(s).  A barrier ends each phase.
+    // Every second iteration (s - s0 even), phase 2 also stores steps s + 2 and s + 3 into the
+    // buffers of s - 2 and s - 1 (their last reader, the second group's P.V(s - 1), ran in
+    // phase 1) and loads steps s + 4 and s + 5 into the registers just stored.  A store waits
+    // for every load issued before it (the compiler counts loop-carried loads conservatively),
+    // so the loads get two iterations to land only if none is issued between them and their
+    // store: storing one step per iteration, they had one (measured: with the stores and loads
+    // skipped, 229 -> 187 us).
+    static_assert(BUFS == 4, "the ping-pong schedule takes four buffers");
 
     const bool lead = wave < W / 2;
-    auto buf_of = [&](int s) { return (s - s0) % 3; };
+    auto buf_of = [&](int s) { return (s - s0) & 3; };
     fetch(s0, wa);
     fetch(s0 + 1, wb);
     if (s0 < se) stage(s0, 0, wa);
-    fetch(s0 + 2, wa);
     if (s0 + 1 < se) stage(s0 + 1, 1, wb);
+    fetch(s0 + 2, wa);
     fetch(s0 + 3, wb);
     __syncthreads();
     // The two groups run separate loops with the same barriers (two per step), so that each
     // keeps only its own registers live across them.
     f32x4 S[TPW][2];
     V8 pHi[TPW], pLo[TPW];
-    auto tail = [&](int s, Words& w) {             // phase 2's staging, then its barrier
-      if (s + 2 < se) stage(s + 2, buf_of(s + 2), w);
-      fetch(s + 4, w);
+    auto tail = [&](int s, bool store) {          // phase 2's stores and loads, its barrier
+      if (store) {
+        if (s + 2 < se) stage(s + 2, buf_of(s + 2), wa);
+        if (s + 3 < se) stage(s + 3, buf_of(s + 3), wb);
+        fetch(s + 4, wa);
+        fetch(s + 5, wb);
+      }
       __syncthreads();
     };
     if (lead) {
       if (s0 < se && active(s0)) scores(0, S);
-      auto iteration = [&](int s, Words& w) {
+      auto iteration = [&](int s, bool store) {
         if (active(s)) softmax(s, buf_of(s), S, pHi, pLo);
         __syncthreads();
         if (active(s)) pv(buf_of(s), pHi, pLo);
         if (s + 1 < se && active(s + 1)) scores(buf_of(s + 1), S);
-        tail(s, w);
+        tail(s, store);
       };
       for (int s = s0; s < se;) {
-        iteration(s, wa);
+        iteration(s, true);
         if (++s >= se) break;
-        iteration(s, wb);
+        iteration(s, false);
         ++s;
       }
     } else {
-      auto iteration = [&](int s, Words& w) {
+      auto iteration = [&](int s, bool store) {
         if (s > s0 && active(s - 1)) pv(buf_of(s - 1), pHi, pLo);
         if (active(s)) scores(buf_of(s), S);
         __syncthreads();
         if (active(s)) softmax(s, buf_of(s), S, pHi, pLo);
-        tail(s, w);
+        tail(s, store);
       };
       for (int s = s0; s < se;) {
-        iteration(s, wa);
+        iteration(s, true);
         if (++s >= se) break;
-        iteration(s, wb);
+        iteration(s, false);
         ++s;
       }
       if (se > s0 && active(se - 1)) pv(buf_of(se - 1), pHi, pLo);
@@ -724,7 +733,7 @@ static hipError_t launch_chunk(const MultiArgs& a, hipStream_t stream) {
 template <int D, int QT, int KVT>
 static hipError_t launch_multi_t(const MultiArgs& a, hipStream_t stream) {
   if (a.row_blocks > 0 && a.chunk_waves == kChunkPingPong.waves)
-    return launch_chunk<D, QT, KVT, kChunkPingPong.waves, kChunkPingPong.tiles, 3>(a, stream);
+    return launch_chunk<D, QT, KVT, kChunkPingPong.waves, kChunkPingPong.tiles, 4>(a, stream);
   if (a.row_blocks > 0)   // one key partition: the chunk kernel writes the rows itself
     return launch_chunk<D, QT, KVT, kChunkWide.waves, kChunkWide.tiles, 3>(a, stream);
   long long wgs = (a.total_items + kMultiWaves - 1) / kMultiWaves;
