@@ -467,7 +467,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
   };
   // online softmax of step s's scores (LDS buffer buf holds the step): rescales the
   // accumulators and gives the weights as the P^T operands of P.V
-  auto softmax = [&](int s, int buf, const f32x4 (&S)[TPW][2], V8 (&pHi)[TPW], V8 (&pLo)[TPW]) {
+  auto softmax = [&](int s, int buf, f32x4 (&S)[TPW][2], V8 (&pHi)[TPW], V8 (&pLo)[TPW]) {
     const int t0 = kStepTokens * s;
     // fp8: this lane's 8 tokens lie in block grp / 2 of the step; its K scale multiplies the
     // scores, its V scale the weights (after their sum is taken)
@@ -484,20 +484,21 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
     // (or smallest, for a negative scale) raw one, and exp2(fma(s, scale, -m)) saves a pass.
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      float sc[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sc[jj] = S[u][jj >> 2][jj & 3];
+      // masked in place: a copy of the scores would cost a move per register on every step
       if constexpr (FP8) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) sc[jj] *= ksc;
+        for (int jj = 0; jj < 8; ++jj) S[u][jj >> 2][jj & 3] *= ksc;
       }
       const float masked = qs >= 0.0f ? -INFINITY : INFINITY;
       if (partial) {
         const int nval = min(max(end_lane[u] - tb, 0), 8);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-          if (jj >= nval) sc[jj] = masked;
+          if (jj >= nval) S[u][jj >> 2][jj & 3] = masked;
       }
+      float sc[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) sc[jj] = S[u][jj >> 2][jj & 3];
       float mx = sc[0];
       if (qs >= 0.0f) {
 #pragma unroll
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, NT * TPW * (SPLIT_P ? 2 : 1), 0);
     }
   };
-  auto softmax_pv = [&](int s, int buf, const f32x4 (&S)[TPW][2]) {
+  auto softmax_pv = [&](int s, int buf, f32x4 (&S)[TPW][2]) {
     V8 pHi[TPW], pLo[TPW];
     softmax(s, buf, S, pHi, pLo);
     pv(buf, pHi, pLo);

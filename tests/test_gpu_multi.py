@@ -161,6 +161,33 @@ def test_balanced_split_shapes(case):
     m.check(m.run(), f"split {case}", relief=SHORT_WINDOWS)
 
 
+def _set_v(m, b, kvh, tokens, value):
+    """Store `value` in every dimension of V for the given tokens of sequence b, KV head kvh."""
+    bits = workloads.storage_bits(np.array([value]), m.spec.kv_dtype)[0]
+    for t in tokens:
+        blk = m.wl.block_tables[b, t // 16]
+        m.v[blk, kvh, :, t % 16] = bits
+
+
+def test_chunk_rows_with_long_windows():
+    """bf16 prefill chunks whose rows see 189..1200 keys (no row in its first few keys): the
+    strict bound, no relief."""
+    m = Multi("bf16", "bf16", 2, 4, 128, (700, 1200), (512, 512), seed=109)
+    m.check(m.run(), "long windows")
+
+
+@pytest.mark.parametrize("value", [70000.0, 65280.0, -65280.0])
+def test_chunk_large_v_values(value):
+    """V elements of magnitude 65280 and 70144, far outside N(0,1), in every dimension of four
+    tokens of one head: the products keep their precision at any magnitude.  Outputs near the
+    large values are large, where the output format itself can miss the bound (relief)."""
+    m = Multi("bf16", "bf16", 2, 4, 128, (1500, 900), (600, 300), seed=111)
+    _set_v(m, 0, 1, (3, 700, 1201, 1499), value)
+    got = m.run()
+    assert np.isfinite(oracle.to_f64(got[:int(m.qs[-1])], "bf16")).all()
+    m.check(got, f"large V {value}", relief=True)
+
+
 def test_more_queries_than_context_and_loose_bounds():
     """Rows before the context are zero; host bounds larger than needed change nothing."""
     m = Multi("bf16", "bf16", 2, 4, 128, (3, 1, 40), (6, 4, 2), seed=101, spare_rows=2)
