@@ -348,12 +348,19 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
   // one; threads past the step's words reload a word), so that the count of loads in flight is
   // the same on every path and the wait before staging a step leaves the later steps' loads in
   // flight instead of draining them all.
-  auto fetch = [&](int s, Words& w) {
-    s = max(min(s, se_ - 1), 0);      // an empty range reloads a block its table holds
+  // the physical blocks of step s (a step past the range: the last one's; an empty range: a
+  // block its table holds)
+  struct StepIds {
+    int p0, p1;
+  };
+  auto ids_of = [&](int s) {
+    s = max(min(s, se_ - 1), 0);
     const int jb0 = 2 * s, jb1 = 2 * s + 1 < j1 ? 2 * s + 1 : 2 * s;
-    int p0 = trow[jb0], p1 = trow[jb1];
-    p0 = (unsigned)p0 < (unsigned)a.num_blocks ? p0 : 0;
-    p1 = (unsigned)p1 < (unsigned)a.num_blocks ? p1 : 0;
+    return StepIds{trow[jb0], trow[jb1]};
+  };
+  auto fetch_ids = [&](StepIds id, Words& w) {
+    const int p0 = (unsigned)id.p0 < (unsigned)a.num_blocks ? id.p0 : 0;
+    const int p1 = (unsigned)id.p1 < (unsigned)a.num_blocks ? id.p1 : 0;
     if constexpr (FP8) {
       w.sk0 = a.k_scale[(size_t)p0 * Hkv + kvh];
       w.sk1 = a.k_scale[(size_t)p1 * Hkv + kvh];
@@ -366,6 +373,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
     if constexpr (PT > 2) fetch_word(tid + 2 * NTHR, p0, p1, w.k2, w.v2);
     if constexpr (PT > 3) fetch_word(tid + 3 * NTHR, p0, p1, w.k3, w.v3);
   };
+  auto fetch = [&](int s, Words& w) { fetch_ids(ids_of(s), w); };
   // V halves of 8 tokens starting at token tv of the step: tokens at or past the end zeroed
   auto keep_v = [&](uint4 x, int t0, int tv) {
     const int valid = L - (t0 + tv);
@@ -601,12 +609,24 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
     // keeps only its own registers live across them.
     f32x4 S[TPW][2];
     V8 pHi[TPW], pLo[TPW];
+    // The block ids of the two steps the next stores load are read two iterations before their
+    // use, by one vector load (lanes 0-3: the blocks of steps s and s + 1), whose wait falls in
+    // order behind the K/V loads.  Scalar loads of them at their use left the table's latency in
+    // the phase twice per store iteration, and scalar loads issued early are waited on by the
+    // barrier (they share its wait counter with LDS operations).
+    auto ids_vec = [&](int s) {
+      const int ss = max(min(s + ((lane >> 1) & 1), se_ - 1), 0);
+      const int jb = 2 * ss + (lane & 1);
+      return trow[jb < j1 ? jb : 2 * ss];
+    };
+    int ids = ids_vec(s0 + 4);
     auto tail = [&](int s, bool store) {          // phase 2's stores and loads, its barrier
       if (store) {
         if (s + 2 < se) stage(s + 2, buf_of(s + 2), wa);
         if (s + 3 < se) stage(s + 3, buf_of(s + 3), wb);
-        fetch(s + 4, wa);
-        fetch(s + 5, wb);
+        fetch_ids(StepIds{__builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1)}, wa);
+        fetch_ids(StepIds{__builtin_amdgcn_readlane(ids, 2), __builtin_amdgcn_readlane(ids, 3)}, wb);
+        ids = ids_vec(s + 6);
       }
       __syncthreads();
     };
