@@ -500,6 +500,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
     }
     const bool partial = t0 + kStepTokens > end_lo;          // wave-uniform
     const int tb = t0 + 8 * grp;
+    // headroom of the reference max: weights below 2^8 (bf16 hi/lo and fp16 P hold them);
+    // fp16 P over an fp8 cache carries the V block scale too, so there the weights stay <= 1
+    constexpr float kLazy = QT == DT_F16 && FP8 ? 0.0f : 8.0f;
 
     // Scores stay unscaled until the exponent: the largest scaled score is the scaled largest
     // (or smallest, for a negative scale) raw one, and exp2(fma(s, scale, -m)) saves a pass.
@@ -520,32 +523,44 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
       float sc[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) sc[jj] = S[u][jj >> 2][jj & 3];
+      // the lane's largest scaled score (the smallest raw one for a negative scale)
       float mx = sc[0];
       if (qs >= 0.0f) {
 #pragma unroll
         for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
-        mx = max_across_rows(mx);
       } else {
 #pragma unroll
         for (int jj = 1; jj < 8; ++jj) mx = fminf(mx, sc[jj]);
-        mx = -max_across_rows(-mx);
       }
-      const float m_new = fmaxf(m_run[u], mx * qs);
-      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run[u] - m_ref);
+      // A row's reference max moves only when a score exceeds it by more than kLazy (log2
+      // units), so weights stay below 2^kLazy; a step that moves no reference in the wave needs
+      // no reduction across the row's lanes and no rescale.
+      float alpha = 1.0f;
+      if (__any(mx * qs > m_run[u] + kLazy)) {
+        const float mr = qs >= 0.0f ? max_across_rows(mx) : -max_across_rows(-mx);
+        const float m_new = fmaxf(m_run[u], mr * qs);
+        const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+        alpha = fast_exp2(m_run[u] - m_ref);
+        m_run[u] = m_new;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[u][t] *= alpha;
+        }
+      }
+      const float m_ref = m_run[u] == -INFINITY ? 0.0f : m_run[u];
       float pr[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) pr[jj] = fast_exp2(__builtin_fmaf(sc[jj], qs, -m_ref));
+      if (partial) {                              // a zero scale makes the masked exponents NaN
+        const int nval = min(max(end_lane[u] - tb, 0), 8);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (jj >= nval) pr[jj] = 0.0f;
+      }
       float psum = pr[0];
 #pragma unroll
       for (int jj = 1; jj < 8; ++jj) psum += pr[jj];
       l_run[u] = l_run[u] * alpha + psum;
-      m_run[u] = m_new;
-      // once the running maxima settle, most steps leave them unchanged (alpha = 1 exactly)
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[u][t] *= alpha;
-      }
       if constexpr (FP8) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) pr[jj] *= vsc;

@@ -134,6 +134,26 @@ def test_small_ragged_batches(kv_dtype, q_dtype, lens):
     assert np.array_equal(host_bits(fused.out), dev.decode(partition_tokens=0))
 
 
+@pytest.mark.parametrize("kv_dtype,q_dtype", [("bf16", "bf16"), ("fp8_e4m3", "bf16"),
+                                               ("f16", "f16")])
+@pytest.mark.parametrize("scale", [0.0, -0.09])
+@pytest.mark.parametrize("P", [0, 64])
+def test_zero_and_negative_scale(kv_dtype, q_dtype, scale, P):
+    """A zero softmax scale gives every visible key the same weight (the output is the mean of
+    V), a negative one weights the smallest scores most; ragged lengths put masked slots in the
+    last step of most heads.  Balanced split and fixed partitions."""
+    lens = (1, 17, 300, 600, 33, 0, 129)
+    spec = Spec("scales", len(lens), 8, 2, 128, q_dtype, kv_dtype, ("list", lens),
+                pool=("times", 2), seed=47)
+    wl = workloads.make(spec)
+    wl.scale = scale
+    dev = Dev(wl)
+    dev.append()
+    ref, _, _ = oracle_after_append(wl)
+    assert_close(dev.decode(partition_tokens=P), ref, q_dtype, f"scale {scale} P{P}",
+                 relief=True)
+
+
 @pytest.mark.parametrize("kv_dtype,q_dtype", [("bf16", "bf16"), ("f16", "f16")])
 def test_length_one_returns_v_exactly(kv_dtype, q_dtype):
     spec = Spec("one", 5, 16, 2, 128, q_dtype, kv_dtype, ("list", (1,) * 5), pool=("times", 2),

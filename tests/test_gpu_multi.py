@@ -188,6 +188,29 @@ def test_chunk_large_v_values(value):
     m.check(got, f"large V {value}", relief=True)
 
 
+SCALE_CASES = [
+    # (q dtype, kv dtype, group, context lengths, new tokens, partition): the ping-pong chunk
+    # shape (512 rows a head), the four-wave one (128), the balanced split (a few rows) and
+    # fixed partitions, each with masked slots in the last steps
+    ("bf16", "bf16", 4, (700, 1200), (512, 512), 0),
+    ("bf16", "bf16", 4, (700, 333), (32, 32), 0),
+    ("f16", "fp8_e4m3", 4, (700, 333), (32, 32), 0),
+    ("bf16", "bf16", 8, LENS, DRAFT, 0),
+    ("bf16", "fp8_e4m3", 8, LENS, DRAFT, 48),
+]
+
+
+@pytest.mark.parametrize("case", SCALE_CASES, ids=lambda c: f"{c[0]}-{c[1]}-g{c[2]}-P{c[5]}-T{max(c[4])}")
+@pytest.mark.parametrize("scale", [0.0, -0.09])
+def test_zero_and_negative_scale(case, scale):
+    """A zero softmax scale weights every visible key alike (the output is the mean of V); a
+    negative one weights the smallest scores most."""
+    qd, kvd, g, lens, T, P = case
+    m = Multi(qd, kvd, 2, g, 128, lens, T, seed=112 + SCALE_CASES.index(case))
+    m.wl.scale = scale
+    m.check(m.run(partition_tokens=P), f"scale {scale} {case}", relief=True)
+
+
 def test_more_queries_than_context_and_loose_bounds():
     """Rows before the context are zero; host bounds larger than needed change nothing."""
     m = Multi("bf16", "bf16", 2, 4, 128, (3, 1, 40), (6, 4, 2), seed=101, spare_rows=2)
