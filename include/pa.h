@@ -244,8 +244,10 @@ pa_status pa_decode(const pa_decode_desc* desc, const void* q, const void* k_cac
  * balanced split-KV: equal chunks of the batch's (sequence, KV head, block) space, each walked
  * by one wave holding the head's 16-row tiles (two waves of two tiles for 33-64 rows), partial
  * results merged by log-sum-exp inside the kernel.  Larger heads take a kernel that
- * stages K/V in LDS for blocks of rows; a fixed partition_tokens cuts every row tile's keys into
- * partitions merged by a second kernel.
+ * stages K/V in LDS for blocks of rows; when those blocks are too few to fill the GPU (a small
+ * batch of long contexts) it also cuts the keys into partitions of at least 512 tokens, merged
+ * by a second kernel.  A fixed partition_tokens cuts every row tile's keys into partitions
+ * merged by a second kernel.
  *
  * The workspace (pa_decode_multi_workspace_size bytes, 16-byte aligned; none when the size is
  * 0) follows pa_decode's contract: zero-filled once before its first use, its first 256 KiB are

@@ -773,10 +773,14 @@ static hipError_t launch_chunk(const MultiArgs& a, hipStream_t stream) {
 
 template <int D, int QT, int KVT>
 static hipError_t launch_multi_t(const MultiArgs& a, hipStream_t stream) {
-  if (a.row_blocks > 0 && a.chunk_waves == kChunkPingPong.waves)
-    return launch_chunk<D, QT, KVT, kChunkPingPong.waves, kChunkPingPong.tiles, 4>(a, stream);
-  if (a.row_blocks > 0)   // one key partition: the chunk kernel writes the rows itself
-    return launch_chunk<D, QT, KVT, kChunkWide.waves, kChunkWide.tiles, 3>(a, stream);
+  if (a.row_blocks > 0) {   // with one key partition the chunk kernel writes the rows itself
+    const hipError_t e =
+        a.chunk_waves == kChunkPingPong.waves
+            ? launch_chunk<D, QT, KVT, kChunkPingPong.waves, kChunkPingPong.tiles, 4>(a, stream)
+            : launch_chunk<D, QT, KVT, kChunkWide.waves, kChunkWide.tiles, 3>(a, stream);
+    if (e != hipSuccess || a.num_parts <= 1) return e;
+    return launch_merge<D, QT>(a, stream);
+  }
   long long wgs = (a.total_items + kMultiWaves - 1) / kMultiWaves;
   wgs = (wgs + 7) / 8 * 8;
   if (wgs > 0) {

@@ -204,6 +204,8 @@ struct ChunkShape {
 };
 constexpr ChunkShape kChunkWide = {4, 2};
 constexpr ChunkShape kChunkPingPong = {8, 2};
+constexpr int kCUs = 256;                   // compute units of an MI355X
+constexpr int kChunkMinPartBlocks = 32;     // chunk_kernel's own key partitions: 512+ tokens
 
 struct MultiPlan {
   int tiles_per_head, num_parts, part_blocks;
@@ -227,13 +229,13 @@ constexpr long kMaxSplitWorkgroups = 512;
 // Key partitions for `base` independent units so that about `target` units run, each at least
 // kMultiMinPartBlocks blocks long; part_blocks is even unless partition_tokens fixes it.
 inline void multi_parts(MultiPlan& p, long long base, long long target, long long maxblk,
-                        int partition_tokens) {
+                        int partition_tokens, int min_part_blocks = kMultiMinPartBlocks) {
   long long pb;
   if (partition_tokens > 0) {
     pb = partition_tokens / kBlock;
   } else {
     long long np = (target + base - 1) / (base > 0 ? base : 1);
-    const long long np_max = (maxblk + kMultiMinPartBlocks - 1) / kMultiMinPartBlocks;
+    const long long np_max = (maxblk + min_part_blocks - 1) / min_part_blocks;
     if (np > np_max) np = np_max;
     if (np < 1) np = 1;
     pb = (maxblk + np - 1) / np;
@@ -279,9 +281,11 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
     const int block_rows = 16 * sh.waves * sh.tiles;
     p.chunk_waves = sh.waves;
     p.row_blocks = (int)((rows + block_rows - 1) / block_rows);
-    p.num_parts = 1;
-    p.part_blocks = (int)(maxblk + (maxblk & 1));
-    p.items = (long long)batch * num_kv_heads * p.row_blocks;
+    // Too few row blocks to fill the chip (a small batch of long prompts): the keys are cut
+    // into partitions as well, merged afterwards like multi_kernel's.
+    const long long wgs = (long long)batch * num_kv_heads * p.row_blocks;
+    multi_parts(p, wgs, (long long)kCUs * (8 / sh.waves), maxblk, 0, kChunkMinPartBlocks);
+    p.items = wgs * p.num_parts;
     return p;
   }
   multi_parts(p, (long long)batch * num_kv_heads * (p.tiles_per_head > 0 ? p.tiles_per_head : 1),

@@ -211,6 +211,16 @@ def test_zero_and_negative_scale(case, scale):
     m.check(m.run(partition_tokens=P), f"scale {scale} {case}", relief=True)
 
 
+@pytest.mark.parametrize("qd,kvd,T", [("bf16", "bf16", 64), ("bf16", "bf16", 32),
+                                      ("f16", "fp8_e4m3", 64), ("bf16", "fp8_e4m3", 24)])
+def test_chunk_rows_with_key_partitions(qd, kvd, T):
+    """One long and one short prompt: too few blocks of rows to fill the GPU, so the keys are cut
+    into partitions too (merged afterwards); the short prompt's later partitions see no key of
+    its rows.  Every row, both row-block shapes."""
+    m = Multi(qd, kvd, 2, 4, 128, (6000, 700), (T, T), seed=116)
+    m.check(m.run(), f"key partitions {qd} {kvd} T{T}")
+
+
 def test_more_queries_than_context_and_loose_bounds():
     """Rows before the context are zero; host bounds larger than needed change nothing."""
     m = Multi("bf16", "bf16", 2, 4, 128, (3, 1, 40), (6, 4, 2), seed=101, spare_rows=2)
