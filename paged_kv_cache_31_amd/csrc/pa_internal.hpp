@@ -227,7 +227,7 @@ inline int split_chunk_waves(int tiles) { return tiles > 2 ? 2 : 1; }
 constexpr long kMaxSplitWorkgroups = 512;
 
 // Key partitions for `base` independent units so that about `target` units run, each at least
-// kMultiMinPartBlocks blocks long; part_blocks is even unless partition_tokens fixes it.
+// min_part_blocks blocks long; part_blocks is even unless partition_tokens fixes it.
 inline void multi_parts(MultiPlan& p, long long base, long long target, long long maxblk,
                         int partition_tokens, int min_part_blocks = kMultiMinPartBlocks) {
   long long pb;
