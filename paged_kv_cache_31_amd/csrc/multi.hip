@@ -210,15 +210,16 @@ static hipError_t launch_merge(const MultiArgs& a, hipStream_t stream) {
 // A workgroup of W waves takes 16 * TPW * W consecutive rows of one head (TPW 16-column MFMA
 // tiles per wave) and walks the keys of one partition of them in 32-token steps.  Each step's K
 // and V tiles are loaded from HBM once per workgroup (every thread a few 16-byte words, two steps
-// ahead of their use) and written to one of two LDS buffers; the waves read their MFMA operands
-// from LDS, so the tiles of a head share every load.  Per step a wave issues 8 MFMAs per tile for
+// ahead of their use) and written to one of three or four LDS buffers; the waves read their
+// MFMA operands from LDS, so the tiles of a head share every load.  Per step a wave issues 8 MFMAs per tile for
 // the scores and 8 (fp16) or 16 (bf16: P as a hi/lo pair) per tile for P.V.  Operand layouts are
 // those of the streaming core: K token rows in the A operand in the order that makes the score
 // layout the P^T operand, V^T as the A operand of P.V (the LDS V tile is dim-major, 32 tokens
 // per dimension row, rows padded by 16 bytes to spread LDS banks).  V elements of tokens at or
 // past the context end are zeroed when staged, so garbage in the last block's unused slots never
-// reaches the products.  With several key partitions the unnormalised result and its (max,
-// exp-sum) go to the workspace for multi_merge_kernel, as in multi_kernel.
+// reaches the products.  With several key partitions (taken when the blocks of rows alone are
+// too few to fill the GPU) the unnormalised result and its (max, exp-sum) go to the workspace
+// for multi_merge_kernel, as in multi_kernel.
 template <int D, int W, int EB>
 struct ChunkLds {
   // K token rows are unpadded; their 16-byte chunks are permuted per row (kswz) so that the 16
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
   constexpr int PT = Lay::PER_THREAD;
   constexpr int ROWS_W = 16 * TPW;                           // rows per wave
   constexpr int ROWS_G = ROWS_W * W;                         // rows per workgroup
-  static_assert(BUFS == 2 || BUFS == 3 || (BUFS == 4 && W == 8), "LDS step buffers");
+  static_assert(BUFS == 3 || (BUFS == 4 && W == 8), "LDS step buffers");
   __shared__ __attribute__((aligned(16))) uint8_t lds[BUFS * Lay::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -709,30 +710,6 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
       iteration(s, Sa, Sb, wa);
       if (++s >= se) break;
       iteration(s, Sb, Sa, wb);
-      ++s;
-    }
-  } else {
-    // Two buffers (step s in buffer (s - s0) % 2): step s is computed while step s + 1 is
-    // stored from registers into the other buffer and step s + 2 is loaded into the registers
-    // step s has left; unrolled by two for the register sets.
-    fetch(s0, wa);
-    fetch(s0 + 1, wb);
-    if (s0 < se) stage(s0, 0, wa);
-    __syncthreads();
-    auto iteration = [&](int s, int buf, Words& wn, Words& wf) {
-      fetch(s + 2, wf);
-      if (active(s)) {
-        f32x4 S[TPW][2];
-        scores(buf, S);
-        softmax_pv(s, buf, S);
-      }
-      if (s + 1 < se) stage(s + 1, buf ^ 1, wn);
-      __syncthreads();
-    };
-    for (int s = s0; s < se;) {
-      iteration(s, 0, wb, wa);
-      if (++s >= se) break;
-      iteration(s, 1, wa, wb);
       ++s;
     }
   }
