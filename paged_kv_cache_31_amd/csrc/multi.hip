@@ -215,20 +215,25 @@ static hipError_t launch_merge(const MultiArgs& a, hipStream_t stream) {
 // the scores and 8 (fp16) or 16 (bf16: P as a hi/lo pair) per tile for P.V.  Operand layouts are
 // those of the streaming core: K token rows in the A operand in the order that makes the score
 // layout the P^T operand, V^T as the A operand of P.V (the LDS V tile is dim-major, 32 tokens
-// per dimension row, rows padded by 16 bytes to spread LDS banks).  V elements of tokens at or
+// per dimension row, rows padded by 32 bytes to spread LDS banks).  V elements of tokens at or
 // past the context end are zeroed when staged, so garbage in the last block's unused slots never
 // reaches the products.  With several key partitions (taken when the blocks of rows alone are
 // too few to fill the GPU) the unnormalised result and its (max, exp-sum) go to the workspace
 // for multi_merge_kernel, as in multi_kernel.
 template <int D, int W, int EB>
 struct ChunkLds {
+  // Bank model (measured on gfx950 with the LDS bank-conflict counter): a 128-bit read serves
+  // 16 lanes a cycle from 64 four-byte banks, the lanes with equal bit 5 and equal parity of bits
+  // 2-4 of the lane id; a 128-bit store serves 8 consecutive lanes a cycle from 32 banks.
   // K token rows are unpadded; their 16-byte chunks are permuted per row (kswz) so that the 16
   // rows one operand read touches (rows 0-3, 8-11, 16-19, 24-27 of the step) fall on distinct
-  // banks.  With 2*D-byte rows, rows r and r + 16 would otherwise share banks.  LDS always holds
+  // banks.  With 2*D-byte rows, rows r and r + 16 would otherwise share banks.  V dimension rows
+  // take 96 bytes (64 of data): with 80 the operand reads and the 16-bit staging stores both
+  // met two-way conflicts (a third of the kernel's LDS cycles on a prefill chunk).  LDS always holds
   // 16-bit elements (fp8 codes are widened, exactly, when staged); the fp8 block scales of the
   // step (K then V, for its two blocks) follow the V tile.
   static constexpr int KSTRIDE = 2 * D;                      // bytes per K token row
-  static constexpr int VSTRIDE = 2 * kStepTokens + 16;       // bytes per V dimension row
+  static constexpr int VSTRIDE = 2 * kStepTokens + 32;       // bytes per V dimension row
   static constexpr int KBYTES = kStepTokens * KSTRIDE;
   static constexpr int SCALES = KBYTES + D * VSTRIDE;        // 4 floats: k0, k1, v0, v1
   static constexpr int BUF = SCALES + 16;
@@ -410,14 +415,21 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
     // K: 16 codes of one token row (dims cb .. cb + 15) -> two 16-byte chunks of 16-bit values
     const int tok = off / D, cb = off - tok * D;
     const int row = kBlock * blk + tok;
+    // Each store writes one half per thread: the first half where bit 2 of idx is clear, the
+    // second where it is set, so that the 8 threads one store cycle serves cover all 32 banks.
+    const int sw = (idx >> 2) & 1;
     uint8_t* kr = kb + row * Lay::KSTRIDE;
-    *reinterpret_cast<uint4*>(kr + 16 * kswz<D>(row, cb / 8)) = widen16(kx.x, kx.y);
-    *reinterpret_cast<uint4*>(kr + 16 * kswz<D>(row, cb / 8 + 1)) = widen16(kx.z, kx.w);
+    *reinterpret_cast<uint4*>(kr + 16 * kswz<D>(row, cb / 8 + sw)) =
+        widen16(sw ? kx.z : kx.x, sw ? kx.w : kx.y);
+    *reinterpret_cast<uint4*>(kr + 16 * kswz<D>(row, cb / 8 + 1 - sw)) =
+        widen16(sw ? kx.x : kx.z, sw ? kx.y : kx.w);
     // V: one dimension row of the block (16 tokens) -> its two 8-token halves
     const int d = off / 16, tv = kBlock * blk;
     uint8_t* vr = vb + d * Lay::VSTRIDE + 2 * tv;
-    *reinterpret_cast<uint4*>(vr) = keep_v(widen16(vx.x, vx.y), t0, tv);
-    *reinterpret_cast<uint4*>(vr + 16) = keep_v(widen16(vx.z, vx.w), t0, tv + 8);
+    *reinterpret_cast<uint4*>(vr + 16 * sw) =
+        keep_v(widen16(sw ? vx.z : vx.x, sw ? vx.w : vx.y), t0, tv + 8 * sw);
+    *reinterpret_cast<uint4*>(vr + 16 - 16 * sw) =
+        keep_v(widen16(sw ? vx.x : vx.z, sw ? vx.y : vx.w), t0, tv + 8 - 8 * sw);
   };
   auto stage_word = [&](int idx, int t0, uint8_t* kb, uint8_t* vb, uint4 kx, uint4 vx) {
     if constexpr (FP8) {
