@@ -22,6 +22,8 @@
 // kernel; with one partition the kernel normalises and writes the output itself.  Without a
 // fixed partition, heads of few rows take the balanced split (multi_split_kernel) and larger
 // ones chunk_kernel below.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "pa_internal.hpp"
 #include "stepper.hpp"
@@ -249,6 +251,40 @@ __device__ __forceinline__ int kswz(int r, int c) {
   else return c ^ (((r >> 1) & 1) | (((r >> 3) & 3) << 1));   // 8 chunks; rows alternate halves
 }
 
+// Tiles loaded straight into LDS (16-bit caches): V dimension rows are unpadded (64 bytes: a
+// load writes 16 consecutive bytes per lane, so padding would cost loads), and the rows with
+// bit 2 set hold their two blocks swapped, which keeps the operand reads on distinct banks.
+constexpr int kDirectVRow = 2 * kStepTokens;
+__device__ __forceinline__ int vswz(int d, int c) { return c ^ (2 * ((d >> 2) & 1)); }
+
+// s_waitcnt that waits until at most N vector memory operations of this wave are outstanding
+// (and nothing else)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// One 16-byte load per lane straight into LDS (global_load_lds_dwordx4): lane i writes
+// dst + 16 i, dst being wave-uniform.  (A function of its own: called from a generic lambda, the
+// builtin kept the host compiler from emitting the kernel's launch stub.)
+__device__ __forceinline__ void lds_load16(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// Workgroup barrier for loads straight into LDS: each wave first waits until its own loads up
+// to the one N operations back have landed, so that once every wave has arrived those steps are
+// whole in LDS.  (__syncthreads would wait for every load in flight: its release fence covers
+// the loads that write LDS.)  LDS reads before the barrier have been consumed by then; the
+// signal fences keep the compiler from moving memory operations across it.
+template <int N>
+__device__ __forceinline__ void direct_barrier() {
+  wait_vm<N>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int D, int QT, int KVT, int W, int TPW, int BUFS>
 __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
   typedef Mfma<QT> M;
@@ -268,7 +304,10 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
   constexpr int ROWS_W = 16 * TPW;                           // rows per wave
   constexpr int ROWS_G = ROWS_W * W;                         // rows per workgroup
   static_assert(BUFS == 3 || (BUFS == 4 && W == 8), "LDS step buffers");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[BUFS * Lay::BUF];
+  // 16-bit caches in the ping-pong shape load their tiles straight into LDS (four buffers of
+  // their own, declared with that loop); the others stage through registers into `lds`
+  constexpr bool DIRECT = W == 8 && !FP8;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DIRECT ? 16 : BUFS * Lay::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -463,21 +502,22 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
 
   // ---- products of one step for this wave's tiles
   const int krow0 = 16 * (col >> 3) + 8 * ((col >> 2) & 1) + (col & 3);
+  const int vchunk = vswz(col, grp);                      // (row 16 t + col: same bit 2)
   const float qs = a.qk_scale_log2;
   // scores of step s (unscaled) for this wave's tiles, from LDS buffer buf
   // the ping-pong shape issues all LDS operand reads of a product block before its MFMAs
   // (measured: prefill chunk 231.3 -> 228.8 us)
   constexpr bool PRE = W == 8;
-  auto scores = [&](int buf, f32x4 (&S)[TPW][2]) {
-    const uint8_t* kb = lds + buf * Lay::BUF;
+  auto scores_at = [&](const uint8_t* kb, f32x4 (&S)[TPW][2]) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
       for (int m = 0; m < 2; ++m) S[u][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     auto kop = [&](int m, int cc) {
       const int row = krow0 + 4 * m;
-      return as_vec8<V8>(*reinterpret_cast<const uint4*>(
-          kb + row * Lay::KSTRIDE + 16 * kswz<D>(row, 4 * cc + grp)));
+      // one vector load (a uint4 read is split into dwords and merged again late, which drops
+      // what tells the compiler which LDS buffer it reads)
+      return *reinterpret_cast<const V8*>(kb + row * Lay::KSTRIDE + 16 * kswz<D>(row, 4 * cc + grp));
     };
     V8 kAll[PRE ? 2 : 1][PRE ? NC : 1];
     if constexpr (PRE) {
@@ -499,6 +539,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * NC * TPW, 0);
     }
   };
+  auto scores = [&](int buf, f32x4 (&S)[TPW][2]) { scores_at(lds + buf * Lay::BUF, S); };
   // online softmax of step s's scores (LDS buffer buf holds the step): rescales the
   // accumulators and gives the weights as the P^T operands of P.V
   auto softmax = [&](int s, int buf, f32x4 (&S)[TPW][2], V8 (&pHi)[TPW], V8 (&pLo)[TPW]) {
@@ -589,16 +630,32 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
     }
   };
   // the P.V products of a step whose weights softmax() gave, V from LDS buffer buf
-  auto pv = [&](int buf, const V8 (&pHi)[TPW], const V8 (&pLo)[TPW]) {
-    const uint8_t* vb = lds + buf * Lay::BUF + Lay::KBYTES;
-    auto vop = [&](int t) {
-      return as_vec8<V8>(*reinterpret_cast<const uint4*>(
-          vb + (16 * t + col) * Lay::VSTRIDE + 16 * grp));
+  // (tiles loaded straight into LDS keep whatever the cache holds past the context end, so the
+  // step holding it zeroes those V elements after reading them)
+  auto pv_at = [&](const uint8_t* vb, int t0, const V8 (&pHi)[TPW], const V8 (&pLo)[TPW]) {
+    auto vraw = [&](int t) {          // whole-vector loads, as kop's
+      if constexpr (DIRECT)
+        return *reinterpret_cast<const u32x4*>(vb + (16 * t + col) * kDirectVRow + 16 * vchunk);
+      else
+        return *reinterpret_cast<const u32x4*>(vb + (16 * t + col) * Lay::VSTRIDE + 16 * grp);
     };
+    auto vop = [&](int t) { return __builtin_bit_cast(V8, vraw(t)); };
     V8 vAll[PRE ? NT : 1];
     if constexpr (PRE) {
+      u32x4 raw[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) vAll[t] = vop(t);
+      for (int t = 0; t < NT; ++t) raw[t] = vraw(t);
+      if (DIRECT && t0 + kStepTokens > L) {             // (selects: no divergent branch)
+        const int valid = L - (t0 + 8 * grp);
+        auto keep = [&](int k) {
+          return (2 * k < valid ? 0x0000FFFFu : 0u) | (2 * k + 1 < valid ? 0xFFFF0000u : 0u);
+        };
+        const u32x4 km = {keep(0), keep(1), keep(2), keep(3)};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) raw[t] &= km;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) vAll[t] = __builtin_bit_cast(V8, raw[t]);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -614,6 +671,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, NT * TPW * (SPLIT_P ? 2 : 1), 0);
     }
   };
+  auto pv = [&](int buf, const V8 (&pHi)[TPW], const V8 (&pLo)[TPW]) {
+    pv_at(lds + buf * Lay::BUF + Lay::KBYTES, 0, pHi, pLo);
+  };
   auto softmax_pv = [&](int s, int buf, f32x4 (&S)[TPW][2]) {
     V8 pHi[TPW], pLo[TPW];
     softmax(s, buf, S, pHi, pLo);
@@ -622,7 +682,128 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
 
   const int se = s0 + nsteps;
   auto active = [&](int s) { return has_rows && kStepTokens * s < end_hi; };
-  if constexpr (W == 8) {
+  if constexpr (DIRECT) {
+    // The ping-pong schedule below with the tiles loaded straight into LDS
+    // (global_load_lds_dwordx4: each lane writes 16 bytes, consecutive in lane order, at a
+    // wave-uniform LDS address): no register staging and no LDS stores.  Four buffers, each an
+    // LDS array of its own so that the compiler can tell them apart (a read of one buffer then
+    // waits for none of the loads into the others); the loop is unrolled by four so that every
+    // buffer index is known.  Step s + 3 is loaded at the middle barrier of iteration s, into
+    // the buffer step s - 1 left (its last readers ran before that barrier), and must have
+    // landed by the middle barrier of iteration s + 2 (the first group reads it after that one).
+    // Every step's loads are issued whatever the step (past the range: the last step again), so
+    // that the count of vector memory operations behind a step's loads is fixed: one step's
+    // (NSEG per wave) per iteration.
+    constexpr int KBY = kStepTokens * 2 * D;                 // K tile of a step, then V
+    constexpr int DBUF = 2 * KBY;
+    constexpr int NSEG = D / 64;                             // 1 KiB segments per wave and step
+    static_assert(DBUF == 8 * NSEG * 1024 && D * kDirectVRow == KBY, "direct layout");
+    __shared__ __attribute__((aligned(16))) uint8_t db0[DBUF], db1[DBUF], db2[DBUF], db3[DBUF];
+    auto bufp = [&](auto bc) -> uint8_t* {
+      constexpr int B = decltype(bc)::value & 3;
+      return B == 0 ? db0 : B == 1 ? db1 : B == 2 ? db2 : db3;
+    };
+    // waves 0-3 load the K tile (token rows, chunks permuted by kswz), waves 4-7 the V tile
+    // (dimension rows, chunks permuted by vswz); per lane and segment: the block of the step
+    // and the byte offset inside its (block, head) tile
+    const bool dk = wave < 4;
+    const uint8_t* dsrc = dk ? kc : vc;
+    const int dl0 = (dk ? 0 : KBY) + 1024 * NSEG * (wave & 3);
+    int dofs[NSEG], dblk[NSEG];
+#pragma unroll
+    for (int j = 0; j < NSEG; ++j) {
+      const int o = 1024 * (NSEG * (wave & 3) + j) + 16 * lane;
+      if (dk) {
+        const int row = o / (2 * D), c = kswz<D>(row, (o % (2 * D)) / 16);   // kswz: an involution
+        dblk[j] = row / kBlock;
+        dofs[j] = (row % kBlock) * 2 * D + 16 * c;
+      } else {
+        const int d = o / kDirectVRow, c = vswz(d, (o % kDirectVRow) / 16);
+        dblk[j] = c >> 1;
+        dofs[j] = d * 2 * kBlock + 16 * (c & 1);
+      }
+    }
+    auto load_step = [&](StepIds id, auto bc) {
+      constexpr int B = decltype(bc)::value & 3;
+      const int p0 = (unsigned)id.p0 < (unsigned)a.num_blocks ? id.p0 : 0;
+      const int p1 = (unsigned)id.p1 < (unsigned)a.num_blocks ? id.p1 : 0;
+#pragma unroll
+      for (int j = 0; j < NSEG; ++j) {
+        const uint8_t* src = dsrc + ((size_t)(dblk[j] ? p1 : p0) * Hkv + kvh) * TB + dofs[j];
+        lds_load16(src, bufp(bc) + dl0 + 1024 * j);
+      }
+    };
+    typedef std::integral_constant<int, 0> B0;
+    typedef std::integral_constant<int, 1> B1;
+    typedef std::integral_constant<int, 2> B2;
+    typedef std::integral_constant<int, 3> B3;
+    const bool lead = wave < W / 2;
+    // The partition's block ids go to LDS first (the plan keeps partitions of this kernel within
+    // kDirectMaxBlocks): read from there, they cost no vector load in the loop, whose result the
+    // compiler would wait for together with every tile load issued before it.
+    __shared__ int dids[kDirectMaxBlocks];
+    for (int k = tid; k < j1 - j0; k += NTHR) dids[k] = trow[j0 + k];
+    __syncthreads();
+    auto ids_at = [&](int s) {            // a step past the range: the last one's
+      const int ss = max(min(s, se_ - 1), s0);
+      const int jb = 2 * ss - j0;
+      return StepIds{dids[jb], dids[2 * ss + 1 < j1 ? jb + 1 : jb]};
+    };
+    f32x4 S[TPW][2];
+    V8 pHi[TPW], pLo[TPW];
+    // the middle barrier of iteration s: step s + 1 in LDS; then step s + 3's loads (its block
+    // ids read at the start of the iteration)
+    auto middle = [&](auto bc, StepIds id) {
+      constexpr int B = decltype(bc)::value;
+      direct_barrier<NSEG>();
+      load_step(id, std::integral_constant<int, B + 3>());
+    };
+    // The loop starts three iterations early, which only load steps s0 .. s0 + 2: with every
+    // load issued from inside the loop, the compiler keeps track of which buffer each one fills
+    // across the loop's back edge (loads issued before the loop made it wait for all of them at
+    // the first reads of every pass).  Step s lives in buffer (s - s0) % 4.
+    auto run = [&](auto iteration) {
+      for (int s = s0 - 3; s < se;) {
+        iteration(s, B1());
+        if (++s >= se) break;
+        iteration(s, B2());
+        if (++s >= se) break;
+        iteration(s, B3());
+        if (++s >= se) break;
+        iteration(s, B0());
+        ++s;
+      }
+    };
+    auto on = [&](int s) { return s >= s0 && s < se && active(s); };
+    if (lead) {
+      run([&](int s, auto bc) {
+        constexpr int B = decltype(bc)::value;
+        const StepIds id = ids_at(s + 3);
+        if (on(s)) softmax(s, 0, S, pHi, pLo);
+        middle(bc, id);
+        if (on(s)) pv_at(bufp(bc) + KBY, kStepTokens * s, pHi, pLo);
+        if (on(s + 1)) scores_at(bufp(std::integral_constant<int, B + 1>()), S);
+        direct_barrier<63>();
+      });
+    } else {
+      run([&](int s, auto bc) {
+        constexpr int B = decltype(bc)::value;
+        const StepIds id = ids_at(s + 3);
+        if (on(s - 1))
+          pv_at(bufp(std::integral_constant<int, B + 3>()) + KBY, kStepTokens * (s - 1), pHi, pLo);
+        if (on(s)) scores_at(bufp(bc), S);
+        middle(bc, id);
+        if (on(s)) softmax(s, 0, S, pHi, pLo);
+        direct_barrier<63>();
+      });
+    }
+    wait_vm<0>();                                            // no load into LDS left in flight
+    if (!lead && se > s0 && active(se - 1)) {
+      const int bl = (se - 1 - s0) & 3;
+      const uint8_t* vb = (bl == 0 ? db0 : bl == 1 ? db1 : bl == 2 ? db2 : db3) + KBY;
+      pv_at(vb, kStepTokens * (se - 1), pHi, pLo);
+    }
+  } else if constexpr (W == 8) {
     // Ping-pong (four buffers, step s in buffer (s - s0) % 4).  Waves w and w + 4 share a
     // SIMD; the second group (waves 4-7) runs half a step behind the first, so that on every
     // SIMD one wave is in its softmax (vector ALU) while the other issues matrix products.
@@ -763,6 +944,9 @@ static hipError_t launch_chunk(const MultiArgs& a, hipStream_t stream) {
 template <int D, int QT, int KVT>
 static hipError_t launch_multi_t(const MultiArgs& a, hipStream_t stream) {
   if (a.row_blocks > 0) {   // with one key partition the chunk kernel writes the rows itself
+    // the 16-bit ping-pong instance holds a partition's block ids in LDS
+    if (a.chunk_waves == kChunkPingPong.waves && KVT != DT_FP8 && a.part_blocks > kDirectMaxBlocks)
+      return hipErrorInvalidValue;
     const hipError_t e =
         a.chunk_waves == kChunkPingPong.waves
             ? launch_chunk<D, QT, KVT, kChunkPingPong.waves, kChunkPingPong.tiles, 4>(a, stream)

@@ -205,7 +205,10 @@ struct ChunkShape {
 constexpr ChunkShape kChunkWide = {4, 2};
 constexpr ChunkShape kChunkPingPong = {8, 2};
 constexpr int kCUs = 256;                   // compute units of an MI355X
-constexpr int kChunkMinPartBlocks = 32;     // chunk_kernel's own key partitions: 512+ tokens
+constexpr int kChunkMinPartBlocks = 32;
+// chunk_kernel over 16-bit caches in the ping-pong shape holds its partition's block ids in LDS:
+// its partitions are at most this many blocks (32768 tokens)
+constexpr int kDirectMaxBlocks = 2048;     // chunk_kernel's own key partitions: 512+ tokens
 
 struct MultiPlan {
   int tiles_per_head, num_parts, part_blocks;
@@ -229,7 +232,8 @@ constexpr long kMaxSplitWorkgroups = 512;
 // Key partitions for `base` independent units so that about `target` units run, each at least
 // min_part_blocks blocks long; part_blocks is even unless partition_tokens fixes it.
 inline void multi_parts(MultiPlan& p, long long base, long long target, long long maxblk,
-                        int partition_tokens, int min_part_blocks = kMultiMinPartBlocks) {
+                        int partition_tokens, int min_part_blocks = kMultiMinPartBlocks,
+                        long long max_part_blocks = 0) {
   long long pb;
   if (partition_tokens > 0) {
     pb = partition_tokens / kBlock;
@@ -241,6 +245,7 @@ inline void multi_parts(MultiPlan& p, long long base, long long target, long lon
     pb = (maxblk + np - 1) / np;
     pb += pb & 1;
     if (pb < 2) pb = 2;
+    if (max_part_blocks > 0 && pb > max_part_blocks) pb = max_part_blocks;   // even
   }
   long long np = (maxblk + pb - 1) / pb;
   if (np < 1) np = 1;
@@ -284,7 +289,9 @@ inline MultiPlan multi_plan(int batch, int num_kv_heads, int group, int max_quer
     // Too few row blocks to fill the chip (a small batch of long prompts): the keys are cut
     // into partitions as well, merged afterwards like multi_kernel's.
     const long long wgs = (long long)batch * num_kv_heads * p.row_blocks;
-    multi_parts(p, wgs, (long long)kCUs * (8 / sh.waves), maxblk, 0, kChunkMinPartBlocks);
+    const bool direct = sh.waves == kChunkPingPong.waves && !fp8_kv;
+    multi_parts(p, wgs, (long long)kCUs * (8 / sh.waves), maxblk, 0, kChunkMinPartBlocks,
+                direct ? kDirectMaxBlocks : 0);
     p.items = wgs * p.num_parts;
     return p;
   }
