@@ -221,6 +221,28 @@ def test_chunk_rows_with_key_partitions(qd, kvd, T):
     m.check(m.run(), f"key partitions {qd} {kvd} T{T}")
 
 
+def test_chunk_partition_cap_long_context():
+    """A 35000-token bf16 prompt with 1024 new rows per head: 256 blocks of rows, so the plan keeps
+    one key partition, and the 16-bit chunk kernel's cap (2048 blocks, the partition's block ids
+    held in LDS) cuts the 2188 blocks in two, merged afterwards.  Sampled rows (every KV head,
+    first and last rows included) against the oracle; row i attends the first 33977 + i tokens."""
+    L, T, G, hkv = 35000, 1024, 8, 8
+    m = Multi("bf16", "bf16", hkv, G, 128, (L,), (T,), seed=117)
+    got = m.run()
+    wl, s = m.wl, m.spec
+    rng = np.random.default_rng(117)
+    rows = sorted({0, 1, 512, T - 2, T - 1} | set(int(r) for r in rng.integers(0, T, 11)))
+    qf = oracle.to_f64(m.q[rows], s.q_dtype)                       # [rows][Hq][D]
+    ref = np.zeros((len(rows), hkv * G, 128))
+    for kvh in range(hkv):
+        k, v = oracle.gather(m.k, m.v, s.kv_dtype, wl.block_tables[0], L, kvh)
+        for r, i in enumerate(rows):
+            n = L - T + i + 1
+            ref[r, kvh * G:(kvh + 1) * G], _ = oracle.attend(qf[r, kvh * G:(kvh + 1) * G],
+                                                            k[:n], v[:n], float(np.float32(wl.scale)))
+    assert_close(got[rows], ref, s.q_dtype, "partition cap, sampled rows")
+
+
 def test_more_queries_than_context_and_loose_bounds():
     """Rows before the context are zero; host bounds larger than needed change nothing."""
     m = Multi("bf16", "bf16", 2, 4, 128, (3, 1, 40), (6, 4, 2), seed=101, spare_rows=2)
