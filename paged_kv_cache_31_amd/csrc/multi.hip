@@ -742,11 +742,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void chunk_kernel(MultiArgs a) {
     // kDirectMaxBlocks): read from there, they cost no vector load in the loop, whose result the
     // compiler would wait for together with every tile load issued before it.
     __shared__ int dids[kDirectMaxBlocks];
-    for (int k = tid; k < j1 - j0; k += NTHR) dids[k] = trow[j0 + k];
+    // (the launch rejects longer partitions; the bound keeps the copy inside the table anyway)
+    for (int k = tid; k < min(j1 - j0, kDirectMaxBlocks); k += NTHR) dids[k] = trow[j0 + k];
     __syncthreads();
     auto ids_at = [&](int s) {            // a step past the range: the last one's
       const int ss = max(min(s, se_ - 1), s0);
-      const int jb = 2 * ss - j0;
+      const int jb = min(2 * ss - j0, kDirectMaxBlocks - 2);
       return StepIds{dids[jb], dids[2 * ss + 1 < j1 ? jb + 1 : jb]};
     };
     f32x4 S[TPW][2];
