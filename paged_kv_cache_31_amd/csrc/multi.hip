@@ -211,15 +211,17 @@ static hipError_t launch_merge(const MultiArgs& a, hipStream_t stream) {
 //
 // A workgroup of W waves takes 16 * TPW * W consecutive rows of one head (TPW 16-column MFMA
 // tiles per wave) and walks the keys of one partition of them in 32-token steps.  Each step's K
-// and V tiles are loaded from HBM once per workgroup (every thread a few 16-byte words, two steps
-// ahead of their use) and written to one of three or four LDS buffers; the waves read their
-// MFMA operands from LDS, so the tiles of a head share every load.  Per step a wave issues 8 MFMAs per tile for
-// the scores and 8 (fp16) or 16 (bf16: P as a hi/lo pair) per tile for P.V.  Operand layouts are
-// those of the streaming core: K token rows in the A operand in the order that makes the score
-// layout the P^T operand, V^T as the A operand of P.V (the LDS V tile is dim-major, 32 tokens
-// per dimension row, rows padded by 32 bytes to spread LDS banks).  V elements of tokens at or
-// past the context end are zeroed when staged, so garbage in the last block's unused slots never
-// reaches the products.  With several key partitions (taken when the blocks of rows alone are
+// and V tiles are loaded from HBM once per workgroup into one of three or four LDS buffers (16-bit
+// caches in the 8-wave shape: straight into LDS, three steps ahead; otherwise every thread a few
+// 16-byte words through registers, two steps ahead, fp8 widened on the way); the waves read their
+// MFMA operands from LDS, so the tiles of a head share every load.  Per step a wave issues 8 MFMAs
+// per tile for the scores and 8 (fp16) or 16 (bf16: P as a hi/lo pair) per tile for P.V.  Operand
+// layouts are those of the streaming core: K token rows in the A operand in the order that makes
+// the score layout the P^T operand, V^T as the A operand of P.V (the LDS V tile is dim-major, 32
+// tokens per dimension row; rows padded to 96 bytes when staged through registers).  V elements of
+// tokens at or past the context end are zeroed (when staged, or after the read on the direct
+// path), so garbage in the last block's unused slots never reaches the products.  With several
+// key partitions (taken when the blocks of rows alone are
 // too few to fill the GPU) the unnormalised result and its (max, exp-sum) go to the workspace
 // for multi_merge_kernel, as in multi_kernel.
 template <int D, int W, int EB>
